@@ -1,0 +1,197 @@
+"""Seeded synthetic workloads for the fused KV-cache write epilog.
+
+This module only draws inputs: token rows, gamma, cos/sin tables, slot
+mappings and prefilled caches.  It holds none of the epilog's arithmetic and
+is shared by the oracle tests, the GPU parity tests, the smoke check and the
+benchmark, so that both sides consume identical bytes.
+
+bf16 tensors are numpy ``uint16`` bit patterns; fp32 draws are rounded to
+bf16 by torch's CPU conversion (round to nearest even).
+
+Shapes follow the workloads the pages describe: DeepSeek-style rows of
+d = 576 (512 latent + 64 rope, "aclnnKvRmsNormRopeCache" 约束说明, N = 1) and
+indexer rows of d = 128 ("indexer_quant_cache" 约束, d = 128 example).  No
+public dataset is involved; every value is drawn from a seeded generator.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+MODE_FP8_BF16SCALE = 0
+MODE_FP8_E8M0 = 1
+MODE_MXFP4 = 3
+MODE_BF16_SPLIT = 4
+
+PREFILL = 0xAB
+
+
+def to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round fp32 (or fp64) values to bf16 bit patterns (torch, RNE)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class CacheSpec:
+    """[block_num, block_size, 1, head_dim]; head_dim and block_stride in
+    elements of ``elem_bytes`` bytes."""
+    block_num: int
+    block_size: int
+    head_dim: int
+    block_stride: int
+    elem_bytes: int = 1
+
+    @property
+    def num_slots(self) -> int:
+        return self.block_num * self.block_size
+
+    @property
+    def alloc_bytes(self) -> int:
+        return ((self.block_num - 1) * self.block_stride
+                + self.block_size * self.head_dim) * self.elem_bytes
+
+    @property
+    def geom(self):
+        return (self.block_num, self.block_size, self.head_dim, self.block_stride)
+
+    def row_offset(self, slot: int) -> int:
+        """Byte offset of a slot's row (independent restatement of the paged
+        layout, used by the tests' address checks)."""
+        blk, pos = divmod(int(slot), self.block_size)
+        return (blk * self.block_stride + pos * self.head_dim) * self.elem_bytes
+
+
+@dataclass
+class Workload:
+    name: str
+    mode: int
+    T: int
+    d: int
+    group_size: int
+    x: np.ndarray                      # uint16 [T, d]
+    slots: np.ndarray                  # int32 [T]
+    cache: CacheSpec
+    cache_init: np.ndarray             # uint8 [cache.alloc_bytes]
+    gamma: Optional[np.ndarray] = None  # uint16 [d-64]
+    cos: Optional[np.ndarray] = None    # uint16 [T, 64]
+    sin: Optional[np.ndarray] = None    # uint16 [T, 64]
+    eps: float = 1e-6
+    aux: Optional[CacheSpec] = None
+    aux_init: Optional[np.ndarray] = None
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def hits(self) -> int:
+        return int(np.count_nonzero((self.slots >= 0)
+                                    & (self.slots < self.cache.num_slots)))
+
+
+def slot_mapping(rng, T: int, num_slots: int, skip_frac: float = 0.0,
+                 n_skip: Optional[int] = None) -> np.ndarray:
+    """Distinct slots drawn as the first T entries of a permutation of
+    [0, num_slots), then exactly round(skip_frac * T) of them (or n_skip) set
+    to -1 at random positions."""
+    assert T <= num_slots
+    s = rng.permutation(num_slots)[:T].astype(np.int32)
+    k = int(round(skip_frac * T)) if n_skip is None else int(n_skip)
+    if k:
+        s[rng.choice(T, size=k, replace=False)] = -1
+    return s
+
+
+def rope_tables(rng, T: int, max_pos: int, theta: float = 10000.0, dk: int = 64):
+    """cos/sin [T, dk] for random integer positions < max_pos:
+    cos[t, k] = cos(pos_t * theta^(-2 (k mod dk/2) / dk)), in fp64, rounded
+    to bf16."""
+    pos = rng.integers(0, max_pos, size=T).astype(np.float64)
+    half = dk // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / dk)
+    ang = pos[:, None] * inv[None, :]
+    ang = np.concatenate([ang, ang], axis=1)
+    return to_bf16(np.cos(ang)), to_bf16(np.sin(ang)), pos
+
+
+def normal_rows(rng, T: int, d: int, row_sigma: float = 0.0,
+                outlier_frac: float = 0.0, outlier_mult: float = 100.0) -> np.ndarray:
+    """x ~ N(0,1) * per-row lognormal(0, row_sigma), with exactly
+    round(outlier_frac * T * d) random elements multiplied by outlier_mult."""
+    x = rng.standard_normal((T, d), dtype=np.float32)
+    if row_sigma > 0:
+        x *= rng.lognormal(0.0, row_sigma, size=(T, 1)).astype(np.float32)
+    n_out = int(round(outlier_frac * T * d))
+    if n_out:
+        idx = rng.choice(T * d, size=n_out, replace=False)
+        x.reshape(-1)[idx] *= np.float32(outlier_mult)
+    return to_bf16(x)
+
+
+def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
+         aux: Optional[CacheSpec] = None, norm: bool = False, rope: bool = False,
+         row_sigma: float = 0.0, outlier_frac: float = 0.0, skip_frac: float = 0.0,
+         n_skip: Optional[int] = None, max_pos: int = 32768, eps: float = 1e-6,
+         group_size: Optional[int] = None, x: Optional[np.ndarray] = None) -> Workload:
+    rng = np.random.default_rng(seed)
+    if group_size is None:
+        group_size = 32 if mode == MODE_MXFP4 else 64
+    if x is None:
+        x = normal_rows(rng, T, d, row_sigma, outlier_frac)
+    gamma = cos = sin = None
+    if norm:
+        gamma = to_bf16(rng.uniform(0.5, 1.5, size=d - 64))
+    if rope:
+        cos, sin, _ = rope_tables(rng, T, max_pos)
+    slots = slot_mapping(rng, T, cache.num_slots, skip_frac, n_skip)
+    cache_init = np.full(cache.alloc_bytes, PREFILL, np.uint8)
+    aux_init = None if aux is None else np.full(aux.alloc_bytes, PREFILL, np.uint8)
+    return Workload(name, mode, T, d, group_size, x, slots, cache, cache_init,
+                    gamma, cos, sin, eps, aux, aux_init)
+
+
+# ---- the five named workloads ---------------------------------------------
+
+CONFIG_NAMES = ("mode0_tiny_d256", "rmsnorm_rope_bf16_d576", "mode1_prefill_d576",
+                "mxfp4_indexer_d128", "fused_epilog_d576")
+
+
+def config(i: int) -> Workload:
+    if i == 0:
+        # quantMode 0, x [64,256] ~ N(0,1), group 64, cache [8,16,1,416] u8
+        # prefilled 0xAB, 64 distinct slots in [0,128) with 8 set to -1.
+        return make(CONFIG_NAMES[0], MODE_FP8_BF16SCALE, 64, 256, seed=0,
+                    cache=CacheSpec(8, 16, 416, 16 * 416), n_skip=8)
+    if i == 1:
+        # RMSNorm(512) + RoPE(64) to bf16 ckv [1024,128,1,512] and
+        # k [1024,128,1,64] caches; 64 tokens, 5% skipped.
+        return make(CONFIG_NAMES[1], MODE_BF16_SPLIT, 64, 576, seed=1,
+                    cache=CacheSpec(1024, 128, 512, 128 * 512, 2),
+                    aux=CacheSpec(1024, 128, 64, 128 * 64, 2),
+                    norm=True, rope=True, skip_frac=0.05, max_pos=32768)
+    if i == 2:
+        # quantMode 1 prefill: [16384,576], lognormal(0,2) row magnitudes and
+        # 0.1% outliers x100; cache [512,128,1,656]; 2% skipped.
+        return make(CONFIG_NAMES[2], MODE_FP8_E8M0, 16384, 576, seed=2,
+                    cache=CacheSpec(512, 128, 656, 128 * 656),
+                    row_sigma=2.0, outlier_frac=0.001, skip_frac=0.02)
+    if i == 3:
+        # MX-FP4 indexer: [131072,128], lognormal(0,1) rows; cache
+        # [1024,128,1,64] u8 + cache_scale [1024,128,1,4]; 1% skipped.
+        return make(CONFIG_NAMES[3], MODE_MXFP4, 131072, 128, seed=3,
+                    cache=CacheSpec(1024, 128, 64, 128 * 64),
+                    aux=CacheSpec(1024, 128, 4, 128 * 4),
+                    row_sigma=1.0, skip_frac=0.01)
+    if i == 4:
+        # Full fused epilog: [262144,576], RMSNorm(512) + RoPE(64,
+        # positions < 131072) then quantMode 0; 672-byte rows in a cache
+        # [2048,128,1,672] whose block stride is 1.25x the dense one; 3% skipped.
+        return make(CONFIG_NAMES[4], MODE_FP8_BF16SCALE, 262144, 576, seed=4,
+                    cache=CacheSpec(2048, 128, 672, 128 * 672 * 5 // 4),
+                    norm=True, rope=True, max_pos=131072, skip_frac=0.03)
+    raise IndexError(i)

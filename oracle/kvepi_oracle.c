@@ -1,0 +1,394 @@
+/*
+ * kvepi_oracle.c -- plain CPU oracle of the fused KV-cache write epilog.
+ *
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check and the benchmark's CPU
+ * baseline leg).  It shares no code with the HIP path.  Every function says
+ * which passage it follows; the page titles are those of the vendor operator
+ * documentation pages this method comes from.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fPIC -shared.
+ * All floating point is IEEE binary32 evaluated in source order (x86-64 SSE,
+ * no excess precision, no contraction); binary64 is used only where a value
+ * is exact in it (comparisons against fmax*2^E, scaled code search).
+ */
+#include "kvepi_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ======================================================================== */
+/* bf16                                                                      */
+/* ======================================================================== */
+
+float kvo_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static uint32_t f32_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+/* Round a binary32 value to bfloat16, to nearest with ties to the even
+ * significand.  Written from the definition: take the two bf16 neighbours of
+ * f (truncated towards zero, and one bf16 ulp further from zero), pick the
+ * nearer one, exactly compared in binary64, and the even one on a tie. */
+uint16_t kvo_f32_to_bf16(float f) {
+  uint32_t u = f32_bits(f);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN */
+  if (isinf(f)) return (uint16_t)(u >> 16);
+  uint16_t lo = (uint16_t)(u >> 16);     /* towards zero */
+  uint16_t hi = (uint16_t)(lo + 1u);     /* away from zero (may become inf) */
+  double dlo = (double)kvo_bf16_to_f32(lo);
+  double dhi = (double)kvo_bf16_to_f32(hi);
+  double df = (double)f;
+  double elo = fabs(df - dlo);
+  double ehi = fabs(dhi - df);
+  if (isinf(dhi)) {
+    /* hi would be the overflow: the rounding boundary is the midpoint
+     * between the largest finite bf16 and 2^128. */
+    double mid = dlo + (ldexp(1.0, 128) * (dlo < 0 ? -1.0 : 1.0) - dlo) / 2.0;
+    if (fabs(df) < fabs(mid)) return lo;
+    if (fabs(df) > fabs(mid)) return hi;
+    return (lo & 1u) ? hi : lo;
+  }
+  if (elo < ehi) return lo;
+  if (ehi < elo) return hi;
+  return (lo & 1u) ? hi : lo;
+}
+
+/* ======================================================================== */
+/* FP8 E4M3FN and FP4 E2M1 encoders                                          */
+/* ======================================================================== */
+
+/* Round-half-even of a binary64 value that is exact (the callers only pass
+ * v * 2^k of a binary32 v).  nearbyint follows the default to-nearest-even
+ * rounding mode. */
+static double rne(double a) { return nearbyint(a); }
+
+/* E4M3FN (OCP 8-bit floating point): sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; subnormals m * 2^-9; no infinities; S.1111.111 is NaN so the
+ * largest finite magnitude is 1.75 * 2^8 = 448.  Values are rounded to the
+ * nearest representable magnitude, ties to the even code, and magnitudes
+ * beyond 448 saturate to 448.  The sign of zero is kept.
+ *
+ * This is the round() of "aclnnKvCompressEpilog" 计算公式 (q_i =
+ * round(x_i / scale_g)) with the FP8 format named by "aclnnKvRmsNormRopeCache"
+ * 约束说明 (FLOAT8E4M3FN); round-half-even is the CAST_RINT of the
+ * "aclnnDequantRopeQuantKvcache" kernel walkthrough. */
+uint8_t kvo_enc_e4m3(float v) {
+  uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  if (isnan(v)) return (uint8_t)(sign | 0x7F);
+  double a = fabs((double)v);
+  if (a > 448.0) return (uint8_t)(sign | 0x7E);
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: magnitude = k * 2^-9, k = 0..8 (k == 8 is the
+     * smallest normal 2^-6, whose code is also 8) */
+    int k = (int)rne(a * 512.0);
+    return (uint8_t)(sign | k);
+  }
+  int e;
+  double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  e -= 1;                  /* a = (2m) * 2^e, 2m in [1, 2) */
+  double frac = 2.0 * m - 1.0;
+  int mm = (int)rne(frac * 8.0);
+  if (mm == 8) {
+    mm = 0;
+    e += 1;
+  }
+  if (e > 8 || (e == 8 && mm == 7)) return (uint8_t)(sign | 0x7E);
+  return (uint8_t)(sign | ((e + 7) << 3) | mm);
+}
+
+/* E2M1 (OCP MX FP4): sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  Nearest, ties to the even code,
+ * saturating at 6 ("aclnnKvCompressEpilog" 计算公式 FLOAT4_E2M1(x / scale);
+ * "indexer_quant_cache" 接口功能 MX-FP4).  Returns the 4-bit code. */
+uint8_t kvo_enc_e2m1(float v) {
+  uint8_t sign = signbit(v) ? 0x8 : 0x0;
+  if (isnan(v)) return (uint8_t)(sign | 0x7);
+  double a = fabs((double)v);
+  if (a > 6.0) return (uint8_t)(sign | 0x7);
+  if (a < 1.0) {
+    int k = (int)rne(a * 2.0); /* 0, 0.5 or (k == 2) the smallest normal 1.0 */
+    return (uint8_t)(sign | k);
+  }
+  int e;
+  double m = frexp(a, &e);
+  e -= 1; /* a = (2m) * 2^e, e in {0, 1, 2} */
+  double frac = 2.0 * m - 1.0;
+  int mm = (int)rne(frac * 2.0);
+  if (mm == 2) {
+    mm = 0;
+    e += 1;
+  }
+  if (e > 2) return (uint8_t)(sign | 0x7);
+  return (uint8_t)(sign | ((e + 1) << 1) | mm);
+}
+
+/* e8m0 scale exponent: the smallest integer E with amax <= fmax * 2^E, i.e.
+ * the scale amax / fmax rounded up to a power of two ("aclnnKvCompressEpilog"
+ * 计算公式, quantMode=1: the e8m0 scale is rounded up to a power of two).
+ * Clamped to the e8m0 range [-127, 127] (byte E + 127; 255 is NaN and never
+ * produced).  amax == 0 gives -127. */
+int kvo_e8m0_exponent(float amax, float fmax) {
+  if (!(amax > 0.0f)) return -127;
+  double a = (double)amax, f = (double)fmax;
+  int E;
+  frexp(a / f, &E); /* a/f in [2^(E-1), 2^E) up to binary64 rounding */
+  /* settle E with exact binary64 comparisons (f * 2^E is exact) */
+  while (E > -127 && ldexp(f, E - 1) >= a) E--;
+  while (E < 127 && ldexp(f, E) < a) E++;
+  if (E < -127) E = -127;
+  if (E > 127) E = 127;
+  return E;
+}
+
+void kvo_enc_e4m3_batch(const float *v, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_enc_e4m3(v[i]);
+}
+void kvo_enc_e2m1_batch(const float *v, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_enc_e2m1(v[i]);
+}
+void kvo_f32_to_bf16_batch(const float *v, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_f32_to_bf16(v[i]);
+}
+void kvo_e8m0_exponent_batch(const float *amax, float fmax, int32_t *out,
+                             int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_e8m0_exponent(amax[i], fmax);
+}
+
+/* ======================================================================== */
+/* RMSNorm and RoPE ("aclnnKvRmsNormRopeCache", 计算公式)                    */
+/* ======================================================================== */
+
+/* Balanced pairwise sum of v[0..n), n a power of two. */
+static float tree_sum(const float *v, int64_t n) {
+  if (n == 1) return v[0];
+  return tree_sum(v, n / 2) + tree_sum(v + n / 2, n / 2);
+}
+
+float kvo_sumsq_tree(const uint16_t *x, int64_t n) {
+  int64_t p = 1;
+  while (p < n) p <<= 1;
+  float *sq = (float *)calloc((size_t)p, sizeof(float));
+  for (int64_t i = 0; i < n; ++i) {
+    float xi = kvo_bf16_to_f32(x[i]);
+    sq[i] = xi * xi; /* square_x = x * x (exact for a bf16 x) */
+  }
+  float ss = tree_sum(sq, p);
+  free(sq);
+  return ss;
+}
+
+/* (2) rmsNorm: square_x = x*x; mean_square_x = mean(square_x);
+ * rms = sqrt(mean_square_x + epsilon); y = (x / rms) * gamma, written in
+ * binary32 and rounded once more to the bf16 output. */
+void kvo_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t n,
+                     float eps, uint16_t *y) {
+  float ss = kvo_sumsq_tree(x, n);
+  float mean_sq = ss / (float)n;
+  float rms = sqrtf(mean_sq + eps);
+  for (int64_t i = 0; i < n; ++i) {
+    float xi = kvo_bf16_to_f32(x[i]);
+    float t = xi / rms;
+    float u = t * kvo_bf16_to_f32(gamma[i]);
+    y[i] = kvo_f32_to_bf16(u);
+  }
+}
+
+/* (1) interleaveRope on the 64 rope columns: x1 = x[0::2], x2 = x[1::2];
+ * y = cat(x1, x2) * cos + cat(-x2, x1) * sin.  The output is half-split:
+ * y[j] = x1[j]*cos[j] - x2[j]*sin[j], y[32+j] = x2[j]*cos[32+j] +
+ * x1[j]*sin[32+j]. */
+void kvo_rope_row(const uint16_t *x, const uint16_t *cos, const uint16_t *sin,
+                  uint16_t *y) {
+  for (int j = 0; j < 32; ++j) {
+    float x1 = kvo_bf16_to_f32(x[2 * j]);
+    float x2 = kvo_bf16_to_f32(x[2 * j + 1]);
+    float c0 = kvo_bf16_to_f32(cos[j]), s0 = kvo_bf16_to_f32(sin[j]);
+    float c1 = kvo_bf16_to_f32(cos[32 + j]), s1 = kvo_bf16_to_f32(sin[32 + j]);
+    float p1 = x1 * c0;
+    float p2 = (-x2) * s0;
+    y[j] = kvo_f32_to_bf16(p1 + p2);
+    float p3 = x2 * c1;
+    float p4 = x1 * s1;
+    y[32 + j] = kvo_f32_to_bf16(p3 + p4);
+  }
+}
+
+/* ======================================================================== */
+/* Row geometry ("aclnnKvCompressEpilog" 约束说明; "indexer_quant_cache" 约束) */
+/* ======================================================================== */
+
+int kvo_row_bytes(int mode, int64_t d, int32_t group_size, int64_t *concat_col,
+                  int64_t *kv_cache_col, int64_t *scale_col) {
+  int64_t cc = 0, kc = 0, sc = 0;
+  if (mode == KVO_MODE_FP8_BF16SCALE || mode == KVO_MODE_FP8_E8M0) {
+    if (group_size != 64 || d % 64 != 0 || d <= 64 || d > 8192) return -1;
+    int64_t nope = d - 64;
+    int64_t groups = (nope + 63) / 64;
+    int64_t sbytes = mode == KVO_MODE_FP8_BF16SCALE ? 2 : 1;
+    cc = nope + 128 + groups * sbytes;
+    kc = mode == KVO_MODE_FP8_E8M0 ? cc : (cc + 31) / 32 * 32;
+    sc = groups;
+  } else if (mode == KVO_MODE_MXFP4) {
+    if (group_size != 32 || d % 32 != 0 || d < 32 || d > 8192) return -1;
+    cc = (d + 1) / 2;
+    kc = cc;
+    sc = (d + 31) / 32;
+  } else if (mode == KVO_MODE_BF16_SPLIT) {
+    if (d % 64 != 0 || d <= 64 || d > 8192) return -1;
+    cc = d - 64; /* ckv elements per row */
+    kc = d - 64;
+    sc = 64; /* k elements per row */
+  } else {
+    return -1;
+  }
+  if (concat_col) *concat_col = cc;
+  if (kv_cache_col) *kv_cache_col = kc;
+  if (scale_col) *scale_col = sc;
+  return 0;
+}
+
+/* ======================================================================== */
+/* Quantisation of one prepared row                                          */
+/* ======================================================================== */
+
+static void put_u16le(uint8_t *p, uint16_t v) {
+  p[0] = (uint8_t)(v & 0xFF);
+  p[1] = (uint8_t)(v >> 8);
+}
+
+/* "aclnnKvCompressEpilog" 计算公式 scenes 1 and 2, with the row layout of
+ * 约束说明 (nope codes | rope at 16 bit | one scale per group | zero padding
+ * to kvCacheCol), and "indexer_quant_cache" mxfp4 (codes of the whole row,
+ * two per byte, scales to cache_scale). */
+int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
+                  uint8_t *out, uint8_t *scale_out) {
+  int64_t cc, kc, sc;
+  if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
+  if (mode == KVO_MODE_FP8_BF16SCALE || mode == KVO_MODE_FP8_E8M0) {
+    int64_t nope = d - 64;
+    memset(out, 0, (size_t)kc);
+    for (int64_t g = 0; g < sc; ++g) {
+      int64_t i0 = g * 64, i1 = i0 + 64 < nope ? i0 + 64 : nope;
+      float amax = 0.0f;
+      for (int64_t i = i0; i < i1; ++i) {
+        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        if (a > amax) amax = a;
+      }
+      float s_use;
+      if (mode == KVO_MODE_FP8_BF16SCALE) {
+        float s32 = amax / 448.0f; /* scale_g = max|x_g| / FP8_MAX */
+        uint16_t sb = kvo_f32_to_bf16(s32);
+        put_u16le(out + nope + 128 + 2 * g, sb);
+        s_use = kvo_bf16_to_f32(sb); /* divide by the scale as stored */
+      } else {
+        int E = kvo_e8m0_exponent(amax, 448.0f);
+        out[nope + 128 + g] = (uint8_t)(E + 127);
+        s_use = ldexpf(1.0f, E);
+      }
+      for (int64_t i = i0; i < i1; ++i) {
+        if (s_use == 0.0f) {
+          out[i] = 0x00;
+        } else {
+          float q = kvo_bf16_to_f32(v[i]) / s_use;
+          out[i] = kvo_enc_e4m3(q);
+        }
+      }
+    }
+    for (int64_t j = 0; j < 64; ++j) put_u16le(out + nope + 2 * j, v[nope + j]);
+    return 0;
+  }
+  if (mode == KVO_MODE_MXFP4) {
+    memset(out, 0, (size_t)kc);
+    for (int64_t g = 0; g < sc; ++g) {
+      int64_t i0 = g * 32, i1 = i0 + 32 < d ? i0 + 32 : d;
+      float amax = 0.0f;
+      for (int64_t i = i0; i < i1; ++i) {
+        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        if (a > amax) amax = a;
+      }
+      int E = kvo_e8m0_exponent(amax, 6.0f);
+      scale_out[g] = (uint8_t)(E + 127);
+      float s_use = ldexpf(1.0f, E);
+      for (int64_t i = i0; i < i1; ++i) {
+        uint8_t c = kvo_enc_e2m1(kvo_bf16_to_f32(v[i]) / s_use);
+        /* element 2j in the low nibble, 2j+1 in the high nibble */
+        if (i % 2 == 0)
+          out[i / 2] = (uint8_t)((out[i / 2] & 0xF0) | c);
+        else
+          out[i / 2] = (uint8_t)((out[i / 2] & 0x0F) | (c << 4));
+      }
+    }
+    return 0;
+  }
+  return -1;
+}
+
+/* ======================================================================== */
+/* Whole epilog                                                              */
+/* ======================================================================== */
+
+static uint8_t *row_ptr(const kvo_cache *c, int64_t slot, int64_t esz) {
+  int64_t blk = slot / c->block_size;
+  int64_t pos = slot % c->block_size;
+  return c->data + (blk * c->block_stride + pos * c->head_dim) * esz;
+}
+
+int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
+               int64_t x_row_stride, const uint16_t *gamma,
+               const uint16_t *cos, const uint16_t *sin, float eps,
+               const int32_t *slot_mapping, int32_t group_size,
+               const kvo_cache *cache, const kvo_cache *aux) {
+  int64_t cc, kc, sc;
+  if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
+  if ((cos == NULL) != (sin == NULL)) return -1;
+  if (mode == KVO_MODE_MXFP4 && (gamma || cos)) return -1;
+  if (mode == KVO_MODE_BF16_SPLIT && (!gamma || !cos)) return -1;
+  if ((mode == KVO_MODE_MXFP4 || mode == KVO_MODE_BF16_SPLIT) && !aux)
+    return -1;
+  int64_t num_slots = cache->block_num * cache->block_size;
+  int64_t nope = d - 64;
+  uint16_t *v = (uint16_t *)malloc((size_t)d * sizeof(uint16_t));
+  uint8_t *row = (uint8_t *)malloc((size_t)kc + 64);
+  uint8_t *srow = (uint8_t *)malloc((size_t)sc + 64);
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0 || s >= num_slots) continue; /* -1: token skipped */
+    const uint16_t *xr = x + t * x_row_stride;
+    if (mode == KVO_MODE_MXFP4) {
+      kvo_quant_row(mode, xr, d, group_size, row, srow);
+      memcpy(row_ptr(cache, s, 1), row, (size_t)kc);
+      memcpy(row_ptr(aux, s, 1), srow, (size_t)sc);
+      continue;
+    }
+    if (gamma)
+      kvo_rmsnorm_row(xr, gamma, nope, eps, v);
+    else
+      memcpy(v, xr, (size_t)nope * sizeof(uint16_t));
+    if (cos)
+      kvo_rope_row(xr + nope, cos + t * 64, sin + t * 64, v + nope);
+    else
+      memcpy(v + nope, xr + nope, 64 * sizeof(uint16_t));
+    if (mode == KVO_MODE_BF16_SPLIT) {
+      uint8_t *ckv = row_ptr(cache, s, 2);
+      uint8_t *k = row_ptr(aux, s, 2);
+      for (int64_t i = 0; i < nope; ++i) put_u16le(ckv + 2 * i, v[i]);
+      for (int64_t j = 0; j < 64; ++j) put_u16le(k + 2 * j, v[nope + j]);
+      continue;
+    }
+    kvo_quant_row(mode, v, d, group_size, row, NULL);
+    memcpy(row_ptr(cache, s, 1), row, (size_t)kc);
+  }
+  free(v);
+  free(row);
+  free(srow);
+  return 0;
+}

@@ -1,0 +1,101 @@
+/*
+ * kvepi_oracle.h -- plain, slow, single-threaded CPU oracle of the fused
+ * KV-cache write epilog.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library includes, links or
+ * calls this code; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with the
+ * HIP path.
+ *
+ * What it computes (sources, cited by page title and section):
+ *  - "aclnnKvCompressEpilog", 功能说明 / 计算公式: the last 64 columns of a row
+ *    are the rope segment, the first d-64 the nope segment; per-group amax
+ *    quantisation of the nope segment, q_i = round(x_i / scale_g) with
+ *    scale_g = max|x_g| / FP8_MAX; mode 0 stores the scale as bf16, mode 1 as
+ *    an e8m0 power of two rounded up.
+ *  - "aclnnKvCompressEpilog", 约束说明: the cache is [blockNum, blockSize, 1,
+ *    headDim]; the row byte count kvCacheCol = align(concatCol); slot -1 is
+ *    skipped; only the blockNum dimension may be non-contiguous.
+ *  - "aclnnKvRmsNormRopeCache", 计算公式 (1) interleaveRope and (2) rmsNorm.
+ *  - "indexer_quant_cache", 接口功能 / 约束: MX-FP4 groups of 32 with an e8m0
+ *    scale written to a separate cache_scale tensor; rows not hit keep their
+ *    values.
+ *
+ * Arithmetic: IEEE fp32 (the precision the quantiser's division is defined
+ * in), evaluated in the order written, compiled with -ffp-contract=off.  The
+ * one order the pages leave open, the RMSNorm sum of squares, is a balanced
+ * pairwise tree over the zero-padded power-of-two length.
+ *
+ * bf16 values are passed as their uint16_t bit patterns.
+ */
+#ifndef KVEPI_ORACLE_H
+#define KVEPI_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Output modes (the oracle's own numbering). */
+#define KVO_MODE_FP8_BF16SCALE 0 /* group-64 E4M3 codes, bf16 scale        */
+#define KVO_MODE_FP8_E8M0 1      /* group-64 E4M3 codes, e8m0 scale        */
+#define KVO_MODE_MXFP4 3         /* group-32 E2M1 nibbles, e8m0 scale row  */
+#define KVO_MODE_BF16_SPLIT 4    /* RMSNorm -> ckv cache, RoPE -> k cache  */
+
+/* ---- number formats ---------------------------------------------------- */
+float kvo_bf16_to_f32(uint16_t h);
+uint16_t kvo_f32_to_bf16(float f);     /* round to nearest, ties to even   */
+uint8_t kvo_enc_e4m3(float v);         /* OCP E4M3FN, RNE, saturate to 448 */
+uint8_t kvo_enc_e2m1(float v);         /* OCP E2M1 nibble, RNE, sat. to 6  */
+int kvo_e8m0_exponent(float amax, float fmax); /* smallest E>=-127 with
+                                                  amax <= fmax*2^E         */
+
+void kvo_enc_e4m3_batch(const float *v, uint8_t *out, int64_t n);
+void kvo_enc_e2m1_batch(const float *v, uint8_t *out, int64_t n);
+void kvo_f32_to_bf16_batch(const float *v, uint16_t *out, int64_t n);
+void kvo_e8m0_exponent_batch(const float *amax, float fmax, int32_t *out,
+                             int64_t n);
+
+/* ---- per-row steps ----------------------------------------------------- */
+/* RMSNorm over n bf16 values: y = bf16((x / sqrt(mean(x^2) + eps)) * gamma) */
+void kvo_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t n,
+                     float eps, uint16_t *y);
+/* Sum of squares as the balanced pairwise tree (exposed for its pin). */
+float kvo_sumsq_tree(const uint16_t *x, int64_t n);
+/* Interleaved RoPE on 64 values -> 64 half-split values. */
+void kvo_rope_row(const uint16_t *x, const uint16_t *cos, const uint16_t *sin,
+                  uint16_t *y);
+
+/* Row geometry.  Returns 0 on success, -1 for an unsupported combination. */
+int kvo_row_bytes(int mode, int64_t d, int32_t group_size, int64_t *concat_col,
+                  int64_t *kv_cache_col, int64_t *scale_col);
+
+/* Quantise one prepared row v[0..d) (bf16 bits: nope segment already
+ * normalised if RMSNorm is on, rope segment already rotated if RoPE is on)
+ * into out[0..kv_cache_col) (modes 0/1) or out[0..d/2) plus
+ * scale_out[0..d/32) (MX-FP4). */
+int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
+                  uint8_t *out, uint8_t *scale_out);
+
+/* ---- whole epilog ------------------------------------------------------ */
+/* Cache geometry: [block_num, block_size, 1, head_dim] with head_dim and
+ * block_stride counted in elements of elem_bytes bytes. */
+typedef struct {
+  uint8_t *data;
+  int64_t block_num, block_size, head_dim, block_stride;
+} kvo_cache;
+
+/* Runs the epilog for tokens t = 0..T-1 in order.  gamma (length d-64) and
+ * cos/sin ([T,64]) may be NULL.  aux is the cache_scale tensor (MX-FP4) or
+ * the k cache (BF16 split).  Returns 0, or -1 on an argument it rejects. */
+int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
+               int64_t x_row_stride, const uint16_t *gamma,
+               const uint16_t *cos, const uint16_t *sin, float eps,
+               const int32_t *slot_mapping, int32_t group_size,
+               const kvo_cache *cache, const kvo_cache *aux);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
