@@ -1,0 +1,191 @@
+/*
+ * kvepi.h -- C ABI of the fused KV-cache write epilog for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * For each token row t of a bf16 activation x[T, d] whose slot_mapping[t] is
+ * a valid slot, the library writes one packed row into a paged cache
+ * [blockNum, blockSize, 1, headDim] in place:
+ *
+ *   1. optional RMSNorm over the nope segment x[t, 0:d-64]
+ *        ("aclnnKvRmsNormRopeCache", 计算公式 (2) rmsNorm),
+ *   2. optional interleaved RoPE over the rope segment x[t, d-64:d], giving a
+ *      half-split result ("aclnnKvRmsNormRopeCache", 计算公式 (1)),
+ *   3. per-group amax dynamic quantisation of the nope segment
+ *        ("aclnnKvCompressEpilog", 计算公式 scenes 1 and 2) or of the whole
+ *        row in MX-FP4 ("indexer_quant_cache", 接口功能),
+ *   4. the scatter of the packed row to slot slot_mapping[t]; tokens whose
+ *      slot is -1 are skipped and every byte outside the written rows keeps
+ *      its value ("aclnnKvCompressEpilog", 约束说明; "indexer_quant_cache",
+ *      语义说明).
+ *
+ * The call is split in two stages, as on the pages: kvepi_get_workspace
+ * validates the arguments and returns the workspace size, kvepi_run validates
+ * again and launches asynchronously on the caller's HIP stream
+ * ("aclnnKvCompressEpilog", the two-stage interface description).
+ *
+ * Conventions shared by every entry point
+ *  - bf16 data is passed as 16-bit little-endian bit patterns.
+ *  - Pointers named x, gamma, cos, sin, slot_mapping and kvepi_cache.data are
+ *    DEVICE pointers; they are checked for NULL and alignment only, never
+ *    dereferenced on the host.  Struct and out-parameter pointers are HOST
+ *    pointers.
+ *  - The caller owns every buffer, the workspace and the stream.  The library
+ *    allocates nothing and keeps no pointer after a call returns.
+ *  - kvepi_run is asynchronous: buffers must stay alive and unmodified until
+ *    the stream has passed the launched kernel.  The library never
+ *    synchronises the stream.
+ *  - Every check runs before any launch, so a call that returns an error
+ *    writes nothing.
+ *  - Results are deterministic: the same inputs give the same bytes
+ *    ("aclnnKvCompressEpilog", 约束说明: deterministic by default).
+ */
+#ifndef KVEPI_H
+#define KVEPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVEPI_VERSION 100 /* 1.0.0 */
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KVEPI_API __attribute__((visibility("default")))
+#else
+#define KVEPI_API
+#endif
+
+typedef enum kvepi_status {
+  KVEPI_OK = 0,
+  KVEPI_ERR_NULLPTR = 1,     /* a required pointer is NULL                  */
+  KVEPI_ERR_SHAPE = 2,       /* a size violates the operation's constraints */
+  KVEPI_ERR_LAYOUT = 3,      /* strides / alignment / cache layout invalid  */
+  KVEPI_ERR_PARAM = 4,       /* group size, eps or optional-input mismatch  */
+  KVEPI_ERR_UNSUPPORTED = 5, /* quant mode or combination not implemented   */
+  KVEPI_ERR_WORKSPACE = 6,   /* workspace smaller than kvepi_get_workspace  */
+  KVEPI_ERR_RUNTIME = 7      /* the HIP runtime refused the launch          */
+} kvepi_status;
+
+/* quant_mode values.
+ *  0  FP8 E4M3 codes per group of 64 nope values, scale = amax/448 stored as
+ *     bf16 ("aclnnKvCompressEpilog" 计算公式, quantMode=0).
+ *     Row: [d-64 codes | 64 rope bf16 | ceil((d-64)/64) bf16 scales | zero pad
+ *     to a multiple of 32 bytes].
+ *  1  as 0, scale stored as one e8m0 byte, the power of two 2^E with E the
+ *     smallest integer such that amax <= 448 * 2^E (quantMode=1).  Row is not
+ *     padded.
+ *  2  quantMode=2 of the page (HiFloat8 rope + FP4 nope): not implemented,
+ *     the HiFloat8 encoding is not defined there -> KVEPI_ERR_UNSUPPORTED.
+ *  3  MX-FP4: E2M1 codes of the whole row, two per byte (element 2j in the
+ *     low nibble), one e8m0 scale (amax <= 6 * 2^E) per group of 32 written
+ *     to cache_aux ("indexer_quant_cache", mxfp4 mode).
+ *  4  bf16 split: RMSNorm output -> cache (ckv, headDim >= d-64 bf16),
+ *     RoPE output -> cache_aux (k, headDim >= 64 bf16)
+ *     ("aclnnKvRmsNormRopeCache", 接口功能).
+ */
+#define KVEPI_MODE_FP8_BF16SCALE 0
+#define KVEPI_MODE_FP8_E8M0 1
+#define KVEPI_MODE_HIF8_FP4 2
+#define KVEPI_MODE_MXFP4 3
+#define KVEPI_MODE_BF16_SPLIT 4
+
+/* A paged cache [block_num, block_size, 1, head_dim] ("aclnnKvCompressEpilog",
+ * 约束说明: four dimensions, dimension -2 fixed at 1, only the block
+ * dimension may be non-contiguous; "indexer_quant_cache" 约束: blocks may be
+ * laid out loosely but are contiguous inside).
+ *  data          DEVICE pointer to element [0,0,0,0]; any byte alignment.
+ *  head_dim      elements per row (uint8 caches: bytes; bf16 caches for mode
+ *                4: 2-byte elements).
+ *  block_stride  elements between consecutive blocks, >= block_size*head_dim.
+ * Slot s lives at data + ((s / block_size) * block_stride +
+ * (s % block_size) * head_dim) * element_size.  num_slots = block_num *
+ * block_size must be <= 2^31 - 1. */
+typedef struct kvepi_cache {
+  void *data;
+  int64_t block_num;
+  int64_t block_size;
+  int64_t head_dim;
+  int64_t block_stride;
+} kvepi_cache;
+
+/* Row geometry of a mode ("aclnnKvCompressEpilog", 约束说明, headDim rule:
+ * concatCol = (d-64) + 128 + ceil((d-64)/64) * scaleBytes with scaleBytes 2
+ * for mode 0 and 1 for mode 1; kvCacheCol = concatCol for mode 1 and
+ * concatCol rounded up to 32 bytes for mode 0; e.g. d=256 in mode 1 gives
+ * 323.  "indexer_quant_cache", 约束: MX-FP4 codes take ceil(d/2) bytes and
+ * scaleCol = ceil(d/32), e.g. d=128 gives 4.)
+ *   concat_col    bytes of data per row (mode 4: ckv elements per row)
+ *   kv_cache_col  bytes written per row, the minimum headDim (mode 4: d-64)
+ *   scale_col     scale entries per row (mode 3: the minimum cache_aux
+ *                 headDim; mode 4: 64, the k-cache elements per row)
+ * Any out-pointer may be NULL.  Errors: KVEPI_ERR_UNSUPPORTED for an unknown
+ * mode or mode 2, KVEPI_ERR_SHAPE for d outside the mode's range
+ * (modes 0/1/4: d % 64 == 0 and 64 < d <= 8192; mode 3: d % 32 == 0 and
+ * 32 <= d <= 8192), KVEPI_ERR_PARAM for a group size other than 64 (modes
+ * 0/1) or 32 (mode 3). */
+KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t group_size,
+                             int64_t *concat_col, int64_t *kv_cache_col,
+                             int64_t *scale_col);
+
+/* Stage one: validate and report the workspace size (always 0 in this
+ * implementation; NULL workspaces are accepted).
+ *
+ *  x             DEVICE, bf16 [num_tokens, d], rows x_row_stride elements
+ *                apart; 16-byte aligned base, x_row_stride % 8 == 0 and
+ *                x_row_stride >= d.  Leading dimensions of the caller's
+ *                tensor are flattened into num_tokens
+ *                ("aclnnKvCompressEpilog", 约束说明, slotMapping shape rule).
+ *  gamma         DEVICE, bf16 [d-64], 16-byte aligned, or NULL for no
+ *                RMSNorm (required in mode 4, rejected in mode 3).
+ *  cos, sin      DEVICE, bf16 [num_tokens, 64] contiguous, 16-byte aligned,
+ *                both or neither; NULL for no RoPE (the rope columns are then
+ *                copied unchanged).  Required in mode 4, rejected in mode 3.
+ *  slot_mapping  DEVICE, int32 [num_tokens], 4-byte aligned.  -1 skips the
+ *                token; any value outside [0, num_slots) is skipped too.
+ *                Valid values must be distinct; with duplicates the result of
+ *                the repeated rows is unspecified ("aclnnKvCompressEpilog",
+ *                约束说明).
+ *  cache         HOST struct describing the main cache (uint8; bf16 in mode
+ *                4).  headDim >= kv_cache_col.
+ *  cache_aux     HOST struct, NULL except in mode 3 (cache_scale, uint8,
+ *                headDim >= scale_col) and mode 4 (k cache, bf16,
+ *                headDim >= 64); same block_num and block_size as cache.
+ *  quant_mode    KVEPI_MODE_*.
+ *  group_size    64 (modes 0, 1), 32 (mode 3), ignored in mode 4.
+ *  eps           RMSNorm epsilon, finite and >= 0 (used only with gamma).
+ *  workspace_bytes  HOST out-parameter.
+ * num_tokens == 0 is valid and makes kvepi_run a no-op. */
+KVEPI_API kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, int64_t d,
+                                 int64_t x_row_stride, const void *gamma,
+                                 const void *cos, const void *sin,
+                                 const int32_t *slot_mapping,
+                                 const kvepi_cache *cache,
+                                 const kvepi_cache *cache_aux,
+                                 int32_t quant_mode, int32_t group_size,
+                                 float eps, uint64_t *workspace_bytes);
+
+/* Stage two: validate as kvepi_get_workspace, then enqueue the epilog on
+ * `stream` (a hipStream_t; NULL = the null stream of the current device).
+ * The current HIP device must be the one holding the buffers.  Returns
+ * KVEPI_ERR_WORKSPACE if workspace_bytes is below the stage-one size and
+ * KVEPI_ERR_RUNTIME if the launch is refused (for example on a device that
+ * is not gfx950). */
+KVEPI_API kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
+                       int64_t x_row_stride, const void *gamma,
+                       const void *cos, const void *sin,
+                       const int32_t *slot_mapping, const kvepi_cache *cache,
+                       const kvepi_cache *cache_aux, int32_t quant_mode,
+                       int32_t group_size, float eps, void *workspace,
+                       uint64_t workspace_bytes, void *stream);
+
+/* Static text for a status code (never NULL). */
+KVEPI_API const char *kvepi_status_str(kvepi_status status);
+
+/* KVEPI_VERSION of the built library. */
+KVEPI_API int32_t kvepi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVEPI_H */

@@ -1,0 +1,165 @@
+"""Thin ctypes binding of libkvepi.so (argument marshalling only).
+
+The functions carry the C ABI's names.  They take torch tensors for device
+memory and torch's current HIP stream, turn them into the plain pointers and
+sizes of ``include/kvepi.h``, and raise ``KvepiError`` on a non-OK status.
+Every step of the epilog runs in the library's HIP kernels; there is no
+fallback of any kind: if the library is missing this module raises on import
+of the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvepi.so")
+
+KVEPI_OK = 0
+STATUS_NAMES = {0: "KVEPI_OK", 1: "KVEPI_ERR_NULLPTR", 2: "KVEPI_ERR_SHAPE",
+                3: "KVEPI_ERR_LAYOUT", 4: "KVEPI_ERR_PARAM", 5: "KVEPI_ERR_UNSUPPORTED",
+                6: "KVEPI_ERR_WORKSPACE", 7: "KVEPI_ERR_RUNTIME"}
+
+KVEPI_MODE_FP8_BF16SCALE = 0
+KVEPI_MODE_FP8_E8M0 = 1
+KVEPI_MODE_HIF8_FP4 = 2
+KVEPI_MODE_MXFP4 = 3
+KVEPI_MODE_BF16_SPLIT = 4
+
+
+class KvepiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kvepi_status_str(status)}")
+
+
+class kvepi_cache(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("block_num", ctypes.c_int64),
+                ("block_size", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("block_stride", ctypes.c_int64)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the in-tree HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m kv_cache_epilog_amd.build` "
+                "(the epilog has no non-HIP implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        CP = ctypes.POINTER(kvepi_cache)
+        L.kvepi_row_bytes.argtypes = [I32, I64, I32, P, P, P]
+        L.kvepi_row_bytes.restype = ctypes.c_int
+        L.kvepi_get_workspace.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F, P]
+        L.kvepi_get_workspace.restype = ctypes.c_int
+        L.kvepi_run.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F, P,
+                                ctypes.c_uint64, P]
+        L.kvepi_run.restype = ctypes.c_int
+        L.kvepi_status_str.argtypes = [ctypes.c_int]
+        L.kvepi_status_str.restype = ctypes.c_char_p
+        L.kvepi_version.argtypes = []
+        L.kvepi_version.restype = I32
+        _lib = L
+    return _lib
+
+
+def kvepi_status_str(status: int) -> str:
+    return lib().kvepi_status_str(int(status)).decode()
+
+
+def kvepi_version() -> int:
+    return int(lib().kvepi_version())
+
+
+def kvepi_row_bytes(quant_mode: int, d: int, group_size: int):
+    """(concat_col, kv_cache_col, scale_col) of a mode."""
+    cc, kc, sc = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = lib().kvepi_row_bytes(quant_mode, d, group_size, ctypes.byref(cc), ctypes.byref(kc),
+                               ctypes.byref(sc))
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_row_bytes")
+    return cc.value, kc.value, sc.value
+
+
+# ---- marshalling -----------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _x_view(x):
+    """x [..., d] -> (ptr, T, d, row_stride) without copying."""
+    if x.dim() < 1 or x.element_size() != 2:
+        raise ValueError("x must be a 16-bit (bf16) tensor")
+    d = x.shape[-1]
+    if x.stride(-1) != 1:
+        raise ValueError("x rows must be contiguous")
+    if x.dim() == 1:
+        return _ptr(x), 1, d, d
+    if x.dim() == 2:
+        return _ptr(x), x.shape[0], d, x.stride(0)
+    if not x.is_contiguous():
+        raise ValueError("x with more than 2 dims must be contiguous")
+    return _ptr(x), x.numel() // d if d else 0, d, d
+
+
+def cache_desc(cache) -> kvepi_cache:
+    """A 4-D cache tensor [block_num, block_size, 1, head_dim] (any block
+    stride; contiguous inside a block) -> kvepi_cache."""
+    if cache.dim() != 4 or cache.shape[2] != 1:
+        raise ValueError("cache must be [block_num, block_size, 1, head_dim]")
+    if cache.stride(3) != 1 or cache.stride(1) != cache.shape[3]:
+        raise ValueError("cache blocks must be contiguous inside")
+    return kvepi_cache(_ptr(cache), cache.shape[0], cache.shape[1], cache.shape[3],
+                       cache.stride(0))
+
+
+def _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin, cache_aux, eps):
+    xp, T, d, xs = _x_view(x)
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have one entry per token row")
+    if slot_mapping.element_size() != 4 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 tensor")
+    for name, t in (("gamma", gamma), ("cos", cos), ("sin", sin)):
+        if t is not None and (not t.is_contiguous() or t.element_size() != 2):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+    c = cache_desc(cache)
+    a = None if cache_aux is None else cache_desc(cache_aux)
+    return (xp, T, d, xs, _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(slot_mapping),
+            ctypes.byref(c), None if a is None else ctypes.byref(a),
+            int(quant_mode), int(group_size), ctypes.c_float(eps)), (c, a)
+
+
+def kvepi_get_workspace(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
+                        gamma=None, cos=None, sin=None, cache_aux=None,
+                        eps: float = 1e-6) -> int:
+    args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
+                        cache_aux, eps)
+    ws = ctypes.c_uint64()
+    st = lib().kvepi_get_workspace(*args, ctypes.byref(ws))
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_get_workspace")
+    return ws.value
+
+
+def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
+              gamma=None, cos=None, sin=None, cache_aux=None, eps: float = 1e-6,
+              workspace=None, stream=None) -> None:
+    """Enqueue the epilog on `stream` (a torch.cuda.Stream; default: torch's
+    current stream).  Updates cache / cache_aux in place, asynchronously."""
+    import torch
+    args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
+                        cache_aux, eps)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    ws_ptr = None if workspace is None else _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kvepi_run(*args, ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_run")

@@ -1,0 +1,41 @@
+"""Builds libkvepi.so in-tree with hipcc for gfx950 (no GPU needed)."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libkvepi.so")
+SOURCES = [os.path.join(CSRC, "kvepi_kernels.hip"), os.path.join(CSRC, "kvepi_host.cpp")]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    "-fvisibility=hidden",  # export only the C ABI
+    # the epilog's arithmetic is IEEE binary32 in source order
+    "-ffp-contract=off", "-fno-fast-math",
+    # never let the compiler form packed-fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,227 @@
+// kvepi_host.cpp -- argument validation, row geometry and the two-stage C ABI
+// of the fused KV-cache write epilog.  Pure host code: no call in this file
+// touches the GPU, so every check can run (and be tested) without one.
+#include <math.h>
+#include <stdint.h>
+
+#include "kvepi.h"
+#include "kvepi_plan.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Largest power of two <= 16 dividing v (v == 0 counts as 16-aligned).
+int32_t pow2_align(uint64_t v) {
+  int32_t a = 16;
+  while (a > 1 && (v & (uint64_t)(a - 1)) != 0) a >>= 1;
+  return a;
+}
+
+int32_t min_align(int32_t a, int32_t b) { return a < b ? a : b; }
+
+// Row geometry ("aclnnKvCompressEpilog" 约束说明 headDim rule;
+// "indexer_quant_cache" 约束 headDim/scaleCol rule).
+kvepi_status row_geometry(int32_t mode, int64_t d, int32_t group_size,
+                          int64_t *cc, int64_t *kc, int64_t *sc) {
+  switch (mode) {
+    case KVEPI_MODE_FP8_BF16SCALE:
+    case KVEPI_MODE_FP8_E8M0: {
+      if (d % 64 != 0 || d <= 64 || d > 8192) return KVEPI_ERR_SHAPE;
+      if (group_size != 64) return KVEPI_ERR_PARAM;
+      const int64_t nope = d - 64;
+      const int64_t groups = (nope + 63) / 64;
+      const int64_t scale_bytes = mode == KVEPI_MODE_FP8_BF16SCALE ? 2 : 1;
+      *cc = nope + 128 + groups * scale_bytes;
+      *kc = mode == KVEPI_MODE_FP8_E8M0 ? *cc : (*cc + 31) / 32 * 32;
+      *sc = groups;
+      return KVEPI_OK;
+    }
+    case KVEPI_MODE_MXFP4:
+      if (d % 32 != 0 || d < 32 || d > 8192) return KVEPI_ERR_SHAPE;
+      if (group_size != 32) return KVEPI_ERR_PARAM;
+      *cc = (d + 1) / 2;
+      *kc = *cc;
+      *sc = (d + 31) / 32;
+      return KVEPI_OK;
+    case KVEPI_MODE_BF16_SPLIT:
+      if (d % 64 != 0 || d <= 64 || d > 8192) return KVEPI_ERR_SHAPE;
+      *cc = d - 64;
+      *kc = d - 64;
+      *sc = 64;
+      return KVEPI_OK;
+    default:
+      return KVEPI_ERR_UNSUPPORTED;
+  }
+}
+
+// Checks one paged cache and returns its byte geometry.
+kvepi_status check_cache(const kvepi_cache *c, int64_t elem, int64_t min_cols,
+                         int64_t *pitch, int64_t *bstride, int32_t *align) {
+  if (c == nullptr || c->data == nullptr) return KVEPI_ERR_NULLPTR;
+  if (c->block_num <= 0 || c->block_size <= 0 || c->head_dim <= 0)
+    return KVEPI_ERR_SHAPE;
+  if (c->block_num > INT32_MAX || c->block_size > INT32_MAX ||
+      c->block_num * c->block_size > INT32_MAX)
+    return KVEPI_ERR_SHAPE;
+  if (c->head_dim < min_cols) return KVEPI_ERR_SHAPE;
+  if (c->head_dim > (INT64_C(1) << 40) / c->block_size) return KVEPI_ERR_SHAPE;
+  if (c->block_stride < c->block_size * c->head_dim) return KVEPI_ERR_LAYOUT;
+  if (c->block_stride > (INT64_C(1) << 46) / c->block_num) return KVEPI_ERR_SHAPE;
+  if (elem == 2 && !aligned(c->data, 2)) return KVEPI_ERR_LAYOUT;
+  *pitch = c->head_dim * elem;
+  *bstride = c->block_stride * elem;
+  *align = min_align(pow2_align(reinterpret_cast<uintptr_t>(c->data)),
+                     min_align(pow2_align((uint64_t)*pitch),
+                               pow2_align((uint64_t)*bstride)));
+  return KVEPI_OK;
+}
+
+}  // namespace
+
+kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
+                            int64_t x_row_stride, const void *gamma,
+                            const void *cos, const void *sin,
+                            const int32_t *slot_mapping,
+                            const kvepi_cache *cache,
+                            const kvepi_cache *cache_aux, int32_t quant_mode,
+                            int32_t group_size, float eps, kvepi_plan *p) {
+  if (quant_mode == KVEPI_MODE_HIF8_FP4) return KVEPI_ERR_UNSUPPORTED;
+  int64_t cc = 0, kc = 0, sc = 0;
+  kvepi_status st = row_geometry(quant_mode, d, group_size, &cc, &kc, &sc);
+  if (st != KVEPI_OK) return st;
+
+  if (num_tokens < 0 || num_tokens > INT32_MAX) return KVEPI_ERR_SHAPE;
+  if (num_tokens > 0 && (x == nullptr || slot_mapping == nullptr))
+    return KVEPI_ERR_NULLPTR;
+  if (x_row_stride < d || x_row_stride % 8 != 0) return KVEPI_ERR_LAYOUT;
+  if (x != nullptr && !aligned(x, 16)) return KVEPI_ERR_LAYOUT;
+  if (slot_mapping != nullptr && !aligned(slot_mapping, 4))
+    return KVEPI_ERR_LAYOUT;
+
+  const bool has_norm = gamma != nullptr;
+  const bool has_rope = cos != nullptr || sin != nullptr;
+  if (has_rope && (cos == nullptr || sin == nullptr)) return KVEPI_ERR_PARAM;
+  if (quant_mode == KVEPI_MODE_MXFP4 && (has_norm || has_rope))
+    return KVEPI_ERR_UNSUPPORTED;
+  if (quant_mode == KVEPI_MODE_BF16_SPLIT && (!has_norm || !has_rope))
+    return KVEPI_ERR_PARAM;
+  if (has_norm && (!isfinite(eps) || eps < 0.0f)) return KVEPI_ERR_PARAM;
+  if (has_norm && !aligned(gamma, 16)) return KVEPI_ERR_LAYOUT;
+  if (has_rope && (!aligned(cos, 16) || !aligned(sin, 16)))
+    return KVEPI_ERR_LAYOUT;
+
+  const bool needs_aux =
+      quant_mode == KVEPI_MODE_MXFP4 || quant_mode == KVEPI_MODE_BF16_SPLIT;
+  if (needs_aux && cache_aux == nullptr) return KVEPI_ERR_NULLPTR;
+  if (!needs_aux && cache_aux != nullptr) return KVEPI_ERR_PARAM;
+
+  const int64_t elem = quant_mode == KVEPI_MODE_BF16_SPLIT ? 2 : 1;
+  kvepi_plan q{};
+  st = check_cache(cache, elem, kc, &q.c_pitch, &q.c_bstride, &q.c_align);
+  if (st != KVEPI_OK) return st;
+  if (needs_aux) {
+    st = check_cache(cache_aux, elem, sc, &q.a_pitch, &q.a_bstride, &q.a_align);
+    if (st != KVEPI_OK) return st;
+    if (cache_aux->block_num != cache->block_num ||
+        cache_aux->block_size != cache->block_size)
+      return KVEPI_ERR_SHAPE;
+  }
+
+  if (p != nullptr) {
+    q.mode = quant_mode;
+    q.norm = has_norm;
+    q.rope = has_rope;
+    q.T = num_tokens;
+    q.d = d;
+    q.nope = quant_mode == KVEPI_MODE_MXFP4 ? d : d - 64;
+    q.x_stride = x_row_stride;
+    q.x = static_cast<const uint16_t *>(x);
+    q.gamma = static_cast<const uint16_t *>(gamma);
+    q.cos = static_cast<const uint16_t *>(cos);
+    q.sin = static_cast<const uint16_t *>(sin);
+    q.slots = slot_mapping;
+    q.cache = static_cast<uint8_t *>(cache->data);
+    q.aux = needs_aux ? static_cast<uint8_t *>(cache_aux->data) : nullptr;
+    q.block_size = cache->block_size;
+    q.num_slots = cache->block_num * cache->block_size;
+    q.concat_col = cc;
+    q.kv_cache_col = kc;
+    q.scale_col = sc;
+    q.eps = eps;
+    *p = q;
+  }
+  return KVEPI_OK;
+}
+
+extern "C" {
+
+kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t group_size,
+                             int64_t *concat_col, int64_t *kv_cache_col,
+                             int64_t *scale_col) {
+  if (quant_mode == KVEPI_MODE_HIF8_FP4) return KVEPI_ERR_UNSUPPORTED;
+  int64_t cc = 0, kc = 0, sc = 0;
+  kvepi_status st = row_geometry(quant_mode, d, group_size, &cc, &kc, &sc);
+  if (st != KVEPI_OK) return st;
+  if (concat_col) *concat_col = cc;
+  if (kv_cache_col) *kv_cache_col = kc;
+  if (scale_col) *scale_col = sc;
+  return KVEPI_OK;
+}
+
+kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, int64_t d,
+                                 int64_t x_row_stride, const void *gamma,
+                                 const void *cos, const void *sin,
+                                 const int32_t *slot_mapping,
+                                 const kvepi_cache *cache,
+                                 const kvepi_cache *cache_aux,
+                                 int32_t quant_mode, int32_t group_size,
+                                 float eps, uint64_t *workspace_bytes) {
+  if (workspace_bytes == nullptr) return KVEPI_ERR_NULLPTR;
+  kvepi_status st =
+      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
+                     slot_mapping, cache, cache_aux, quant_mode, group_size,
+                     eps, nullptr);
+  if (st != KVEPI_OK) return st;
+  *workspace_bytes = 0;
+  return KVEPI_OK;
+}
+
+kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
+                       int64_t x_row_stride, const void *gamma,
+                       const void *cos, const void *sin,
+                       const int32_t *slot_mapping, const kvepi_cache *cache,
+                       const kvepi_cache *cache_aux, int32_t quant_mode,
+                       int32_t group_size, float eps, void *workspace,
+                       uint64_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;  // the epilog needs no workspace (size 0)
+  kvepi_plan plan;
+  kvepi_status st =
+      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
+                     slot_mapping, cache, cache_aux, quant_mode, group_size,
+                     eps, &plan);
+  if (st != KVEPI_OK) return st;
+  if (plan.T == 0) return KVEPI_OK;
+  return kvepi_launch(plan, stream);
+}
+
+const char *kvepi_status_str(kvepi_status s) {
+  switch (s) {
+    case KVEPI_OK: return "KVEPI_OK";
+    case KVEPI_ERR_NULLPTR: return "KVEPI_ERR_NULLPTR: a required pointer is NULL";
+    case KVEPI_ERR_SHAPE: return "KVEPI_ERR_SHAPE: a size violates the operation's constraints";
+    case KVEPI_ERR_LAYOUT: return "KVEPI_ERR_LAYOUT: invalid stride, alignment or cache layout";
+    case KVEPI_ERR_PARAM: return "KVEPI_ERR_PARAM: invalid group size, eps or optional-input combination";
+    case KVEPI_ERR_UNSUPPORTED: return "KVEPI_ERR_UNSUPPORTED: quant mode or combination not implemented";
+    case KVEPI_ERR_WORKSPACE: return "KVEPI_ERR_WORKSPACE: workspace too small";
+    case KVEPI_ERR_RUNTIME: return "KVEPI_ERR_RUNTIME: the HIP runtime refused the launch";
+  }
+  return "KVEPI_ERR_UNKNOWN";
+}
+
+int32_t kvepi_version(void) { return KVEPI_VERSION; }
+
+}  // extern "C"

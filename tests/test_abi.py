@@ -1,0 +1,175 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/kvepi.h declares, reports the page's row geometry, and rejects bad
+arguments before any launch (validation is pure host code; device pointers
+are only checked for NULL and alignment, never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_epilog_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvepi.h")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KVEPI_API\s+[\w\s\*]*?\b(kvepi_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == {"kvepi_row_bytes", "kvepi_get_workspace", "kvepi_run",
+                          "kvepi_status_str", "kvepi_version"}
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_only_the_c_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert funcs == set(declared_functions()), funcs
+
+
+def test_version_and_status_strings():
+    assert B.kvepi_version() == 100
+    for code, name in B.STATUS_NAMES.items():
+        assert B.kvepi_status_str(code).startswith(name)
+    assert "UNKNOWN" in B.kvepi_status_str(99)
+
+
+def _golden_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "row_bytes.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append(tuple(int(v) for v in line.split()[:6]))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_rows())
+def test_row_bytes_page_values(row):
+    mode, d, g, cc, kc, sc = row
+    assert B.kvepi_row_bytes(mode, d, g) == (cc, kc, sc)
+
+
+@pytest.mark.parametrize("mode,d,g,status", [
+    (2, 256, 64, 5), (7, 256, 64, 5), (0, 100, 64, 2), (0, 64, 64, 2), (1, 8256, 64, 2),
+    (0, 256, 32, 4), (3, 48, 32, 2), (3, 128, 64, 4), (3, 8224, 32, 2)])
+def test_row_bytes_rejects(mode, d, g, status):
+    with pytest.raises(B.KvepiError) as e:
+        B.kvepi_row_bytes(mode, d, g)
+    assert e.value.status == status
+
+
+# ---- validation through both stages, with fake (never dereferenced) pointers --
+
+P16 = 0x10000  # 16-byte-aligned stand-in device addresses
+P16B = 0x20000
+P16C = 0x30000
+P16D = 0x40000
+
+
+def _cache(data=0x50000, bn=8, bs=16, hd=352, stride=None):
+    return B.kvepi_cache(data, bn, bs, hd, bs * hd if stride is None else stride)
+
+
+def call(stage, *, x=P16, T=64, d=256, xs=None, gamma=None, cos=None, sin=None, slots=P16B,
+         cache=None, aux=None, mode=0, group=64, eps=1e-6, ws_bytes=0):
+    L = B.lib()
+    cache = _cache() if cache is None else cache
+    xs = d if xs is None else xs
+    cp = ctypes.byref(cache) if cache is not False else None
+    ap = ctypes.byref(aux) if aux is not None else None
+    if stage == 1:
+        ws = ctypes.c_uint64(123)
+        st = L.kvepi_get_workspace(x, T, d, xs, gamma, cos, sin, slots, cp, ap, mode, group,
+                                   ctypes.c_float(eps), ctypes.byref(ws))
+        return st, ws.value
+    # stage 2: a valid call would launch -- only invalid calls are made here
+    st = L.kvepi_run(x, T, d, xs, gamma, cos, sin, slots, cp, ap, mode, group,
+                     ctypes.c_float(eps), None, ws_bytes, None)
+    return st, None
+
+
+def test_valid_call_reports_zero_workspace():
+    assert call(1) == (0, 0)
+    assert call(1, T=0, x=None, slots=None) == (0, 0)
+    assert call(1, d=576, cache=_cache(hd=672), gamma=P16C, cos=P16D, sin=P16D + 0x1000) == (0, 0)
+    aux = _cache(data=0x60000, hd=4)
+    assert call(1, d=128, mode=3, group=32, cache=_cache(hd=64), aux=aux) == (0, 0)
+    assert call(1, d=576, mode=1, cache=_cache(hd=648)) == (0, 0)
+    ckv = _cache(hd=512)
+    k = _cache(data=0x70000, hd=64)
+    assert call(1, d=576, mode=4, cache=ckv, aux=k, gamma=P16C, cos=P16D,
+                sin=P16D + 0x1000) == (0, 0)
+
+
+BAD = [
+    # (description, kwargs, expected status)
+    ("mode 2 (HiFloat8)", dict(mode=2), 5),
+    ("unknown mode", dict(mode=9), 5),
+    ("d not a multiple of 64", dict(d=200), 2),
+    ("d too large", dict(d=8256), 2),
+    ("group size", dict(group=32), 4),
+    ("negative T", dict(T=-1), 2),
+    ("null x", dict(x=None), 1),
+    ("null slots", dict(slots=None), 1),
+    ("null cache", dict(cache=False), 1),
+    ("null cache data", dict(cache=B.kvepi_cache(None, 8, 16, 352, 16 * 352)), 1),
+    ("x misaligned", dict(x=P16 + 2), 3),
+    ("x row stride < d", dict(xs=128), 3),
+    ("x row stride not 16 B", dict(xs=260), 3),
+    ("slots misaligned", dict(slots=P16B + 2), 3),
+    ("cos without sin", dict(cos=P16C), 4),
+    ("negative eps", dict(gamma=P16C, eps=-1.0), 4),
+    ("nan eps", dict(gamma=P16C, eps=float("nan")), 4),
+    ("gamma misaligned", dict(gamma=P16C + 8), 3),
+    ("headDim below kvCacheCol", dict(cache=_cache(hd=351)), 2),
+    ("block stride too small", dict(cache=_cache(stride=16 * 352 - 1)), 3),
+    ("zero blocks", dict(cache=_cache(bn=0)), 2),
+    ("num_slots over int32", dict(cache=_cache(bn=1 << 20, bs=1 << 12)), 2),
+    ("aux given to mode 0", dict(aux=_cache(hd=4)), 4),
+    ("mxfp4 without cache_scale", dict(mode=3, d=128, group=32, cache=_cache(hd=64)), 1),
+    ("mxfp4 with gamma", dict(mode=3, d=128, group=32, cache=_cache(hd=64), gamma=P16C,
+                              aux=_cache(hd=4)), 5),
+    ("mxfp4 cache_scale too narrow", dict(mode=3, d=128, group=32, cache=_cache(hd=64),
+                                          aux=_cache(hd=3)), 2),
+    ("mxfp4 cache_scale other block count", dict(mode=3, d=128, group=32,
+                                                 cache=_cache(hd=64), aux=_cache(bn=4, hd=4)), 2),
+    ("split without rope", dict(mode=4, d=576, gamma=P16C, cache=_cache(hd=512),
+                                aux=_cache(hd=64)), 4),
+    ("split k cache too narrow", dict(mode=4, d=576, gamma=P16C, cos=P16D, sin=P16D,
+                                      cache=_cache(hd=512), aux=_cache(hd=63)), 2),
+    ("split ckv misaligned", dict(mode=4, d=576, gamma=P16C, cos=P16D, sin=P16D,
+                                  cache=_cache(data=0x50001, hd=512), aux=_cache(hd=64)), 3),
+]
+
+
+@pytest.mark.parametrize("desc,kw,status", BAD, ids=[b[0] for b in BAD])
+@pytest.mark.parametrize("stage", [1, 2])
+def test_rejects(desc, kw, status, stage):
+    st, _ = call(stage, **kw)
+    assert st == status, (desc, B.kvepi_status_str(st))
+
+
+def test_workspace_out_pointer_required():
+    L = B.lib()
+    c = _cache()
+    st = L.kvepi_get_workspace(P16, 64, 256, 256, None, None, None, P16B, ctypes.byref(c), None,
+                               0, 64, ctypes.c_float(1e-6), None)
+    assert st == 1
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

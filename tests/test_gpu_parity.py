@@ -1,0 +1,175 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every test compares the whole cache allocation byte for byte (plus guard
+bytes around it), so routing, skipped tokens, untouched rows, block gaps and
+bytes past kvCacheCol are all checked, not only the written rows."""
+import numpy as np
+import pytest
+
+import kvgen
+from kvgen import CacheSpec
+
+from parity import check, compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(mode, T, d, *, seed, bs=16, head=None, stride_extra=0, aux_head=None,
+           norm=False, rope=False, skip=0.1, row_sigma=0.0, **kw):
+    import oracle
+    _, kc, sc = oracle.row_bytes(mode, d, 32 if mode == 3 else 64) if mode != 4 else (0, d - 64, 64)
+    head = head or kc
+    nblk = (T + bs - 1) // bs + 2
+    cache = CacheSpec(nblk, bs, head, bs * head + stride_extra, 2 if mode == 4 else 1)
+    aux = None
+    if mode == 3:
+        ah = aux_head or sc
+        aux = CacheSpec(nblk, bs, ah, bs * ah + stride_extra)
+    elif mode == 4:
+        ah = aux_head or 64
+        aux = CacheSpec(nblk, bs, ah, bs * ah + stride_extra, 2)
+    return kvgen.make(f"m{mode}_d{d}_T{T}", mode, T, d, seed=seed, cache=cache, aux=aux,
+                      norm=norm, rope=rope, skip_frac=skip, row_sigma=row_sigma, **kw)
+
+
+# ---- the five named workloads at full size ----------------------------------
+
+@pytest.mark.parametrize("i", range(5))
+def test_config_parity(i):
+    w = kvgen.config(i)
+    n = check(w, label=f"config {i} {w.name}")
+    print(f"config {i} {w.name}: T={w.T} hits={w.hits} one-step code diffs={n}", flush=True)
+
+
+def test_config_repeat_is_deterministic():
+    w = kvgen.config(2)
+    a, _ = run_gpu(w)
+    b, _ = run_gpu(w, repeat=3)
+    assert np.array_equal(a, b)
+
+
+# ---- shape sweeps ---------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("d", [128, 192, 256, 384, 576, 640, 1088, 2112, 4160, 8192])
+@pytest.mark.parametrize("norm,rope", [(False, False), (True, True), (True, False),
+                                       (False, True)])
+def test_fp8_modes_sweep(mode, d, norm, rope):
+    T = 300 if d <= 1088 else 80
+    w = _small(mode, T, d, seed=d + 7 * mode + 3 * norm + rope, bs=7, stride_extra=40,
+               norm=norm, rope=rope, row_sigma=1.5)
+    check(w)
+
+
+@pytest.mark.parametrize("d", [128, 192, 256, 576, 1088, 4160, 8192])
+def test_bf16_split_sweep(d):
+    w = _small(4, 200, d, seed=d, bs=5, stride_extra=8, norm=True, rope=True, row_sigma=1.0)
+    check(w)
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 160, 256, 512, 1024, 4096, 8192])
+def test_mxfp4_sweep(d):
+    w = _small(3, 400 if d <= 1024 else 60, d, seed=d, bs=3, stride_extra=5, row_sigma=2.0)
+    check(w)
+
+
+# ---- layouts and alignment ----------------------------------------------------------
+
+@pytest.mark.parametrize("offset", [0, 1, 2, 4, 8])
+def test_mode1_head_dim_323_any_alignment(offset):
+    # the page's example row (d=256, mode 1 -> 323 bytes) packed at headDim 323
+    w = _small(1, 250, 256, seed=11, bs=32, head=323)
+    check(w, offset=offset)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2, 6])
+def test_mode0_odd_head_dim(offset):
+    w = _small(0, 250, 576, seed=12, bs=9, head=681, stride_extra=3, norm=True, rope=True)
+    check(w, offset=offset)
+
+
+@pytest.mark.parametrize("offset,aux_offset", [(0, 0), (1, 3), (4, 1)])
+def test_mxfp4_odd_layout(offset, aux_offset):
+    w = _small(3, 300, 128, seed=13, bs=11, head=67, aux_head=5, stride_extra=1)
+    check(w, offset=offset, aux_offset=aux_offset)
+
+
+@pytest.mark.parametrize("bs", [1, 2, 3, 100, 128, 1000])
+def test_block_sizes(bs):
+    w = _small(0, 500, 576, seed=bs, bs=bs, stride_extra=32, norm=True, rope=True)
+    check(w)
+
+
+def test_strided_x_rows():
+    w = _small(0, 200, 576, seed=14, norm=True, rope=True)
+    check(w, x_pad=64)
+
+
+def test_non_default_stream():
+    import torch
+    w = _small(1, 200, 576, seed=15)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got, agot = run_gpu(w, stream=s)
+    want, awant = run_oracle(w)
+    compare(w, got, want, agot, awant)
+
+
+# ---- degenerate inputs ------------------------------------------------------------------
+
+def test_zero_tokens_is_noop():
+    import torch
+    from kv_cache_epilog_amd import kvepi_run
+    w = _small(0, 16, 256, seed=16)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    slots = torch.empty((0,), dtype=torch.int32, device="cuda")
+    from parity import cache_tensor
+    cache, flat = cache_tensor(w.cache, w.cache_init, "cuda")
+    kvepi_run(x, slots, cache, 0, 64)
+    torch.cuda.synchronize()
+    assert np.all(flat.cpu().numpy() == kvgen.PREFILL)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 3, 4])
+def test_all_skipped_and_out_of_range(mode):
+    d = 128 if mode == 3 else 576
+    w = _small(mode, 200, d, seed=17, norm=mode == 4, rope=mode == 4)
+    w.slots[:100] = -1
+    w.slots[100:] = w.cache.num_slots + np.arange(100)
+    w.slots[150] = -7
+    w.slots[151] = np.iinfo(np.int32).max
+    got, agot = run_gpu(w)
+    assert np.all(got == kvgen.PREFILL)
+    if agot is not None:
+        assert np.all(agot == kvgen.PREFILL)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 3, 4])
+def test_special_values(mode):
+    # zero rows and groups, negative zeros, bf16 subnormals, huge values and
+    # exact ties: exercises the exact-division fallbacks and code rounding.
+    rng = np.random.default_rng(18)
+    d = 128 if mode == 3 else 576
+    T = 64
+    x = rng.standard_normal((T, d))
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, :64] = 0.0
+    x[3] = rng.standard_normal(d) * 1e-39                 # bf16 subnormals
+    x[4] = rng.standard_normal(d) * 1e30
+    x[5] = rng.standard_normal(d) * 3e38                  # near the bf16 maximum
+    x[6] = np.where(rng.random(d) < 0.5, -0.0, 0.0)
+    x[7, ::2] = 448.0
+    x[8] = np.round(rng.standard_normal(d) * 8) / 16      # many exact ties
+    x[9] = rng.standard_normal(d) * 2.0 ** -120
+    x[10, 5] = 1e-40                                      # one subnormal in a normal row
+    x[11] = 1.0
+    xb = kvgen.to_bf16(x)
+    w = _small(mode, T, d, seed=19, skip=0.0, norm=mode in (0, 4), rope=mode in (0, 4), x=xb)
+    check(w)
+    if mode in (0, 1):
+        w0 = _small(mode, T, d, seed=19, skip=0.0, norm=True, rope=False, x=xb, eps=0.0)
+        w0.x[0] = kvgen.to_bf16(np.ones(d))  # an all-zero row with eps 0 is undefined
+        w0.x[1] = w0.x[0]
+        w0.x[6] = w0.x[0]
+        check(w0)
