@@ -1,0 +1,212 @@
+"""Benchmark of the fused KV-cache write epilog on one MI355X.
+
+A step is one kvepi_run over the whole workload: 262144 bf16 token rows of
+d = 576, RMSNorm over the 512 nope columns, interleaved RoPE over the last 64,
+group-64 FP8 E4M3 quantisation with bf16 scales, scattered as 672-byte rows
+into a paged cache [2048, 128, 1, 672] whose block stride is 1.25x the dense
+one, 3% of the tokens skipped.  Inputs are seeded synthetic data resident in
+HBM before timing starts.
+
+Prints one JSON line: tokens/s (T / kernel time), plus the roofline of the
+epilog kernel (algorithmic bytes per launch / mean launch time, against the
+8 TB/s HBM peak) and the CPU oracle timed on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import kvgen  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "tokens/s and effective HBM GB/s (% of peak), d=576 fused epilog"
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_epilog_amd", "csrc", "kvepi_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(w: kvgen.Workload) -> int:
+    """Bytes the method must move: 4 B slot per token; for every hit row the
+    x row (plus its cos and sin rows with RoPE) and the bytes written; gamma
+    once."""
+    from kv_cache_epilog_amd import kvepi_row_bytes
+    hits = w.hits
+    x_row = 2 * w.d
+    rope = 2 * 2 * 64 if w.cos is not None else 0
+    if w.mode == kvgen.MODE_BF16_SPLIT:
+        written = 2 * (w.d - 64) + 2 * 64
+    elif w.mode == kvgen.MODE_MXFP4:
+        _, kc, sc = kvepi_row_bytes(w.mode, w.d, w.group_size)
+        written = kc + sc
+    else:
+        _, kc, _ = kvepi_row_bytes(w.mode, w.d, w.group_size)
+        written = kc
+    gamma = 2 * (w.d - 64) if w.gamma is not None else 0
+    return 4 * w.T + hits * (x_row + rope + written) + gamma
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on another kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def upload(w: kvgen.Workload, dev):
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def cache(spec, init):
+        flat = torch.from_numpy(init).to(dev)
+        if spec.elem_bytes == 2:
+            flat = flat.view(torch.bfloat16)
+        view = flat.as_strided((spec.block_num, spec.block_size, 1, spec.head_dim),
+                               (spec.block_stride, spec.head_dim, spec.head_dim, 1))
+        return view, flat
+
+    t = dict(x=bf(w.x), slots=torch.from_numpy(w.slots).to(dev),
+             gamma=None if w.gamma is None else bf(w.gamma),
+             cos=None if w.cos is None else bf(w.cos), sin=None if w.sin is None else bf(w.sin))
+    t["cache"], t["cache_flat"] = cache(w.cache, w.cache_init)
+    t["aux"] = t["aux_flat"] = None
+    if w.aux is not None:
+        t["aux"], t["aux_flat"] = cache(w.aux, w.aux_init)
+    return t
+
+
+def cpu_baseline(w: kvgen.Workload, max_seconds: float):
+    """The oracle as it stands (single-threaded C) on the same workload, on
+    leading tokens until about max_seconds of CPU time."""
+    import oracle
+    cache = w.cache_init.copy()
+    aux = None if w.aux_init is None else w.aux_init.copy()
+    # calibrate on a small prefix, then size the sample
+    probe = min(w.T, 2048)
+    t0 = time.perf_counter()
+    _run_oracle_prefix(oracle, w, probe, cache, aux)
+    dt = time.perf_counter() - t0
+    n = int(min(w.T, max(probe, probe * max_seconds / max(dt, 1e-6))))
+    cache = w.cache_init.copy()
+    aux = None if w.aux_init is None else w.aux_init.copy()
+    t0 = time.perf_counter()
+    _run_oracle_prefix(oracle, w, n, cache, aux)
+    dt = time.perf_counter() - t0
+    return n, dt, cache, aux
+
+
+def _run_oracle_prefix(oracle, w, n, cache, aux):
+    oracle.epilog(w.mode, w.x[:n], w.slots[:n], cache, w.cache.geom, group_size=w.group_size,
+                  gamma=w.gamma, cos=None if w.cos is None else w.cos[:n],
+                  sin=None if w.sin is None else w.sin[:n], eps=w.eps, aux_bytes=aux,
+                  aux_geom=None if w.aux is None else w.aux.geom)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload index (default 4: the d=576 fused epilog)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cache_epilog_amd import kvepi_run
+
+    w = kvgen.config(args.config)
+    dev = torch.device("cuda:0")
+    t = upload(w, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kvepi_run(t["x"], t["slots"], t["cache"], w.mode, w.group_size, gamma=t["gamma"],
+                  cos=t["cos"], sin=t["sin"], cache_aux=t["aux"], eps=w.eps, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch HIP events on the launch stream: mean kernel time
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    total0 = torch.cuda.Event(enable_timing=True)
+    total1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    total0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    total1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = total0.elapsed_time(total1)
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_kernel = float(per.mean())
+    ms_per_step = ms_total / args.steps
+
+    abytes = algorithmic_bytes(w)
+    achieved = abytes / (ms_kernel * 1e-3) / 1e9
+    tokens_per_s = w.T / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "tokens": w.T, "d": w.d, "quant_mode": w.mode,
+                   "group_size": w.group_size, "rmsnorm": w.gamma is not None,
+                   "rope": w.cos is not None, "hit_rows": w.hits,
+                   "cache": [w.cache.block_num, w.cache.block_size, 1, w.cache.head_dim],
+                   "block_stride_bytes": w.cache.block_stride * w.cache.elem_bytes,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name),
+                     "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms_kernel,
+                     "kernel_ms_min": float(per.min())},
+    }
+    if not args.no_cpu:
+        n, dt, ocache, oaux = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of {w.name}, single-threaded C oracle, "
+                      f"{dt:.1f} s"}
+        # the timed GPU path wrote the same rows: compare the tokens the
+        # oracle covered
+        got = t["cache_flat"].view(torch.uint8).cpu().numpy()
+        rows = [w.cache.row_offset(s) for s in w.slots[:n] if 0 <= s < w.cache.num_slots]
+        kc = w.cache.head_dim * w.cache.elem_bytes
+        idx = (np.asarray(rows)[:, None] + np.arange(kc)[None, :]).reshape(-1)
+        result["parity_sample_bytes_equal"] = bool(np.array_equal(got[idx], ocache[idx]))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -152,7 +152,8 @@ template <int FE, uint32_t FM>
 __device__ __forceinline__ int e8m0_exp(float amax) {
   const uint32_t u = __float_as_uint(amax);
   const int eb = (int)(u >> 23);
-  if (eb == 0) return -127;  // zero or subnormal amax: below fmax * 2^-127
+  if (eb == 0) return -127;   // zero or subnormal amax: below fmax * 2^-127
+  if (eb == 255) return 127;  // infinite amax: the largest scale
   int E = eb - 127 - FE + (int)((u & 0x7FFFFFu) > FM);
   return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
@@ -435,18 +436,24 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
         } else {
           // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
           // stored value
-          const float s32 = m >= 0x1p-100f ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
+          const float s32 =
+              (m >= 0x1p-100f && m <= 0x1p+100f) ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
           sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
           const float su = __uint_as_float(sbits << 16);
-          // below 2^-80 a residual of the fast division could underflow for a
-          // quotient that still matters; such groups divide exactly
-          if (su >= 0x1p-80f) {
+          // Outside [2^-80, 2^100] a residual or the reciprocal of the fast
+          // division could leave the normal range; such groups divide
+          // exactly.  An infinite scale (an infinite RMSNorm output) gives
+          // +-0 for finite values and the NaN code 0x7F for inf / inf.
+          if (su >= 0x1p-80f && su <= 0x1p+100f) {
             const float rs = 1.0f / su;
 #pragma unroll
             for (int k = 0; k < 8; ++k) q[k] = enc_e4m3(div_fast(v[k], su, rs));
           } else if (su > 0.0f) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = enc_e4m3(v[k] / su);
+            for (int k = 0; k < 8; ++k) {
+              const float qq = v[k] / su;
+              q[k] = qq != qq ? 0x7Fu : enc_e4m3(qq);
+            }
           } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) q[k] = 0u;

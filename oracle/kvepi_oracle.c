@@ -83,7 +83,11 @@ static double rne(double a) { return nearbyint(a); }
  * "aclnnDequantRopeQuantKvcache" kernel walkthrough. */
 uint8_t kvo_enc_e4m3(float v) {
   uint8_t sign = signbit(v) ? 0x80 : 0x00;
-  if (isnan(v)) return (uint8_t)(sign | 0x7F);
+  /* A NaN quotient (inf / inf, when an infinite RMSNorm output meets an
+   * infinite bf16 scale) gets the format's positive NaN code 0x7F: the sign
+   * of a NaN produced by an invalid operation differs between processors,
+   * so it carries no information. */
+  if (isnan(v)) return 0x7F;
   double a = fabs((double)v);
   if (a > 448.0) return (uint8_t)(sign | 0x7E);
   if (a < ldexp(1.0, -6)) {
@@ -138,6 +142,7 @@ uint8_t kvo_enc_e2m1(float v) {
  * produced).  amax == 0 gives -127. */
 int kvo_e8m0_exponent(float amax, float fmax) {
   if (!(amax > 0.0f)) return -127;
+  if (isinf(amax)) return 127;
   double a = (double)amax, f = (double)fmax;
   int E;
   frexp(a / f, &E); /* a/f in [2^(E-1), 2^E) up to binary64 rounding */
