@@ -1,10 +1,22 @@
 // kvepi_kernels.hip -- gfx950 kernels of the fused KV-cache write epilog.
 //
 // One kernel template covers every mode.  A token row is handled by a group
-// of L lanes of one 64-lane wavefront (L = 64 for the d = 576 rows, 16 for
-// the d = 128 indexer rows, so a wave carries 64/L rows at once); each lane
-// owns C 16-byte chunks of 8 bf16 values, chunk index li + L*j, so every
-// load instruction of a wave reads L*16 contiguous bytes of a row.
+// of L lanes of one 64-lane wavefront (64/L rows per wave-iteration: L = 32,
+// two rows per wave, for the d = 576 rows; L = 16, four rows, for the d = 128
+// indexer rows).  Each lane owns C 16-byte chunks of 8 bf16 values, chunk
+// index li + L*j, so every load instruction reads L*16 contiguous bytes of a
+// row.  The path is bound by HBM bandwidth; the design keeps the VALU work
+// per row small enough that the wave scheduler can keep the loads flowing:
+//  - waves are persistent; each wave preloads the slots of its next rows in
+//    one load and issues the next row's loads before computing the current
+//    one (two register sets, manual double buffering);
+//  - the rope segment is spread over 32 lanes (one output pair each);
+//  - codes come from the gfx950 converts v_cvt_pk_fp8_f32 /
+//    v_cvt_scalef32_pk_fp8_f32 / v_cvt_scalef32_pk_fp4_f32, which round to
+//    nearest even exactly like the reference encoders over the value ranges
+//    used here (|q| <= 448 for FP8, |q| <= 6 for FP4, power-of-two scales in
+//    [2^-100, 2^100]); outside those ranges a group falls back to software
+//    encoding.
 //
 // Steps per row (sources cited by page title and section):
 //  1. slot = slot_mapping[t]; -1 (or any value outside [0, num_slots)) skips
@@ -12,21 +24,20 @@
 //     ("aclnnKvCompressEpilog", 约束说明).
 //  2. RMSNorm of the nope segment ("aclnnKvRmsNormRopeCache", 计算公式 (2)):
 //     squares summed as a balanced pairwise tree -- within a lane over its 8
-//     values, then across lanes by a DPP / ds_swizzle butterfly whose
-//     pairing is exactly the tree's (fp32 addition is commutative, so both
-//     lanes of a pair hold the same node), then over the chunk index j;
-//     mean = sum / n, rms = sqrt(mean + eps), t = x / rms, u = t * gamma,
-//     bf16 output.  All in IEEE fp32; x / rms uses the reciprocal with one
-//     FMA correction (Markstein), which returns the correctly rounded
-//     quotient for a bf16 numerator and a normal result -- the row falls
-//     back to full division when that cannot be guaranteed.
+//     values, then across lanes by a DPP / ds_swizzle butterfly whose pairing
+//     is exactly the tree's (fp32 addition is commutative, so both lanes of a
+//     pair hold the same node), then over the chunk index j; mean = sum / n,
+//     rms = sqrt(mean + eps), t = x / rms, u = t * gamma, bf16 output.  All in
+//     IEEE fp32; x / rms uses the reciprocal with one FMA correction
+//     (Markstein), which returns the correctly rounded quotient for a bf16
+//     numerator and a normal result -- a row falls back to full division when
+//     that cannot be guaranteed.
 //  3. Interleaved RoPE of the last 64 columns, half-split output
 //     ("aclnnKvRmsNormRopeCache", 计算公式 (1)).
 //  4. Per-group amax (DPP max over the 8 or 4 lanes of a group), the scale
 //     ("aclnnKvCompressEpilog", 计算公式: amax / 448 as bf16, or the e8m0
-//     power of two rounded up; "indexer_quant_cache": e8m0 over groups of
-//     32 with FP4 max 6) and the codes, round-to-nearest-even with
-//     saturation.
+//     power of two rounded up; "indexer_quant_cache": e8m0 over groups of 32
+//     with FP4 max 6) and the codes, round-to-nearest-even with saturation.
 //  5. Stores of exactly kvCacheCol bytes at the slot's row; the widest store
 //     the row alignment allows is used (16/8/4/2/1 bytes), so odd headDim
 //     such as 323 works.
@@ -46,13 +57,17 @@ struct KArgs {
   int64_t a_pitch, a_bstride;  // bytes
   uint64_t bs_magic;           // slot / block_size == (slot * magic) >> shift
   int32_t bs_shift, block_size;
+  int32_t bs_log2;  // log2(block_size) if a power of two, else -1
   int32_t T, num_slots;
   int32_t nseg;    // values in the quantised/normalised segment (d-64, or d)
   int32_t nchunk;  // nseg / 8
   int32_t concat_col, kv_cache_col;
+  int32_t pad16;  // zero padding as whole 16-byte stores (count), -1: bytes
   int32_t c_align, a_align;
-  float eps, nseg_f;
+  float eps, inv_nseg;  // inv_nseg != 0: nseg is a power of two, mean = ss*inv
+  float nseg_f;
   int32_t nwaves;      // waves in the grid
+  int32_t n_groups;    // row groups (wave-iterations) = ceil(T / rows per wave)
   int32_t xcd_blocks;  // blocks per XCD for the XCD-major remap, 0 = off
 };
 
@@ -63,8 +78,8 @@ __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32), a low.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -76,6 +91,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 // lane ^ 16 inside each half of the wave (ds_swizzle bit-mask mode)
 __device__ __forceinline__ float swz_xor16(float v) {
@@ -100,32 +119,38 @@ __device__ __forceinline__ float grp_sum(float v) {
   return v;
 }
 
+// Max of non-negative floats over aligned groups of G (<= 8) lanes, as
+// unsigned integers (same order for non-negative IEEE values).
 template <int G>
-__device__ __forceinline__ float grp_max(float v) {
-  if constexpr (G >= 2) v = fmaxf(v, dpp<0xB1>(v));
-  if constexpr (G >= 4) v = fmaxf(v, dpp<0x4E>(v));
-  if constexpr (G >= 8) v = fmaxf(v, dpp<0x141>(v));
-  return v;
+__device__ __forceinline__ float grp_max(float f) {
+  uint32_t v = __float_as_uint(f);
+  if constexpr (G >= 2) v = max(v, dpp_u<0xB1>(v));
+  if constexpr (G >= 4) v = max(v, dpp_u<0x4E>(v));
+  if constexpr (G >= 8) v = max(v, dpp_u<0x141>(v));
+  return __uint_as_float(v);
 }
 
 // Correctly rounded a / b from rcp = RN(1 / b) with one FMA correction.
 // Exact for a bf16 numerator whenever the quotient is a normal fp32 number
-// (checked over every bf16 significand against every fp32 divisor
-// significand); the sign of a zero quotient is restored explicitly.
+// and |a| >= 2^-100 (checked over every bf16 significand against every fp32
+// divisor significand).  The last step is evaluated negated so that a zero
+// quotient keeps the sign of a: -(-r*rcp - q0).
 __device__ __forceinline__ float div_fast(float a, float b, float rcp) {
   const float q0 = a * rcp;
   const float r = __builtin_fmaf(-q0, b, a);
-  return __builtin_copysignf(__builtin_fmaf(r, rcp, q0), a);
+  return -__builtin_fmaf(-r, rcp, -q0);
 }
 
 // E4M3FN code of q: round to nearest even, |q| > 448 saturates to 448,
-// sign kept (also for zero).
-__device__ __forceinline__ uint32_t enc_e4m3(float q) {
+// sign kept (also for zero); a NaN gives 0x7F.
+__device__ __forceinline__ uint32_t enc_e4m3_sw(float q) {
   const uint32_t u = __float_as_uint(q);
   const uint32_t s = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7FFFFFFFu;
   uint32_t code;
-  if (a > 0x43E00000u) {          // > 448
+  if (a > 0x7F800000u) {
+    return 0x7Fu;
+  } else if (a > 0x43E00000u) {  // > 448
     code = 0x7Eu;
   } else if (a >= 0x3C800000u) {  // >= 2^-6: keep 3 mantissa bits, RNE
     const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
@@ -138,7 +163,7 @@ __device__ __forceinline__ uint32_t enc_e4m3(float q) {
 
 // E2M1 code (4 bits) of q: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the
 // even code, saturating at 6.
-__device__ __forceinline__ uint32_t enc_e2m1(float q) {
+__device__ __forceinline__ uint32_t enc_e2m1_sw(float q) {
   const float a = __builtin_fabsf(q);
   const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
                      (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
@@ -154,7 +179,7 @@ __device__ __forceinline__ int e8m0_exp(float amax) {
   const int eb = (int)(u >> 23);
   if (eb == 0) return -127;   // zero or subnormal amax: below fmax * 2^-127
   if (eb == 255) return 127;  // infinite amax: the largest scale
-  int E = eb - 127 - FE + (int)((u & 0x7FFFFFu) > FM);
+  const int E = eb - 127 - FE + (int)((u & 0x7FFFFFu) > FM);
   return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
@@ -205,16 +230,34 @@ __device__ __forceinline__ void st_u128(uint8_t *p, uint4 v, int al) {
 
 __device__ __forceinline__ uint8_t *row_addr(uint8_t *base, uint32_t s, const KArgs &a,
                                              int64_t pitch, int64_t bstride) {
-  const uint32_t blk = (uint32_t)(((uint64_t)s * a.bs_magic) >> a.bs_shift);
-  const uint32_t pos = s - blk * (uint32_t)a.block_size;
+  uint32_t blk, pos;
+  if (a.bs_log2 >= 0) {
+    blk = s >> a.bs_log2;
+    pos = s & ((1u << a.bs_log2) - 1u);
+  } else {
+    blk = (uint32_t)(((uint64_t)s * a.bs_magic) >> a.bs_shift);
+    pos = s - blk * (uint32_t)a.block_size;
+  }
   return base + (int64_t)blk * bstride + (int64_t)pos * pitch;
 }
 
+// Streamed inputs (read once) use nontemporal loads.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) {
-  return *reinterpret_cast<const uint4 *>(p);
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint2 ld8(const uint16_t *p) {
-  return *reinterpret_cast<const uint2 *>(p);
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld4(const uint16_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+// gamma is shared by every row: a plain (cached) load.
+__device__ __forceinline__ uint4 ld16_cached(const uint16_t *p) {
+  return *reinterpret_cast<const uint4 *>(p);
 }
 
 __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
@@ -229,260 +272,409 @@ __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
 // ------------------------------------------------------------------------
 enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4 };
 
-template <int MODE, bool NORM, bool ROPE, int L, int C>
-__global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
-  constexpr int R = 64 / L;  // rows per wave per iteration
-  const int lane = threadIdx.x & 63;
-  const int li = lane & (L - 1);
-  const int sub = lane / L;
-  int blk = blockIdx.x;
-  if (a.xcd_blocks > 0) blk = (blk & 7) * a.xcd_blocks + (blk >> 3);
-  const int wave = blk * 4 + (threadIdx.x >> 6);
+// Rope work is split into 32 tasks: task tau = 16h + p produces outputs
+// y[32h + 2p] and y[32h + 2p + 1] from the interleaved pairs 2p and 2p+1
+// (x[4p..4p+3]) and cos/sin[32h + 2p .. +1]; its 4 output bytes sit at rope
+// byte 4*tau, so the 32 tasks write the 128 rope bytes contiguously.
+template <int L>
+struct RopeShape {
+  static constexpr int TPL = L >= 32 ? 1 : 32 / L;  // tasks per lane
+};
 
-  // gamma of this lane's chunks, kept in registers across rows
-  constexpr bool KEEP_G = NORM && C <= 2;
-  uint4 gw[KEEP_G ? C : 1];
-  if constexpr (KEEP_G) {
+template <int MODE, bool ROPE, int L, int C>
+struct RowBuf {
+  static constexpr bool HAS_ROPE_SEG = MODE != M_MXFP4;
+  static constexpr int TPL = RopeShape<L>::TPL;
+  uint4 xw[C];
+  uint2 rx[HAS_ROPE_SEG ? TPL : 1];             // x[4p .. 4p+3] (or 2 copied values)
+  uint32_t rc[HAS_ROPE_SEG && ROPE ? TPL : 1];  // cos pair
+  uint32_t rs[HAS_ROPE_SEG && ROPE ? TPL : 1];  // sin pair
+};
+
+template <int MODE, bool NORM, bool ROPE, int L, int C>
+__device__ __forceinline__ void load_row(const KArgs &a, int64_t row, int li,
+                                         RowBuf<MODE, ROPE, L, C> &b) {
+  const uint16_t *xr = a.x + row * a.x_stride;
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const int c = li + L * j;
-      gw[j] = c < a.nchunk ? ld16(a.gamma + 8 * c) : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < C; ++j) {
+    const int c = li + L * j;
+    if (L * C == a.nchunk || c < a.nchunk)
+      b.xw[j] = ld16(xr + 8 * c);
+    else
+      b.xw[j] = make_uint4(0, 0, 0, 0);
+  }
+  if constexpr (RowBuf<MODE, ROPE, L, C>::HAS_ROPE_SEG) {
+    constexpr int TPL = RowBuf<MODE, ROPE, L, C>::TPL;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const int tau = li + L * k;
+      if (tau < 32) {
+        if constexpr (ROPE) {
+          const int p = tau & 15;
+          b.rx[k] = ld8(xr + a.nseg + 4 * p);
+          b.rc[k] = ld4(a.cos + row * 64 + 2 * tau);
+          b.rs[k] = ld4(a.sin + row * 64 + 2 * tau);
+        } else {
+          b.rx[k] = make_uint2(ld4(xr + a.nseg + 2 * tau), 0u);
+        }
+      }
     }
   }
+}
 
-  for (int64_t rg = wave; rg * R < a.T; rg += a.nwaves) {
-    const int64_t row = rg * R + sub;
-    int slot = row < a.T ? a.slots[row] : -1;
-    if constexpr (L == 64) slot = __builtin_amdgcn_readfirstlane(slot);
-    if ((uint32_t)slot >= (uint32_t)a.num_slots) continue;
+// A computed row waiting to be stored: destination pointers, code words
+// (or the bf16 ckv chunks), scale bits and rope words.
+template <int MODE, int L, int C>
+struct RowOut {
+  uint8_t *p0, *p1;
+  uint4 w[C];
+  uint32_t sb[C];
+  uint32_t ry[MODE == M_MXFP4 ? 1 : RopeShape<L>::TPL];
+};
 
-    const uint16_t *xr = a.x + row * a.x_stride;
-    uint4 xw[C];
+template <int MODE, bool NORM, bool ROPE, int L, int C>
+__device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int li, int sub,
+                                            const RowBuf<MODE, ROPE, L, C> &b,
+                                            const uint4 *g_lds, RowOut<MODE, L, C> &o) {
+  // ---- RMSNorm -> packed bf16 yw ----
+  uint4 yw[C];
+  if constexpr (NORM) {
+    float part[C];
+    float mn = __builtin_inff();
 #pragma unroll
     for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(b.xw[j], v);
+      const float s01 = v[0] * v[0] + v[1] * v[1];
+      const float s23 = v[2] * v[2] + v[3] * v[3];
+      const float s45 = v[4] * v[4] + v[5] * v[5];
+      const float s67 = v[6] * v[6] + v[7] * v[7];
+      part[j] = grp_sum<L>((s01 + s23) + (s45 + s67));
       const int c = li + L * j;
-      xw[j] = c < a.nchunk ? ld16(xr + 8 * c) : make_uint4(0, 0, 0, 0);
-    }
-    // rope chunk (lanes li < 8): 4 interleaved (a, b) pairs
-    uint4 rw = make_uint4(0, 0, 0, 0);
-    uint2 c0w, c1w, s0w, s1w;
-    if constexpr (MODE != M_MXFP4) {
-      if (li < 8) {
-        rw = ld16(xr + a.nseg + 8 * li);
-        if constexpr (ROPE) {
-          const uint16_t *cr = a.cos + row * 64;
-          const uint16_t *sr = a.sin + row * 64;
-          c0w = ld8(cr + 4 * li);
-          c1w = ld8(cr + 32 + 4 * li);
-          s0w = ld8(sr + 4 * li);
-          s1w = ld8(sr + 32 + 4 * li);
-        }
+      if (L * C == a.nchunk || c < a.nchunk) {
+        float m = __builtin_fminf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
+        m = __builtin_fminf(m, __builtin_fminf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+        m = __builtin_fminf(m, __builtin_fminf(__builtin_fabsf(v[4]), __builtin_fabsf(v[5])));
+        m = __builtin_fminf(m, __builtin_fminf(__builtin_fabsf(v[6]), __builtin_fabsf(v[7])));
+        mn = __builtin_fminf(mn, m);
       }
     }
-
-    // ---- RMSNorm -> packed bf16 yw ----
-    uint4 yw[C];
-    if constexpr (NORM) {
-      float part[C];
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        float v[8];
-        unpack8(xw[j], v);
-        float s01 = v[0] * v[0] + v[1] * v[1];
-        float s23 = v[2] * v[2] + v[3] * v[3];
-        float s45 = v[4] * v[4] + v[5] * v[5];
-        float s67 = v[6] * v[6] + v[7] * v[7];
-        part[j] = grp_sum<L>((s01 + s23) + (s45 + s67));
-      }
+    for (int w = 1; w < C; w *= 2)
 #pragma unroll
-      for (int w = 1; w < C; w *= 2)
-#pragma unroll
-        for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
-      const float ss = part[0];
-      const float mean = ss / a.nseg_f;
-      const float rms = __builtin_sqrtf(mean + a.eps);
+      for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
+    const float ss = part[0];
+    const float mean = a.inv_nseg != 0.0f ? ss * a.inv_nseg : ss / a.nseg_f;
+    const float rms = __builtin_sqrtf(mean + a.eps);
+    // The fast division needs a normal rms with a normal reciprocal, every
+    // quotient normal (|x| >= 2^(e(rms) - 252) guarantees it) and an exact
+    // FMA residual (|x| >= 2^-100).  Rows holding a smaller magnitude --
+    // including an exact zero -- divide exactly instead.
+    const int re = (int)(__float_as_uint(rms) >> 23);
+    const int k = re - 252 > -100 ? re - 252 : -100;
+    const float thr = __uint_as_float((uint32_t)(k + 127) << 23);
+    const bool tiny = mn < thr;
+    bool fast = re >= 127 - 100 && re <= 127 + 100;
+    if constexpr (L == 64) {
+      fast = fast && __builtin_amdgcn_ballot_w64(tiny) == 0;
+    } else {
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(tiny);
+      fast = fast && ((bal >> (sub * L)) & ((1ull << L) - 1)) == 0;
+    }
+    if (fast) {
       const float rcp = 1.0f / rms;
-      // The fast division needs a normal rms with a normal reciprocal, a
-      // normal quotient (|x| >= 2^(e(rms) - 252) guarantees it) and an exact
-      // FMA residual (|x| >= 2^-100 keeps it far from underflow).  Zeros are
-      // exact either way, so the scan is over nonzero magnitudes (packed
-      // 16-bit: magnitude - 1 wraps zero to 0xFFFF).
-      const int re = (int)(__float_as_uint(rms) >> 23);
-      bool fast = re >= 127 - 100 && re <= 127 + 100;
-      const int k = re - 252 > -100 ? re - 252 : -100;
-      const uint32_t thr = (uint32_t)(k + 127) << 7;  // bf16 bits of 2^k
-      u16x2_t mn = {0xFFFF, 0xFFFF};
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        const int c = li + L * j;
-        if (c < a.nchunk) {
-          const uint32_t ws[4] = {xw[j].x, xw[j].y, xw[j].z, xw[j].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u16x2_t m = __builtin_bit_cast(u16x2_t, ws[q] & 0x7FFF7FFFu);
-            const u16x2_t one = {1, 1};
-            mn = __builtin_elementwise_min(mn, (u16x2_t)(m - one));
-          }
-        }
-      }
-      const uint32_t mnl = (uint32_t)(mn.x < mn.y ? mn.x : mn.y);
-      const bool tiny = mnl < thr - 1;
-      if constexpr (L == 64) {
-        fast = fast && __builtin_amdgcn_ballot_w64(tiny) == 0;
-      } else {
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(tiny);
-        fast = fast && ((bal >> (sub * L)) & ((1ull << L) - 1)) == 0;
-      }
-#pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const int c = li + L * j;
         float v[8], g[8], y[8];
-        unpack8(xw[j], v);
-        if constexpr (KEEP_G) {
-          unpack8(gw[j], g);
-        } else {
-          unpack8(c < a.nchunk ? ld16(a.gamma + 8 * c) : make_uint4(0, 0, 0, 0), g);
-        }
-        if (fast) {
+        unpack8(b.xw[j], v);
+        const int c = li + L * j;
+        unpack8(c < a.nchunk ? g_lds[c] : make_uint4(0, 0, 0, 0), g);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) y[k] = div_fast(v[k], rms, rcp) * g[k];
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) y[k] = (v[k] / rms) * g[k];
-        }
+        for (int q = 0; q < 8; ++q) y[q] = div_fast(v[q], rms, rcp) * g[q];
         yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
                            pack_bf16(y[6], y[7]));
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < C; ++j) yw[j] = xw[j];
-    }
-
-    // ---- RoPE -> packed bf16 halves (rope lanes) ----
-    uint2 y0w = make_uint2(0, 0), y1w = make_uint2(0, 0);
-    if constexpr (MODE != M_MXFP4 && ROPE) {
-      if (li < 8) {
-        const uint32_t xs[4] = {rw.x, rw.y, rw.z, rw.w};
-        const float c0[4] = {lo_f(c0w.x), hi_f(c0w.x), lo_f(c0w.y), hi_f(c0w.y)};
-        const float c1[4] = {lo_f(c1w.x), hi_f(c1w.x), lo_f(c1w.y), hi_f(c1w.y)};
-        const float s0[4] = {lo_f(s0w.x), hi_f(s0w.x), lo_f(s0w.y), hi_f(s0w.y)};
-        const float s1[4] = {lo_f(s1w.x), hi_f(s1w.x), lo_f(s1w.y), hi_f(s1w.y)};
-        float o0[4], o1[4];
+      for (int j = 0; j < C; ++j) {
+        float v[8], g[8], y[8];
+        unpack8(b.xw[j], v);
+        const int c = li + L * j;
+        unpack8(c < a.nchunk ? g_lds[c] : make_uint4(0, 0, 0, 0), g);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float xa = lo_f(xs[k]), xb = hi_f(xs[k]);
-          o0[k] = xa * c0[k] + (-xb) * s0[k];  // both products exact
-          o1[k] = xb * c1[k] + xa * s1[k];
-        }
-        y0w = make_uint2(pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3]));
-        y1w = make_uint2(pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3]));
+        for (int q = 0; q < 8; ++q) y[q] = (v[q] / rms) * g[q];
+        yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                           pack_bf16(y[6], y[7]));
       }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C; ++j) yw[j] = b.xw[j];
+  }
 
-    // ---- outputs ----
-    if constexpr (MODE == M_SPLIT) {
-      uint8_t *ck = row_addr(a.cache, (uint32_t)slot, a, a.c_pitch, a.c_bstride);
-      uint8_t *kk = row_addr(a.aux, (uint32_t)slot, a, a.a_pitch, a.a_bstride);
+  // ---- RoPE: 4 output bytes per task ----
+  constexpr int TPL = RopeShape<L>::TPL;
+  uint32_t ry[RowBuf<MODE, ROPE, L, C>::HAS_ROPE_SEG ? TPL : 1];
+  if constexpr (RowBuf<MODE, ROPE, L, C>::HAS_ROPE_SEG) {
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const int c = li + L * j;
-        if (c < a.nchunk) st_u128(ck + 16 * c, yw[j], a.c_align);
+    for (int k = 0; k < TPL; ++k) {
+      const int tau = li + L * k;
+      if constexpr (ROPE) {
+        const bool hi = tau >= 16;
+        const float a0 = lo_f(b.rx[k].x), b0 = hi_f(b.rx[k].x);
+        const float a1 = lo_f(b.rx[k].y), b1 = hi_f(b.rx[k].y);
+        const float c0 = lo_f(b.rc[k]), c1 = hi_f(b.rc[k]);
+        const float s0 = lo_f(b.rs[k]), s1 = hi_f(b.rs[k]);
+        // first half: a*c - b*s; second half: b*c + a*s (both products exact)
+        const float p0 = hi ? b0 : a0, q0 = hi ? a0 : -b0;
+        const float p1 = hi ? b1 : a1, q1 = hi ? a1 : -b1;
+        ry[k] = pack_bf16(__builtin_fmaf(p0, c0, q0 * s0), __builtin_fmaf(p1, c1, q1 * s1));
+      } else {
+        ry[k] = b.rx[k].x;
       }
-      if (li < 8) {
-        st_u64(kk + 8 * li, y0w, a.a_align);
-        st_u64(kk + 64 + 8 * li, y1w, a.a_align);
-      }
-    } else if constexpr (MODE == M_MXFP4) {
-      uint8_t *cr = row_addr(a.cache, (uint32_t)slot, a, a.c_pitch, a.c_bstride);
-      uint8_t *sr = row_addr(a.aux, (uint32_t)slot, a, a.a_pitch, a.a_bstride);
+    }
+  }
+
+  // ---- outputs (kept in registers; stored by store_row) ----
+  if constexpr (MODE == M_SPLIT) {
+    o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
+    o.p1 = row_addr(a.aux, slot, a, a.a_pitch, a.a_bstride);
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const int c = li + L * j;
-        float v[8];
-        unpack8(yw[j], v);
-        float m = 0.0f;
+    for (int j = 0; j < C; ++j) o.w[j] = yw[j];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(v[k]));
-        m = grp_max<4>(m);  // 32 values = 4 lanes
-        const int E = e8m0_exp<2, 0x400000u>(m);  // FP4 max 6 = 1.5 * 2^2
+    for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
+  } else if constexpr (MODE == M_MXFP4) {
+    o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
+    o.p1 = row_addr(a.aux, slot, a, a.a_pitch, a.a_bstride);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
+#pragma unroll
+      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
+      m = grp_max<4>(m);  // 32 values = 4 lanes
+      const int E = e8m0_exp<2, 0x400000u>(m);  // FP4 max 6 = 1.5 * 2^2
+      uint32_t word = 0;
+      if (E >= -100 && E <= 100) {
+        const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], sc, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], sc, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], sc, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], sc, 3);
+      } else {
         const float f = exp2_neg(E);
-        uint32_t word = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) word |= enc_e2m1(v[k] * f) << (4 * k);
-        if (c < a.nchunk) {
-          st_u32(cr + 4 * c, word, a.c_align);
-          if ((li & 3) == 0) st_u8(sr + (c >> 2), (uint32_t)(E + 127));
-        }
+        for (int q = 0; q < 8; ++q) word |= enc_e2m1_sw(v[q] * f) << (4 * q);
       }
-    } else {  // FP8 modes
-      uint8_t *cr = row_addr(a.cache, (uint32_t)slot, a, a.c_pitch, a.c_bstride);
+      o.w[j].x = word;
+      o.sb[j] = (uint32_t)(E + 127);
+    }
+  } else {  // FP8 modes
+    o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const int c = li + L * j;
-        float v[8];
-        unpack8(yw[j], v);
-        float m = 0.0f;
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
 #pragma unroll
-        for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(v[k]));
-        m = grp_max<8>(m);  // 64 values = 8 lanes
-        uint32_t q[8];
-        uint32_t sbits;
-        if constexpr (MODE == M_FP8_E8M0) {
-          const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
+      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
+      m = grp_max<8>(m);  // 64 values = 8 lanes
+      uint2 codes;
+      uint32_t sbits;
+      if constexpr (MODE == M_FP8_E8M0) {
+        const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
+        sbits = (uint32_t)(E + 127);
+        if (E >= -100 && E <= 100) {
+          const float sc = __uint_as_float(sbits << 23);
+          s16x2_t w0 = {0, 0}, w1 = {0, 0};
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[0], v[1], sc, false);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[2], v[3], sc, true);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[4], v[5], sc, false);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[6], v[7], sc, true);
+          codes = make_uint2(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1));
+        } else {
           const float f = exp2_neg(E);
+          uint32_t q[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) q[k] = enc_e4m3(v[k] * f);
-          sbits = (uint32_t)(E + 127);
+          for (int k = 0; k < 8; ++k) q[k] = enc_e4m3_sw(v[k] * f);
+          codes = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                             q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+        }
+      } else {
+        // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
+        // stored value.  Outside [2^-80, 2^100] a residual or the reciprocal
+        // of the fast division could leave the normal range; such groups
+        // divide exactly (an infinite scale, from an infinite RMSNorm output,
+        // gives +-0 for finite values and the NaN code for inf / inf).
+        const float s32 =
+            (m >= 0x1p-100f && m <= 0x1p+100f) ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
+        sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
+        const float su = __uint_as_float(sbits << 16);
+        if (su >= 0x1p-80f && su <= 0x1p+100f) {
+          const float rs = 1.0f / su;
+          float qv[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) qv[k] = div_fast(v[k], su, rs);
+          int w0 = 0, w1 = 0;
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], w1, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+          codes = make_uint2((uint32_t)w0, (uint32_t)w1);
         } else {
-          // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
-          // stored value
-          const float s32 =
-              (m >= 0x1p-100f && m <= 0x1p+100f) ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
-          sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
-          const float su = __uint_as_float(sbits << 16);
-          // Outside [2^-80, 2^100] a residual or the reciprocal of the fast
-          // division could leave the normal range; such groups divide
-          // exactly.  An infinite scale (an infinite RMSNorm output) gives
-          // +-0 for finite values and the NaN code 0x7F for inf / inf.
-          if (su >= 0x1p-80f && su <= 0x1p+100f) {
-            const float rs = 1.0f / su;
+          uint32_t q[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = enc_e4m3(div_fast(v[k], su, rs));
-          } else if (su > 0.0f) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const float qq = v[k] / su;
-              q[k] = qq != qq ? 0x7Fu : enc_e4m3(qq);
-            }
-          } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) q[k] = 0u;
-          }
-        }
-        if (c < a.nchunk) {
-          const uint2 codes = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                                         q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
-          st_u64(cr + 8 * c, codes, a.c_align);
-          if ((li & 7) == 0) {
-            const int g = c >> 3;
-            if constexpr (MODE == M_FP8_E8M0)
-              st_u8(cr + a.nseg + 128 + g, sbits);
-            else
-              st_u16(cr + a.nseg + 128 + 2 * g, sbits, a.c_align);
-          }
+          for (int k = 0; k < 8; ++k) q[k] = su > 0.0f ? enc_e4m3_sw(v[k] / su) : 0u;
+          codes = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                             q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
         }
       }
-      if (li < 8) {
-        if constexpr (ROPE) {
-          st_u64(cr + a.nseg + 8 * li, y0w, a.c_align);
-          st_u64(cr + a.nseg + 64 + 8 * li, y1w, a.c_align);
-        } else {
-          st_u128(cr + a.nseg + 16 * li, rw, a.c_align);
+      o.w[j] = make_uint4(codes.x, codes.y, 0u, 0u);
+      o.sb[j] = sbits;
+    }
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
+  }
+}
+
+// Stores one computed row: exactly kvCacheCol bytes (plus the aux row).
+template <int MODE, bool ROPE, int L, int C>
+__device__ __forceinline__ void store_row(const KArgs &a, int li, const RowOut<MODE, L, C> &o) {
+  constexpr int TPL = RopeShape<L>::TPL;
+  if constexpr (MODE == M_SPLIT) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      if (L * C == a.nchunk || c < a.nchunk) st_u128(o.p0 + 16 * c, o.w[j], a.c_align);
+    }
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const int tau = li + L * k;
+      if (tau < 32) st_u32(o.p1 + 4 * tau, o.ry[k], a.a_align);
+    }
+  } else if constexpr (MODE == M_MXFP4) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      if (L * C == a.nchunk || c < a.nchunk) {
+        st_u32(o.p0 + 4 * c, o.w[j].x, a.c_align);
+        if ((li & 3) == 0) st_u8(o.p1 + (c >> 2), o.sb[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      if (L * C == a.nchunk || c < a.nchunk) {
+        st_u64(o.p0 + 8 * c, make_uint2(o.w[j].x, o.w[j].y), a.c_align);
+        if ((li & 7) == 0) {
+          const int g = c >> 3;
+          if constexpr (MODE == M_FP8_E8M0)
+            st_u8(o.p0 + a.nseg + 128 + g, o.sb[j]);
+          else
+            st_u16(o.p0 + a.nseg + 128 + 2 * g, o.sb[j], a.c_align);
         }
       }
-      if constexpr (MODE == M_FP8_BF16) {
-        for (int b = a.concat_col + li; b < a.kv_cache_col; b += L) st_u8(cr + b, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const int tau = li + L * k;
+      if (tau < 32) st_u32(o.p0 + a.nseg + 4 * tau, o.ry[k], a.c_align);
+    }
+    if constexpr (MODE == M_FP8_BF16) {
+      if (a.pad16 >= 0) {
+        for (int b = li; b < a.pad16; b += L)
+          *reinterpret_cast<uint4 *>(o.p0 + a.concat_col + 16 * b) = make_uint4(0, 0, 0, 0);
+      } else {
+        for (int b = a.concat_col + li; b < a.kv_cache_col; b += L) st_u8(o.p0 + b, 0u);
       }
+    }
+  }
+}
+
+template <int MODE, bool NORM, bool ROPE, int L, int C>
+__global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
+  constexpr int R = 64 / L;    // rows per wave-iteration
+  constexpr int WIN = 64 / R;  // iterations covered by one slot window
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (L - 1);
+  const int sub = lane / L;
+  // gamma (the same for every row) staged once per block in LDS
+  extern __shared__ uint4 g_lds[];
+  if constexpr (NORM) {
+    for (int i = threadIdx.x; i < a.nchunk; i += 256) g_lds[i] = ld16_cached(a.gamma + 8 * i);
+    __syncthreads();
+  }
+  int blk = blockIdx.x;
+  if (a.xcd_blocks > 0) blk = (blk & 7) * a.xcd_blocks + (blk >> 3);
+  const int wave = __builtin_amdgcn_readfirstlane(blk * 4 + (int)(threadIdx.x >> 6));
+  if (wave >= a.n_groups) return;
+  const int n_it = (a.n_groups - wave + a.nwaves - 1) / a.nwaves;
+
+  // slot window: lane i holds the slot of iteration base + i / R, row i % R
+  auto load_window = [&](int base) -> int {
+    const int itw = base + lane / R;
+    const int64_t row = ((int64_t)wave + (int64_t)itw * a.nwaves) * R + (lane % R);
+    return (itw < n_it && row < a.T) ? a.slots[row] : -1;
+  };
+  auto pick_slot = [&](int win, int itl) -> uint32_t {
+    if constexpr (R == 1) {
+      return (uint32_t)__builtin_amdgcn_readlane(win, itl);
+    } else if constexpr (R == 2) {
+      const int s0 = __builtin_amdgcn_readlane(win, 2 * itl);
+      const int s1 = __builtin_amdgcn_readlane(win, 2 * itl + 1);
+      return (uint32_t)(sub ? s1 : s0);
+    } else {
+      return (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (itl * R + sub), win);
+    }
+  };
+  auto row_of = [&](int it) -> int64_t {
+    return ((int64_t)wave + (int64_t)it * a.nwaves) * R + sub;
+  };
+  const uint32_t ns = (uint32_t)a.num_slots;
+
+  // One row ahead: the next row's loads are issued before the current row
+  // is computed, then copied into the current buffer (a copy instead of two
+  // unrolled bodies keeps the code size of one row).  Rows of more than two
+  // chunks per lane are not prefetched (their registers are needed for the
+  // row itself).
+  // Software pipeline, one row ahead.  gfx9 has a single in-order counter
+  // for vector loads and stores, so a wait for a load also waits for every
+  // store issued before it.  Each iteration therefore (1) issues the next
+  // row's loads, (2) computes the current row into registers, (3) waits for
+  // the next row's loads -- the only stores still in flight then are the
+  // previous row's, issued a whole computation earlier -- and only then (4)
+  // issues the current row's stores.  The slot window for the iterations
+  // after the current one is loaded one iteration early, so that its wait
+  // is the same one.  Rows of more than two chunks per lane are not
+  // prefetched (their registers are needed for the row itself).
+  constexpr bool PREFETCH = C <= 2;
+  RowBuf<MODE, ROPE, L, C> cur, nxt;
+  RowOut<MODE, L, C> out;
+  int win = load_window(0);
+  int win_next = -1;
+  uint32_t slot = pick_slot(win, 0);
+  if (slot < ns) load_row<MODE, NORM, ROPE, L, C>(a, row_of(0), li, cur);
+  if (WIN == 1 && n_it > 1) win_next = load_window(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing is in flight at the loop entry
+  for (int it = 0; it < n_it; ++it) {
+    uint32_t slot_n = 0xFFFFFFFFu;
+    if (it + 1 < n_it) {
+      if ((it + 1) % WIN == 0) win = win_next;
+      slot_n = pick_slot(win, (it + 1) % WIN);
+      if ((it + 2) % WIN == 0 && it + 2 < n_it) win_next = load_window(it + 2);
+      if (PREFETCH && slot_n < ns) load_row<MODE, NORM, ROPE, L, C>(a, row_of(it + 1), li, nxt);
+    }
+    if (slot < ns) compute_row<MODE, NORM, ROPE, L, C>(a, slot, li, sub, cur, g_lds, out);
+    if constexpr (PREFETCH) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next row and window loaded
+      cur = nxt;
+    }
+    if (slot < ns) store_row<MODE, ROPE, L, C>(a, li, out);
+    slot = slot_n;
+    if constexpr (!PREFETCH) {
+      if (slot < ns) load_row<MODE, NORM, ROPE, L, C>(a, row_of(it + 1), li, cur);
     }
   }
 }
@@ -496,7 +688,8 @@ template <int MODE, bool NORM, bool ROPE>
 kfn_t pick_layout(int L, int C) {
   if (L == 8) return epilog_kernel<MODE, NORM, ROPE, 8, 1>;
   if (L == 16) return epilog_kernel<MODE, NORM, ROPE, 16, 1>;
-  if (L == 32) return epilog_kernel<MODE, NORM, ROPE, 32, 1>;
+  if (L == 32)
+    return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1> : epilog_kernel<MODE, NORM, ROPE, 32, 2>;
   switch (C) {
     case 1: return epilog_kernel<MODE, NORM, ROPE, 64, 1>;
     case 2: return epilog_kernel<MODE, NORM, ROPE, 64, 2>;
@@ -509,13 +702,15 @@ kfn_t pick_layout(int L, int C) {
 kfn_t pick(int mode, bool norm, bool rope, int L, int C) {
   switch (mode) {
     case M_FP8_BF16:
-      if (norm) return rope ? pick_layout<M_FP8_BF16, true, true>(L, C)
-                            : pick_layout<M_FP8_BF16, true, false>(L, C);
+      if (norm)
+        return rope ? pick_layout<M_FP8_BF16, true, true>(L, C)
+                    : pick_layout<M_FP8_BF16, true, false>(L, C);
       return rope ? pick_layout<M_FP8_BF16, false, true>(L, C)
                   : pick_layout<M_FP8_BF16, false, false>(L, C);
     case M_FP8_E8M0:
-      if (norm) return rope ? pick_layout<M_FP8_E8M0, true, true>(L, C)
-                            : pick_layout<M_FP8_E8M0, true, false>(L, C);
+      if (norm)
+        return rope ? pick_layout<M_FP8_E8M0, true, true>(L, C)
+                    : pick_layout<M_FP8_E8M0, true, false>(L, C);
       return rope ? pick_layout<M_FP8_E8M0, false, true>(L, C)
                   : pick_layout<M_FP8_E8M0, false, false>(L, C);
     case M_MXFP4:
@@ -561,38 +756,49 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   while ((INT64_C(1) << l) < p.block_size) ++l;
   const int shift = 31 + l;
   const unsigned __int128 num = (unsigned __int128)1 << shift;
-  a.bs_magic = (uint64_t)((num + (unsigned __int128)p.block_size - 1) / (unsigned __int128)p.block_size);
+  a.bs_magic = (uint64_t)((num + (unsigned __int128)p.block_size - 1) /
+                          (unsigned __int128)p.block_size);
   a.bs_shift = shift;
   a.block_size = (int32_t)p.block_size;
+  a.bs_log2 = (INT64_C(1) << l) == p.block_size ? l : -1;
   a.T = (int32_t)p.T;
   a.num_slots = (int32_t)p.num_slots;
   a.nseg = (int32_t)p.nope;
   a.nchunk = (int32_t)(p.nope / 8);
   a.concat_col = (int32_t)p.concat_col;
   a.kv_cache_col = (int32_t)p.kv_cache_col;
+  a.pad16 = (p.c_align >= 16 && p.concat_col % 16 == 0 &&
+             (p.kv_cache_col - p.concat_col) % 16 == 0)
+                ? (int32_t)((p.kv_cache_col - p.concat_col) / 16)
+                : -1;
   a.c_align = p.c_align;
   a.a_align = p.mode == KVEPI_MODE_MXFP4 || p.mode == KVEPI_MODE_BF16_SPLIT ? p.a_align : 16;
   a.eps = p.eps;
   a.nseg_f = (float)p.nope;
+  a.inv_nseg = (p.nope & (p.nope - 1)) == 0 ? 1.0f / (float)p.nope : 0.0f;
 
-  // layout: L lanes per row (power of two, 8..64), C chunks per lane
+  // layout: L lanes per row (power of two, 8..64), C chunks per lane; rows
+  // of 64 chunks (d = 576) go two to a wave
   int L = 8;
   while (L < 64 && L < a.nchunk) L *= 2;
+  if (a.nchunk == 64) L = 32;
   int C = 1;
   while (C * L < a.nchunk) C *= 2;
 
   const int rows_per_wave = 64 / L;
-  const int64_t waves_needed = (p.T + rows_per_wave - 1) / rows_per_wave;
+  const int64_t n_groups = (p.T + rows_per_wave - 1) / rows_per_wave;
   const int cus = device_cus();
   const int64_t max_waves = (int64_t)cus * 32;  // 8 blocks of 4 waves per CU
-  int64_t waves = waves_needed < max_waves ? waves_needed : max_waves;
-  int64_t blocks = (waves + 3) / 4;
+  const int64_t waves = n_groups < max_waves ? n_groups : max_waves;
+  const int64_t blocks = (waves + 3) / 4;
   a.nwaves = (int32_t)(blocks * 4);
+  a.n_groups = (int32_t)n_groups;
   a.xcd_blocks = (blocks % 8 == 0) ? (int32_t)(blocks / 8) : 0;
 
   kfn_t fn = pick(p.mode, p.norm, p.rope, L, C);
   void *args[] = {&a};
+  const size_t lds = p.norm ? (size_t)p.nope * 2 : 0;  // gamma, 16 KB at most
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)blocks),
-                                 dim3(256), args, 0, static_cast<hipStream_t>(stream));
+                                 dim3(256), args, lds, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVEPI_OK : KVEPI_ERR_RUNTIME;
 }
