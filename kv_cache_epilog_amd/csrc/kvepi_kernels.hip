@@ -80,6 +80,9 @@ __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32), a low.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -139,6 +142,15 @@ __device__ __forceinline__ float div_fast(float a, float b, float rcp) {
   const float q0 = a * rcp;
   const float r = __builtin_fmaf(-q0, b, a);
   return -__builtin_fmaf(-r, rcp, -q0);
+}
+
+// 1 / b correctly rounded, from the hardware reciprocal and one Newton step
+// (checked against IEEE division for every fp32 significand, for exponents
+// in [-100, 100]; callers keep b in that range).
+__device__ __forceinline__ float rcp_rn(float b) {
+  const float y0 = __builtin_amdgcn_rcpf(b);
+  const float e = __builtin_fmaf(-b, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
 }
 
 // E4M3FN code of q: round to nearest even, |q| > 448 saturates to 448,
@@ -242,8 +254,6 @@ __device__ __forceinline__ uint8_t *row_addr(uint8_t *base, uint32_t s, const KA
 }
 
 // Streamed inputs (read once) use nontemporal loads.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -270,6 +280,15 @@ __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
 // ------------------------------------------------------------------------
 // the epilog kernel
 // ------------------------------------------------------------------------
+
+// Write sink for skipped tokens: their (discarded) row goes here instead of
+// being branched around, so that every loop iteration issues the same
+// stores.  Its contents are never read.  Half for the main row (at most
+// 16256 bytes, a bf16 ckv row of d = 8192), half for the aux row, then 16
+// bytes per lane for lanes with nothing to store.
+constexpr int kSinkHalf = 16384;
+__device__ __attribute__((aligned(256))) uint8_t g_sink[2 * kSinkHalf + 64 * 16];
+__device__ int32_t kNoSlot = -1;  // read only; read in place of slots past the end
 enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4 };
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
@@ -291,32 +310,35 @@ struct RowBuf {
   uint32_t rs[HAS_ROPE_SEG && ROPE ? TPL : 1];  // sin pair
 };
 
-template <int MODE, bool NORM, bool ROPE, int L, int C>
+// Loads one row.  Every lane always issues the same loads (indices beyond
+// the row are clamped and their values cleared), so the number of memory
+// operations per iteration is fixed -- see the pipeline in the kernel.
+template <int MODE, bool NORM, bool ROPE, int L, int C, bool FAST>
 __device__ __forceinline__ void load_row(const KArgs &a, int64_t row, int li,
                                          RowBuf<MODE, ROPE, L, C> &b) {
   const uint16_t *xr = a.x + row * a.x_stride;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int c = li + L * j;
-    if (L * C == a.nchunk || c < a.nchunk)
+    if constexpr (FAST) {
       b.xw[j] = ld16(xr + 8 * c);
-    else
-      b.xw[j] = make_uint4(0, 0, 0, 0);
+    } else {
+      const uint4 v = ld16(xr + 8 * min(c, a.nchunk - 1));
+      b.xw[j] = c < a.nchunk ? v : make_uint4(0, 0, 0, 0);
+    }
   }
   if constexpr (RowBuf<MODE, ROPE, L, C>::HAS_ROPE_SEG) {
     constexpr int TPL = RowBuf<MODE, ROPE, L, C>::TPL;
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
-      const int tau = li + L * k;
-      if (tau < 32) {
-        if constexpr (ROPE) {
-          const int p = tau & 15;
-          b.rx[k] = ld8(xr + a.nseg + 4 * p);
-          b.rc[k] = ld4(a.cos + row * 64 + 2 * tau);
-          b.rs[k] = ld4(a.sin + row * 64 + 2 * tau);
-        } else {
-          b.rx[k] = make_uint2(ld4(xr + a.nseg + 2 * tau), 0u);
-        }
+      const int tau = (li + L * k) & 31;
+      if constexpr (ROPE) {
+        const int p = tau & 15;
+        b.rx[k] = ld8(xr + a.nseg + 4 * p);
+        b.rc[k] = ld4(a.cos + row * 64 + 2 * tau);
+        b.rs[k] = ld4(a.sin + row * 64 + 2 * tau);
+      } else {
+        b.rx[k] = make_uint2(ld4(xr + a.nseg + 2 * tau), 0u);
       }
     }
   }
@@ -332,31 +354,35 @@ struct RowOut {
   uint32_t ry[MODE == M_MXFP4 ? 1 : RopeShape<L>::TPL];
 };
 
-template <int MODE, bool NORM, bool ROPE, int L, int C>
-__device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int li, int sub,
+template <int MODE, bool NORM, bool ROPE, int L, int C, bool FAST>
+__device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
                                             const RowBuf<MODE, ROPE, L, C> &b,
                                             const uint4 *g_lds, RowOut<MODE, L, C> &o) {
   // ---- RMSNorm -> packed bf16 yw ----
   uint4 yw[C];
   if constexpr (NORM) {
     float part[C];
-    float mn = __builtin_inff();
+    u16x2_t mn = {0x7FFF, 0x7FFF};  // smallest bf16 magnitude (bits) of the row
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
       unpack8(b.xw[j], v);
-      const float s01 = v[0] * v[0] + v[1] * v[1];
-      const float s23 = v[2] * v[2] + v[3] * v[3];
-      const float s45 = v[4] * v[4] + v[5] * v[5];
-      const float s67 = v[6] * v[6] + v[7] * v[7];
+      // squares of bf16 values are exact, so fma(b, b, a*a) is the
+      // rounded sum of the two squares
+      const float s01 = __builtin_fmaf(v[1], v[1], v[0] * v[0]);
+      const float s23 = __builtin_fmaf(v[3], v[3], v[2] * v[2]);
+      const float s45 = __builtin_fmaf(v[5], v[5], v[4] * v[4]);
+      const float s67 = __builtin_fmaf(v[7], v[7], v[6] * v[6]);
       part[j] = grp_sum<L>((s01 + s23) + (s45 + s67));
       const int c = li + L * j;
-      if (L * C == a.nchunk || c < a.nchunk) {
-        float m = __builtin_fminf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
-        m = __builtin_fminf(m, __builtin_fminf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
-        m = __builtin_fminf(m, __builtin_fminf(__builtin_fabsf(v[4]), __builtin_fabsf(v[5])));
-        m = __builtin_fminf(m, __builtin_fminf(__builtin_fabsf(v[6]), __builtin_fabsf(v[7])));
-        mn = __builtin_fminf(mn, m);
+      if (FAST || c < a.nchunk) {
+        const u16x2_t m01 = __builtin_bit_cast(u16x2_t, b.xw[j].x & 0x7FFF7FFFu);
+        const u16x2_t m23 = __builtin_bit_cast(u16x2_t, b.xw[j].y & 0x7FFF7FFFu);
+        const u16x2_t m45 = __builtin_bit_cast(u16x2_t, b.xw[j].z & 0x7FFF7FFFu);
+        const u16x2_t m67 = __builtin_bit_cast(u16x2_t, b.xw[j].w & 0x7FFF7FFFu);
+        mn = __builtin_elementwise_min(
+            mn, __builtin_elementwise_min(__builtin_elementwise_min(m01, m23),
+                                          __builtin_elementwise_min(m45, m67)));
       }
     }
 #pragma unroll
@@ -369,11 +395,12 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
     // The fast division needs a normal rms with a normal reciprocal, every
     // quotient normal (|x| >= 2^(e(rms) - 252) guarantees it) and an exact
     // FMA residual (|x| >= 2^-100).  Rows holding a smaller magnitude --
-    // including an exact zero -- divide exactly instead.
+    // including an exact zero -- divide exactly instead.  The magnitudes are
+    // compared as bf16 bit patterns (same order as the values).
     const int re = (int)(__float_as_uint(rms) >> 23);
     const int k = re - 252 > -100 ? re - 252 : -100;
-    const float thr = __uint_as_float((uint32_t)(k + 127) << 23);
-    const bool tiny = mn < thr;
+    const uint32_t thr = (uint32_t)(k + 127) << 7;  // bf16 bits of 2^k
+    const bool tiny = (uint32_t)min(mn.x, mn.y) < thr;
     bool fast = re >= 127 - 100 && re <= 127 + 100;
     if constexpr (L == 64) {
       fast = fast && __builtin_amdgcn_ballot_w64(tiny) == 0;
@@ -382,7 +409,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
       fast = fast && ((bal >> (sub * L)) & ((1ull << L) - 1)) == 0;
     }
     if (fast) {
-      const float rcp = 1.0f / rms;
+      const float rcp = rcp_rn(rms);
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         float v[8], g[8], y[8];
@@ -418,7 +445,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
   if constexpr (RowBuf<MODE, ROPE, L, C>::HAS_ROPE_SEG) {
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
-      const int tau = li + L * k;
+      const int tau = (li + L * k) & 31;  // lanes past 31 repeat tasks 0..31
       if constexpr (ROPE) {
         const bool hi = tau >= 16;
         const float a0 = lo_f(b.rx[k].x), b0 = hi_f(b.rx[k].x);
@@ -437,15 +464,11 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
 
   // ---- outputs (kept in registers; stored by store_row) ----
   if constexpr (MODE == M_SPLIT) {
-    o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
-    o.p1 = row_addr(a.aux, slot, a, a.a_pitch, a.a_bstride);
 #pragma unroll
     for (int j = 0; j < C; ++j) o.w[j] = yw[j];
 #pragma unroll
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
   } else if constexpr (MODE == M_MXFP4) {
-    o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
-    o.p1 = row_addr(a.aux, slot, a, a.a_pitch, a.a_bstride);
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
@@ -471,7 +494,6 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
       o.sb[j] = (uint32_t)(E + 127);
     }
   } else {  // FP8 modes
-    o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
@@ -503,16 +525,18 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
         }
       } else {
         // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
-        // stored value.  Outside [2^-80, 2^100] a residual or the reciprocal
-        // of the fast division could leave the normal range; such groups
-        // divide exactly (an infinite scale, from an infinite RMSNorm output,
-        // gives +-0 for finite values and the NaN code for inf / inf).
-        const float s32 =
-            (m >= 0x1p-100f && m <= 0x1p+100f) ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
+        // stored value.  Far from 1 a residual or the reciprocal of the fast
+        // division could leave the normal range; such groups divide exactly
+        // (an infinite scale, from an infinite RMSNorm output, gives +-0 for
+        // finite values and the NaN code for inf / inf).
+        // m in [2^-71, 2^100] keeps m / 448 and the stored scale inside the
+        // range of the fast division and reciprocal
+        const bool fastq = m >= 0x1p-71f && m <= 0x1p+100f;
+        const float s32 = fastq ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
         sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
         const float su = __uint_as_float(sbits << 16);
-        if (su >= 0x1p-80f && su <= 0x1p+100f) {
-          const float rs = 1.0f / su;
+        if (fastq) {
+          const float rs = rcp_rn(su);
           float qv[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) qv[k] = div_fast(v[k], su, rs);
@@ -539,61 +563,70 @@ __device__ __forceinline__ void compute_row(const KArgs &a, uint32_t slot, int l
 }
 
 // Stores one computed row: exactly kvCacheCol bytes (plus the aux row).
-template <int MODE, bool ROPE, int L, int C>
-__device__ __forceinline__ void store_row(const KArgs &a, int li, const RowOut<MODE, L, C> &o) {
+// Every lane issues every store, so that the number of memory operations per
+// iteration is fixed: lanes that carry a copy of a value another lane writes
+// (the group scale, the pad, duplicated rope tasks) write the same bytes to
+// the same address, and lanes with nothing to write (chunks past the row)
+// write to a private slot of the sink.
+template <int MODE, bool ROPE, int L, int C, bool FAST>
+__device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
+                                          const RowOut<MODE, L, C> &o) {
   constexpr int TPL = RopeShape<L>::TPL;
+  // in FAST mode every row start is 16-byte aligned (k rows 4-byte aligned):
+  // the alignment is a constant and the store helpers reduce to one store
+  const int c_al = FAST ? 16 : a.c_align;
+  const int a_al = FAST ? 4 : a.a_align;
+  uint8_t *lsink = g_sink + 2 * kSinkHalf + 16 * lane;
   if constexpr (MODE == M_SPLIT) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int c = li + L * j;
-      if (L * C == a.nchunk || c < a.nchunk) st_u128(o.p0 + 16 * c, o.w[j], a.c_align);
+      st_u128((FAST || c < a.nchunk) ? o.p0 + 16 * c : lsink, o.w[j], c_al);
     }
 #pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      const int tau = li + L * k;
-      if (tau < 32) st_u32(o.p1 + 4 * tau, o.ry[k], a.a_align);
-    }
+    for (int k = 0; k < TPL; ++k) st_u32(o.p1 + 4 * ((li + L * k) & 31), o.ry[k], a_al);
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int c = li + L * j;
-      if (L * C == a.nchunk || c < a.nchunk) {
-        st_u32(o.p0 + 4 * c, o.w[j].x, a.c_align);
-        if ((li & 3) == 0) st_u8(o.p1 + (c >> 2), o.sb[j]);
-      }
+      const bool in = FAST || c < a.nchunk;
+      st_u32(in ? o.p0 + 4 * c : lsink, o.w[j].x, c_al);
+      st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[j]);  // all 4 lanes of the group
     }
   } else {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int c = li + L * j;
-      if (L * C == a.nchunk || c < a.nchunk) {
-        st_u64(o.p0 + 8 * c, make_uint2(o.w[j].x, o.w[j].y), a.c_align);
-        if ((li & 7) == 0) {
-          const int g = c >> 3;
-          if constexpr (MODE == M_FP8_E8M0)
-            st_u8(o.p0 + a.nseg + 128 + g, o.sb[j]);
-          else
-            st_u16(o.p0 + a.nseg + 128 + 2 * g, o.sb[j], a.c_align);
-        }
-      }
+      const bool in = FAST || c < a.nchunk;
+      st_u64(in ? o.p0 + 8 * c : lsink, make_uint2(o.w[j].x, o.w[j].y), c_al);
+      // every lane of the group writes the group's scale
+      if constexpr (MODE == M_FP8_E8M0)
+        st_u8(in ? o.p0 + a.nseg + 128 + (c >> 3) : lsink + 8, o.sb[j]);
+      else
+        st_u16(in ? o.p0 + a.nseg + 128 + 2 * (c >> 3) : lsink + 8, o.sb[j], c_al);
     }
 #pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      const int tau = li + L * k;
-      if (tau < 32) st_u32(o.p0 + a.nseg + 4 * tau, o.ry[k], a.c_align);
-    }
+    for (int k = 0; k < TPL; ++k)
+      st_u32(o.p0 + a.nseg + 4 * ((li + L * k) & 31), o.ry[k], c_al);
     if constexpr (MODE == M_FP8_BF16) {
-      if (a.pad16 >= 0) {
-        for (int b = li; b < a.pad16; b += L)
-          *reinterpret_cast<uint4 *>(o.p0 + a.concat_col + 16 * b) = make_uint4(0, 0, 0, 0);
+      // zero padding (0..31 bytes): one store per lane, duplicates allowed
+      const int npad = a.kv_cache_col - a.concat_col;
+      if (a.pad16 == 1) {
+        *reinterpret_cast<uint4 *>(o.p0 + a.concat_col) = make_uint4(0, 0, 0, 0);
       } else {
-        for (int b = a.concat_col + li; b < a.kv_cache_col; b += L) st_u8(o.p0 + b, 0u);
+        constexpr int PADIT = (31 + L - 1) / L;  // enough stores for 31 bytes
+#pragma unroll
+        for (int k = 0; k < PADIT; ++k) {
+          const int b = li + L * k;
+          st_u8(npad > 0 ? o.p0 + a.concat_col + (b < npad ? b : b % max(npad, 1)) : lsink + 12,
+                0u);
+        }
       }
     }
   }
 }
 
-template <int MODE, bool NORM, bool ROPE, int L, int C>
+template <int MODE, bool NORM, bool ROPE, int L, int C, bool FAST>
 __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   constexpr int R = 64 / L;    // rows per wave-iteration
   constexpr int WIN = 64 / R;  // iterations covered by one slot window
@@ -612,69 +645,93 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   if (wave >= a.n_groups) return;
   const int n_it = (a.n_groups - wave + a.nwaves - 1) / a.nwaves;
 
-  // slot window: lane i holds the slot of iteration base + i / R, row i % R
-  auto load_window = [&](int base) -> int {
-    const int itw = base + lane / R;
-    const int64_t row = ((int64_t)wave + (int64_t)itw * a.nwaves) * R + (lane % R);
-    return (itw < n_it && row < a.T) ? a.slots[row] : -1;
+  const uint32_t ns = (uint32_t)a.num_slots;
+  // Slots of iteration j: lane l loads the slot of row g(j) * R + l % R, where
+  // g(j) = wave + j * nwaves; beyond the wave's iterations or the tokens the
+  // value is -1.  Every lane issues the load.
+  // (out-of-range lanes read the constant -1 instead of being masked, so
+  // that nothing but the load touches the result until it is used)
+  auto slot_load = [&](int j) -> int {
+    const int64_t r = ((int64_t)wave + (int64_t)j * a.nwaves) * R + (lane % R);
+    const bool ok = j < n_it && r < a.T;
+    return __builtin_nontemporal_load(ok ? a.slots + r : &kNoSlot);
   };
-  auto pick_slot = [&](int win, int itl) -> uint32_t {
+  auto slot_pick = [&](int v) -> uint32_t {
     if constexpr (R == 1) {
-      return (uint32_t)__builtin_amdgcn_readlane(win, itl);
+      return (uint32_t)__builtin_amdgcn_readfirstlane(v);
     } else if constexpr (R == 2) {
-      const int s0 = __builtin_amdgcn_readlane(win, 2 * itl);
-      const int s1 = __builtin_amdgcn_readlane(win, 2 * itl + 1);
+      const int s0 = __builtin_amdgcn_readlane(v, 0);
+      const int s1 = __builtin_amdgcn_readlane(v, 1);
       return (uint32_t)(sub ? s1 : s0);
     } else {
-      return (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (itl * R + sub), win);
+      return (uint32_t)__builtin_amdgcn_ds_bpermute(4 * sub, v);
     }
   };
-  auto row_of = [&](int it) -> int64_t {
-    return ((int64_t)wave + (int64_t)it * a.nwaves) * R + sub;
+  // source row of iteration j: its own row when the slot is valid, else row
+  // 0 (a cached dummy read, so that every iteration issues the same loads)
+  auto src_row = [&](int j, uint32_t slot) -> int64_t {
+    return slot < ns ? ((int64_t)wave + (int64_t)j * a.nwaves) * R + sub : 0;
   };
-  const uint32_t ns = (uint32_t)a.num_slots;
+  // destination of a row: its cache row, or the sink for a skipped token
+  auto set_dest = [&](uint32_t slot, RowOut<MODE, L, C> &o) {
+    if (slot < ns) {
+      o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
+      if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT)
+        o.p1 = row_addr(a.aux, slot, a, a.a_pitch, a.a_bstride);
+    } else {
+      o.p0 = g_sink;
+      o.p1 = g_sink + kSinkHalf;
+    }
+  };
 
-  // One row ahead: the next row's loads are issued before the current row
-  // is computed, then copied into the current buffer (a copy instead of two
-  // unrolled bodies keeps the code size of one row).  Rows of more than two
-  // chunks per lane are not prefetched (their registers are needed for the
-  // row itself).
-  // Software pipeline, one row ahead.  gfx9 has a single in-order counter
-  // for vector loads and stores, so a wait for a load also waits for every
-  // store issued before it.  Each iteration therefore (1) issues the next
-  // row's loads, (2) computes the current row into registers, (3) waits for
-  // the next row's loads -- the only stores still in flight then are the
-  // previous row's, issued a whole computation earlier -- and only then (4)
-  // issues the current row's stores.  The slot window for the iterations
-  // after the current one is loaded one iteration early, so that its wait
-  // is the same one.  Rows of more than two chunks per lane are not
-  // prefetched (their registers are needed for the row itself).
-  constexpr bool PREFETCH = C <= 2;
-  RowBuf<MODE, ROPE, L, C> cur, nxt;
   RowOut<MODE, L, C> out;
-  int win = load_window(0);
-  int win_next = -1;
-  uint32_t slot = pick_slot(win, 0);
-  if (slot < ns) load_row<MODE, NORM, ROPE, L, C>(a, row_of(0), li, cur);
-  if (WIN == 1 && n_it > 1) win_next = load_window(1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing is in flight at the loop entry
-  for (int it = 0; it < n_it; ++it) {
-    uint32_t slot_n = 0xFFFFFFFFu;
-    if (it + 1 < n_it) {
-      if ((it + 1) % WIN == 0) win = win_next;
-      slot_n = pick_slot(win, (it + 1) % WIN);
-      if ((it + 2) % WIN == 0 && it + 2 < n_it) win_next = load_window(it + 2);
-      if (PREFETCH && slot_n < ns) load_row<MODE, NORM, ROPE, L, C>(a, row_of(it + 1), li, nxt);
+  if constexpr (C > 2) {
+    // rows of more than two chunks per lane: no prefetch (their registers
+    // are needed for the row itself)
+    RowBuf<MODE, ROPE, L, C> cur;
+    for (int it = 0; it < n_it; ++it) {
+      const uint32_t slot = slot_pick(slot_load(it));
+      load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it, slot), li, cur);
+      if (slot < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, cur, g_lds, out);
+      set_dest(slot, out);
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
     }
-    if (slot < ns) compute_row<MODE, NORM, ROPE, L, C>(a, slot, li, sub, cur, g_lds, out);
-    if constexpr (PREFETCH) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next row and window loaded
-      cur = nxt;
-    }
-    if (slot < ns) store_row<MODE, ROPE, L, C>(a, li, out);
-    slot = slot_n;
-    if constexpr (!PREFETCH) {
-      if (slot < ns) load_row<MODE, NORM, ROPE, L, C>(a, row_of(it + 1), li, cur);
+  } else {
+    // Software pipeline, two rows ahead, with two register sets (A holds the
+    // even iterations, B the odd ones).  gfx9 has a single in-order counter
+    // for vector loads and stores, so a wait for a load also waits for every
+    // store issued before it.  Each half-iteration j therefore computes row
+    // j (loaded two half-iterations earlier), then issues the loads of row
+    // j + 2 and only then the stores of row j; the wait before computing row
+    // j + 2 then leaves the stores of rows j and j + 1 in flight.  Every
+    // half-iteration issues the same memory operations (dummy loads of row 0
+    // and stores to a sink for skipped tokens and for the tail), so the
+    // compiler's wait counts are exact; slots are loaded three
+    // half-iterations ahead.
+    RowBuf<MODE, ROPE, L, C> bA, bB;
+    int v0 = slot_load(0), v1 = slot_load(1), v2 = slot_load(2), v3;
+    uint32_t sA = slot_pick(v0), sB = slot_pick(v1);
+    load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(0, sA), li, bA);
+    load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(1, sB), li, bB);
+    // drain once before the loop: otherwise the loop's waits are sized for
+    // the first trip, whose loads were issued in an order of the compiler's
+    // choosing
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    for (int it = 0; it < n_it; it += 2) {
+      // ---- row it (A) ----
+      v3 = slot_load(it + 3);
+      if (sA < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, bA, g_lds, out);
+      set_dest(sA, out);
+      sA = slot_pick(v2);
+      load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it + 2, sA), li, bA);
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
+      // ---- row it + 1 (B) ----
+      v2 = slot_load(it + 4);
+      if (sB < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, bB, g_lds, out);
+      set_dest(sB, out);
+      sB = slot_pick(v3);
+      load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it + 3, sB), li, bB);
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
     }
   }
 }
@@ -684,39 +741,46 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
 // ------------------------------------------------------------------------
 typedef void (*kfn_t)(const KArgs);
 
-template <int MODE, bool NORM, bool ROPE>
-kfn_t pick_layout(int L, int C) {
-  if (L == 8) return epilog_kernel<MODE, NORM, ROPE, 8, 1>;
-  if (L == 16) return epilog_kernel<MODE, NORM, ROPE, 16, 1>;
+template <int MODE, bool NORM, bool ROPE, bool FAST>
+kfn_t pick_layout_f(int L, int C) {
+  if (L == 8) return epilog_kernel<MODE, NORM, ROPE, 8, 1, FAST>;
+  if (L == 16) return epilog_kernel<MODE, NORM, ROPE, 16, 1, FAST>;
   if (L == 32)
-    return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1> : epilog_kernel<MODE, NORM, ROPE, 32, 2>;
+    return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1, FAST>
+                  : epilog_kernel<MODE, NORM, ROPE, 32, 2, FAST>;
   switch (C) {
-    case 1: return epilog_kernel<MODE, NORM, ROPE, 64, 1>;
-    case 2: return epilog_kernel<MODE, NORM, ROPE, 64, 2>;
-    case 4: return epilog_kernel<MODE, NORM, ROPE, 64, 4>;
-    case 8: return epilog_kernel<MODE, NORM, ROPE, 64, 8>;
-    default: return epilog_kernel<MODE, NORM, ROPE, 64, 16>;
+    case 1: return epilog_kernel<MODE, NORM, ROPE, 64, 1, FAST>;
+    case 2: return epilog_kernel<MODE, NORM, ROPE, 64, 2, FAST>;
+    case 4: return epilog_kernel<MODE, NORM, ROPE, 64, 4, FAST>;
+    case 8: return epilog_kernel<MODE, NORM, ROPE, 64, 8, FAST>;
+    default: return epilog_kernel<MODE, NORM, ROPE, 64, 16, FAST>;
   }
 }
 
-kfn_t pick(int mode, bool norm, bool rope, int L, int C) {
+template <int MODE, bool NORM, bool ROPE>
+kfn_t pick_layout(int L, int C, bool fast) {
+  return fast ? pick_layout_f<MODE, NORM, ROPE, true>(L, C)
+              : pick_layout_f<MODE, NORM, ROPE, false>(L, C);
+}
+
+kfn_t pick(int mode, bool norm, bool rope, int L, int C, bool fast) {
   switch (mode) {
     case M_FP8_BF16:
       if (norm)
-        return rope ? pick_layout<M_FP8_BF16, true, true>(L, C)
-                    : pick_layout<M_FP8_BF16, true, false>(L, C);
-      return rope ? pick_layout<M_FP8_BF16, false, true>(L, C)
-                  : pick_layout<M_FP8_BF16, false, false>(L, C);
+        return rope ? pick_layout<M_FP8_BF16, true, true>(L, C, fast)
+                    : pick_layout<M_FP8_BF16, true, false>(L, C, fast);
+      return rope ? pick_layout<M_FP8_BF16, false, true>(L, C, fast)
+                  : pick_layout<M_FP8_BF16, false, false>(L, C, fast);
     case M_FP8_E8M0:
       if (norm)
-        return rope ? pick_layout<M_FP8_E8M0, true, true>(L, C)
-                    : pick_layout<M_FP8_E8M0, true, false>(L, C);
-      return rope ? pick_layout<M_FP8_E8M0, false, true>(L, C)
-                  : pick_layout<M_FP8_E8M0, false, false>(L, C);
+        return rope ? pick_layout<M_FP8_E8M0, true, true>(L, C, fast)
+                    : pick_layout<M_FP8_E8M0, true, false>(L, C, fast);
+      return rope ? pick_layout<M_FP8_E8M0, false, true>(L, C, fast)
+                  : pick_layout<M_FP8_E8M0, false, false>(L, C, fast);
     case M_MXFP4:
-      return pick_layout<M_MXFP4, false, false>(L, C);
+      return pick_layout<M_MXFP4, false, false>(L, C, fast);
     default:
-      return pick_layout<M_SPLIT, true, true>(L, C);
+      return pick_layout<M_SPLIT, true, true>(L, C, fast);
   }
 }
 
@@ -795,7 +859,11 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   a.n_groups = (int32_t)n_groups;
   a.xcd_blocks = (blocks % 8 == 0) ? (int32_t)(blocks / 8) : 0;
 
-  kfn_t fn = pick(p.mode, p.norm, p.rope, L, C);
+  // FAST: whole chunks per lane and 16-byte aligned rows (4-byte aligned k
+  // rows in the bf16 split mode); stores then need no alignment dispatch
+  const bool fast = L * C == a.nchunk && a.c_align >= 16 &&
+                    (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
+  kfn_t fn = pick(p.mode, p.norm, p.rope, L, C, fast);
   void *args[] = {&a};
   const size_t lds = p.norm ? (size_t)p.nope * 2 : 0;  // gamma, 16 KB at most
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)blocks),
