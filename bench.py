@@ -72,6 +72,74 @@ def measured_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+def _counter_rows(csv_path: str, counter: str):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc CSV."""
+    import csv
+    out = []
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def _mean_of(rows, pick):
+    vals = [v for k, v in rows if pick(k)]
+    if not vals:
+        raise SystemExit("no matching dispatches in the counter file")
+    big = max(vals)
+    vals = [v for v in vals if v >= 0.5 * big]  # the timed-size launches
+    return sum(vals) / len(vals)
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+                  copy_write_csv: str, copy_bytes: int):
+    """Turn FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the epilog kernel
+    into HBM bytes per launch.  Each counter is scaled by the factor that
+    makes it read true on a plain device copy of copy_bytes (which reads and
+    writes exactly copy_bytes)."""
+    is_epi = lambda k: "epilog_kernel" in k  # noqa: E731
+    is_copy = lambda k: "copy" in k.lower()  # noqa: E731
+    kf = _mean_of(_counter_rows(fetch_csv, "FETCH_SIZE"), is_epi)
+    kw = _mean_of(_counter_rows(write_csv, "WRITE_SIZE"), is_epi)
+    cf = _mean_of(_counter_rows(copy_fetch_csv, "FETCH_SIZE"), is_copy)
+    cw = _mean_of(_counter_rows(copy_write_csv, "WRITE_SIZE"), is_copy)
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    read_b = kf * 1024.0 * f_scale
+    write_b = kw * 1024.0 * w_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[workload] = {
+        "kernel_sha256_16": kernel_hash(), "bytes_per_launch": read_b + write_b,
+        "read_bytes": read_b, "write_bytes": write_b,
+        "fetch_kib_raw": kf, "write_kib_raw": kw,
+        "copy_bytes": copy_bytes, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(table[workload]))
+
+
+def copy_probe(mib: int, steps: int):
+    """A plain device-to-device copy of mib MiB, launched steps times: the
+    calibration run for the HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": steps}), flush=True)
+
+
 def upload(w: kvgen.Workload, dev):
     import torch
 
@@ -132,11 +200,28 @@ def main():
                     help="workload index (default 4: the d=576 fused epilog)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB --steps times "
+                         "(counter calibration)")
+    ap.add_argument("--write-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="record HBM bytes per launch of --config's kernel from "
+                         "rocprofv3 --pmc counter files; needs --copy-probe's size")
     args = ap.parse_args()
+    if args.write_traffic:
+        if not args.copy_probe:
+            raise SystemExit("--write-traffic needs --copy-probe MIB (the calibration size)")
+        write_traffic(kvgen.CONFIG_NAMES[args.config], *args.write_traffic,
+                      copy_bytes=args.copy_probe << 20)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
 
     import torch
     from kv_cache_epilog_amd import kvepi_run
@@ -153,23 +238,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-launch HIP events on the launch stream: mean kernel time
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # HIP events on the launch stream around the K back-to-back launches:
+    # the host enqueues faster than the kernel runs, so the region is the
+    # kernels plus their dispatch gaps (an event between launches would
+    # add its own gap to every launch)
     total0 = torch.cuda.Event(enable_timing=True)
     total1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     total0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
+    for _ in range(args.steps):
         step()
-        ends[i].record(stream)
     total1.record(stream)
     torch.cuda.synchronize()
     ms_total = total0.elapsed_time(total1)
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    ms_kernel = float(per.mean())
     ms_per_step = ms_total / args.steps
+    ms_kernel = ms_per_step
 
     abytes = algorithmic_bytes(w)
     achieved = abytes / (ms_kernel * 1e-3) / 1e9
@@ -189,8 +272,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name),
-                     "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms_kernel,
-                     "kernel_ms_min": float(per.min())},
+                     "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms_kernel},
     }
     if not args.no_cpu:
         n, dt, ocache, oaux = cpu_baseline(w, args.cpu_seconds)
