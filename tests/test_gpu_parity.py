@@ -175,3 +175,47 @@ def test_special_values(mode):
         for r in (0, 1, 3, 6):
             w0.x[r] = kvgen.to_bf16(np.ones(d))
         check(w0)
+
+
+def _exponent_sweep_rows(mode, T, d, seed):
+    """Rows whose quantisation groups cycle through every power-of-two scale
+    2^k a bf16 input can produce (k from -141 to the largest that keeps
+    MAX * 2^k finite).  Each group holds its amax MAX * 2^k exactly (so the
+    scale is 2^k in every mode), code midpoints (exact ties) times 2^k, and
+    random values below the amax."""
+    rng = np.random.default_rng(seed)
+    if mode == 3:
+        G, nseg, vmax = 32, d, 6.0
+        mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+        kmax = 125
+    else:
+        G, nseg, vmax = 64, d - 64, 448.0
+        mids = [2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 9.5, 13.5, 17.0, 240.0, 416.0]
+        kmax = 119
+    ks = np.arange(-141, kmax + 1)
+    x = np.zeros((T, d))
+    x[:, nseg:] = rng.standard_normal((T, d - nseg))
+    gi = 0
+    for r in range(T):
+        for g in range(nseg // G):
+            k = float(ks[gi % ks.size])
+            gi += 1
+            v = np.clip(rng.standard_normal(G) * vmax / 3, -vmax, vmax)
+            v[0] = vmax if rng.random() < 0.5 else -vmax
+            nm = G // 4
+            v[1:1 + nm] = rng.choice(mids, nm) * np.where(rng.random(nm) < 0.5, -1.0, 1.0)
+            rng.shuffle(v)
+            x[r, g * G:(g + 1) * G] = v * 2.0 ** k
+    return kvgen.to_bf16(x)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 3])
+def test_scale_exponent_sweep(mode):
+    # every e8m0 / bf16 power-of-two scale, both sides of the range where the
+    # kernel uses the hardware converts and fast division, with exact ties
+    d = 128 if mode == 3 else 576
+    T = 400 if mode == 3 else 200
+    xb = _exponent_sweep_rows(mode, T, d, seed=20 + mode)
+    w = _small(mode, T, d, seed=21, skip=0.0, x=xb)
+    n = check(w)
+    assert n == 0
