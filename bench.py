@@ -194,8 +194,8 @@ def _run_oracle_prefix(oracle, w, n, cache, aux):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4,
                     help="workload index (default 4: the d=576 fused epilog)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

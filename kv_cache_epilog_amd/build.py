@@ -32,7 +32,9 @@ def build(force: bool = True, verbose: bool = False) -> str:
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -3,13 +3,14 @@
 // One kernel template covers every mode.  A token row is handled by a group
 // of L lanes of one 64-lane wavefront (64/L rows per wave-iteration: L = 32,
 // two rows per wave, for the d = 576 rows; L = 16, four rows, for the d = 128
-// indexer rows).  Each lane owns C 16-byte chunks of 8 bf16 values, chunk
-// index li + L*j, so every load instruction reads L*16 contiguous bytes of a
-// row.  The path is bound by HBM bandwidth; the design keeps the VALU work
-// per row small enough that the wave scheduler can keep the loads flowing:
-//  - waves are persistent; each wave preloads the slots of its next rows in
-//    one load and issues the next row's loads before computing the current
-//    one (two register sets, manual double buffering);
+// indexer rows).  Each lane owns C 16-byte chunks of 8 bf16 values, in
+// units of two adjacent chunks when C >= 2 (see Lay), so that the codes of a
+// unit leave in one store and a quantisation group spans whole lanes.  The
+// path is bound by HBM bandwidth; the design keeps the VALU work and the
+// number of memory instructions per row small:
+//  - waves are persistent (one block per resident slot of the device); each
+//    wave loads its slots ahead and issues the loads of the row two steps
+//    ahead before storing the current one (two register sets);
 //  - the rope segment is spread over 32 lanes (one output pair each);
 //  - codes come from the gfx950 converts v_cvt_pk_fp8_f32 /
 //    v_cvt_scalef32_pk_fp8_f32 / v_cvt_scalef32_pk_fp4_f32, which round to
@@ -43,6 +44,8 @@
 //     such as 323 works.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "kvepi_plan.h"
 
@@ -270,6 +273,17 @@ __device__ __forceinline__ uint4 ld16_cached(const uint16_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
 
+// gamma in LDS as fp32, in two planes of L*C float4 (values 0-3 and 4-7 of
+// each chunk), entry j*L + li holding the chunk lane li keeps in register j:
+// every read is 16 contiguous bytes per lane.
+template <int PLANE>
+__device__ __forceinline__ void gamma8(const float4 *g_lds, int e, float (&g)[8]) {
+  const float4 lo = g_lds[e];
+  const float4 hi = g_lds[e + PLANE];
+  g[0] = lo.x; g[1] = lo.y; g[2] = lo.z; g[3] = lo.w;
+  g[4] = hi.x; g[5] = hi.y; g[6] = hi.z; g[7] = hi.w;
+}
+
 __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
   v[0] = lo_f(w.x); v[1] = hi_f(w.x);
   v[2] = lo_f(w.y); v[3] = hi_f(w.y);
@@ -300,6 +314,22 @@ struct RopeShape {
   static constexpr int TPL = L >= 32 ? 1 : 32 / L;  // tasks per lane
 };
 
+// Chunk layout: each lane of a row owns C chunks of 16 bytes (8 values), in
+// units of P adjacent chunks (P = 2 when C >= 2, else 1).  Unit k of lane li
+// is u = li + L*k and covers chunks P*u .. P*u + P-1; register j = P*k + e
+// holds chunk P*u + e.  So a lane's code bytes of one unit are contiguous
+// (one store), the L units of a k form an aligned block of the row (the
+// RMSNorm tree and the quantisation groups stay lane-aligned), and every
+// pair of load instructions reads L*16*P contiguous bytes.
+template <int L, int C>
+struct Lay {
+  static constexpr int P = 1;
+  static constexpr int K = C / P;  // units per lane
+  __device__ static __forceinline__ int chunk(int li, int j) {
+    return P * (li + L * (j / P)) + (j % P);
+  }
+};
+
 template <int MODE, bool ROPE, int L, int C>
 struct RowBuf {
   static constexpr bool HAS_ROPE_SEG = MODE != M_MXFP4;
@@ -313,13 +343,13 @@ struct RowBuf {
 // Loads one row.  Every lane always issues the same loads (indices beyond
 // the row are clamped and their values cleared), so the number of memory
 // operations per iteration is fixed -- see the pipeline in the kernel.
-template <int MODE, bool NORM, bool ROPE, int L, int C, bool FAST>
+template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
 __device__ __forceinline__ void load_row(const KArgs &a, int64_t row, int li,
                                          RowBuf<MODE, ROPE, L, C> &b) {
   const uint16_t *xr = a.x + row * a.x_stride;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const int c = li + L * j;
+    const int c = Lay<L, C>::chunk(li, j);
     if constexpr (FAST) {
       b.xw[j] = ld16(xr + 8 * c);
     } else {
@@ -354,15 +384,17 @@ struct RowOut {
   uint32_t ry[MODE == M_MXFP4 ? 1 : RopeShape<L>::TPL];
 };
 
-template <int MODE, bool NORM, bool ROPE, int L, int C, bool FAST>
+template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
 __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
                                             const RowBuf<MODE, ROPE, L, C> &b,
-                                            const uint4 *g_lds, RowOut<MODE, L, C> &o) {
+                                            const float4 *g_lds, RowOut<MODE, L, C> &o) {
   // ---- RMSNorm -> packed bf16 yw ----
   uint4 yw[C];
+  using LY = Lay<L, C>;
+  constexpr int P = LY::P, K = LY::K;
   if constexpr (NORM) {
-    float part[C];
-    u16x2_t mn = {0x7FFF, 0x7FFF};  // smallest bf16 magnitude (bits) of the row
+    float s8[C];
+    float mn = __builtin_inff();  // smallest magnitude of the lane's values
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
@@ -373,34 +405,34 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       const float s23 = __builtin_fmaf(v[3], v[3], v[2] * v[2]);
       const float s45 = __builtin_fmaf(v[5], v[5], v[4] * v[4]);
       const float s67 = __builtin_fmaf(v[7], v[7], v[6] * v[6]);
-      part[j] = grp_sum<L>((s01 + s23) + (s45 + s67));
-      const int c = li + L * j;
+      s8[j] = (s01 + s23) + (s45 + s67);
+      const int c = LY::chunk(li, j);
       if (FAST || c < a.nchunk) {
-        const u16x2_t m01 = __builtin_bit_cast(u16x2_t, b.xw[j].x & 0x7FFF7FFFu);
-        const u16x2_t m23 = __builtin_bit_cast(u16x2_t, b.xw[j].y & 0x7FFF7FFFu);
-        const u16x2_t m45 = __builtin_bit_cast(u16x2_t, b.xw[j].z & 0x7FFF7FFFu);
-        const u16x2_t m67 = __builtin_bit_cast(u16x2_t, b.xw[j].w & 0x7FFF7FFFu);
-        mn = __builtin_elementwise_min(
-            mn, __builtin_elementwise_min(__builtin_elementwise_min(m01, m23),
-                                          __builtin_elementwise_min(m45, m67)));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mn = __builtin_fminf(mn, __builtin_fabsf(v[q]));
       }
     }
+    // tree: the P chunks of a unit, then the L lanes (butterfly), then the
+    // K unit blocks
+    float part[K];
 #pragma unroll
-    for (int w = 1; w < C; w *= 2)
+    for (int k = 0; k < K; ++k)
+      part[k] = grp_sum<L>(P == 2 ? s8[2 * k] + s8[2 * k + 1] : s8[k]);
 #pragma unroll
-      for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
+    for (int w = 1; w < K; w *= 2)
+#pragma unroll
+      for (int k = 0; k < K; k += 2 * w) part[k] = part[k] + part[k + w];
     const float ss = part[0];
     const float mean = a.inv_nseg != 0.0f ? ss * a.inv_nseg : ss / a.nseg_f;
     const float rms = __builtin_sqrtf(mean + a.eps);
     // The fast division needs a normal rms with a normal reciprocal, every
     // quotient normal (|x| >= 2^(e(rms) - 252) guarantees it) and an exact
     // FMA residual (|x| >= 2^-100).  Rows holding a smaller magnitude --
-    // including an exact zero -- divide exactly instead.  The magnitudes are
-    // compared as bf16 bit patterns (same order as the values).
+    // including an exact zero -- divide exactly instead.
     const int re = (int)(__float_as_uint(rms) >> 23);
     const int k = re - 252 > -100 ? re - 252 : -100;
-    const uint32_t thr = (uint32_t)(k + 127) << 7;  // bf16 bits of 2^k
-    const bool tiny = (uint32_t)min(mn.x, mn.y) < thr;
+    const float thr = __uint_as_float((uint32_t)(k + 127) << 23);  // 2^k
+    const bool tiny = mn < thr;
     bool fast = re >= 127 - 100 && re <= 127 + 100;
     if constexpr (L == 64) {
       fast = fast && __builtin_amdgcn_ballot_w64(tiny) == 0;
@@ -414,8 +446,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       for (int j = 0; j < C; ++j) {
         float v[8], g[8], y[8];
         unpack8(b.xw[j], v);
-        const int c = li + L * j;
-        unpack8(c < a.nchunk ? g_lds[c] : make_uint4(0, 0, 0, 0), g);
+        gamma8<L * C>(g_lds, j * L + li, g);
 #pragma unroll
         for (int q = 0; q < 8; ++q) y[q] = div_fast(v[q], rms, rcp) * g[q];
         yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
@@ -426,8 +457,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       for (int j = 0; j < C; ++j) {
         float v[8], g[8], y[8];
         unpack8(b.xw[j], v);
-        const int c = li + L * j;
-        unpack8(c < a.nchunk ? g_lds[c] : make_uint4(0, 0, 0, 0), g);
+        gamma8<L * C>(g_lds, j * L + li, g);
 #pragma unroll
         for (int q = 0; q < 8; ++q) y[q] = (v[q] / rms) * g[q];
         yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
@@ -470,58 +500,81 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      float v[8];
-      unpack8(yw[j], v);
-      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
+    for (int k = 0; k < K; ++k) {
+      float v[P][8];
 #pragma unroll
-      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
-      m = grp_max<4>(m);  // 32 values = 4 lanes
+      for (int e = 0; e < P; ++e) unpack8(yw[P * k + e], v[e]);
+      float m = __builtin_fmaxf(__builtin_fabsf(v[0][0]), __builtin_fabsf(v[0][1]));
+#pragma unroll
+      for (int e = 0; e < P; ++e)
+#pragma unroll
+        for (int q = e == 0 ? 2 : 0; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[e][q]));
+      m = grp_max<4 / P>(m);  // 32 values = 4 chunks
       const int E = e8m0_exp<2, 0x400000u>(m);  // FP4 max 6 = 1.5 * 2^2
-      uint32_t word = 0;
+      uint32_t word[P];
       if (E >= -100 && E <= 100) {
         const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], sc, 0);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], sc, 1);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], sc, 2);
-        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], sc, 3);
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          uint32_t w = 0;
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][0], v[e][1], sc, 0);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][2], v[e][3], sc, 1);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][4], v[e][5], sc, 2);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][6], v[e][7], sc, 3);
+          word[e] = w;
+        }
       } else {
         const float f = exp2_neg(E);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) word |= enc_e2m1_sw(v[q] * f) << (4 * q);
+        for (int e = 0; e < P; ++e) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) w |= enc_e2m1_sw(v[e][q] * f) << (4 * q);
+          word[e] = w;
+        }
       }
-      o.w[j].x = word;
-      o.sb[j] = (uint32_t)(E + 127);
+      o.w[k] = make_uint4(word[0], word[P - 1], 0u, 0u);
+      o.sb[k] = (uint32_t)(E + 127);
     }
   } else {  // FP8 modes
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      float v[8];
-      unpack8(yw[j], v);
-      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
+    for (int k = 0; k < K; ++k) {
+      float v[P][8];
 #pragma unroll
-      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
-      m = grp_max<8>(m);  // 64 values = 8 lanes
-      uint2 codes;
+      for (int e = 0; e < P; ++e) unpack8(yw[P * k + e], v[e]);
+      float m = __builtin_fmaxf(__builtin_fabsf(v[0][0]), __builtin_fabsf(v[0][1]));
+#pragma unroll
+      for (int e = 0; e < P; ++e)
+#pragma unroll
+        for (int q = e == 0 ? 2 : 0; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[e][q]));
+      m = grp_max<8 / P>(m);  // 64 values = 8 chunks
+      uint32_t cw[2 * P];
       uint32_t sbits;
       if constexpr (MODE == M_FP8_E8M0) {
         const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
         sbits = (uint32_t)(E + 127);
         if (E >= -100 && E <= 100) {
           const float sc = __uint_as_float(sbits << 23);
-          s16x2_t w0 = {0, 0}, w1 = {0, 0};
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[0], v[1], sc, false);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[2], v[3], sc, true);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[4], v[5], sc, false);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[6], v[7], sc, true);
-          codes = make_uint2(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1));
+#pragma unroll
+          for (int e = 0; e < P; ++e) {
+            s16x2_t w0 = {0, 0}, w1 = {0, 0};
+            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[e][0], v[e][1], sc, false);
+            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[e][2], v[e][3], sc, true);
+            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[e][4], v[e][5], sc, false);
+            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[e][6], v[e][7], sc, true);
+            cw[2 * e] = __builtin_bit_cast(uint32_t, w0);
+            cw[2 * e + 1] = __builtin_bit_cast(uint32_t, w1);
+          }
         } else {
           const float f = exp2_neg(E);
-          uint32_t q[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) q[k] = enc_e4m3_sw(v[k] * f);
-          codes = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                             q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+          for (int e = 0; e < P; ++e) {
+            uint32_t q[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) q[t] = enc_e4m3_sw(v[e][t] * f);
+            cw[2 * e] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            cw[2 * e + 1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+          }
         }
       } else {
         // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
@@ -537,30 +590,64 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         const float su = __uint_as_float(sbits << 16);
         if (fastq) {
           const float rs = rcp_rn(su);
-          float qv[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) qv[k] = div_fast(v[k], su, rs);
-          int w0 = 0, w1 = 0;
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], w1, false);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
-          codes = make_uint2((uint32_t)w0, (uint32_t)w1);
+          for (int e = 0; e < P; ++e) {
+            float qv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) qv[t] = div_fast(v[e][t], su, rs);
+            int w0 = 0, w1 = 0;
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], w1, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+            cw[2 * e] = (uint32_t)w0;
+            cw[2 * e + 1] = (uint32_t)w1;
+          }
         } else {
-          uint32_t q[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) q[k] = su > 0.0f ? enc_e4m3_sw(v[k] / su) : 0u;
-          codes = make_uint2(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                             q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24));
+          for (int e = 0; e < P; ++e) {
+            uint32_t q[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) q[t] = su > 0.0f ? enc_e4m3_sw(v[e][t] / su) : 0u;
+            cw[2 * e] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            cw[2 * e + 1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+          }
         }
       }
-      o.w[j] = make_uint4(codes.x, codes.y, 0u, 0u);
-      o.sb[j] = sbits;
+      o.w[k] = make_uint4(cw[0], cw[1], cw[2 * P - 2], cw[2 * P - 1]);
+      o.sb[k] = sbits;
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
   }
 }
+
+// FAST == 2 (mode 0, rows of one or two per wave): the rows of a
+// wave-iteration are assembled in LDS and leave as 16-byte pieces, lane i
+// storing piece i (and i + 64, ...); lanes past the last piece repeat
+// earlier pieces (same bytes, same address).  This replaces the many narrow
+// stores of a row (codes, scales, rope, pad) by two wide ones.
+template <int L, int C>
+struct Stage {
+  static constexpr int R = 64 / L;
+  // the largest row of this layout: nope codes, rope, bf16 scales, pad to 32
+  static constexpr int KCMAX = ((8 * L * C + 128 + 2 * ((8 * L * C + 63) / 64) + 31) / 32) * 32;
+  static constexpr int NST = (R * KCMAX / 16 + 63) / 64;  // store instructions
+  int lds[NST];   // byte offset of the piece in the wave's staging area
+  int off[NST];   // byte offset of the piece in its row
+  bool row1[NST]; // piece of the second row
+  __device__ void init(int lane, int kc) {
+    const int np = kc / 16, npt = R * np;
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int p = lane + 64 * i;
+      const int q = p < npt ? p : p % npt;
+      lds[i] = 16 * q;
+      row1[i] = q >= np;
+      off[i] = 16 * (q >= np ? q - np : q);
+    }
+  }
+};
 
 // Stores one computed row: exactly kvCacheCol bytes (plus the aux row).
 // Every lane issues every store, so that the number of memory operations per
@@ -568,42 +655,88 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 // (the group scale, the pad, duplicated rope tasks) write the same bytes to
 // the same address, and lanes with nothing to write (chunks past the row)
 // write to a private slot of the sink.
-template <int MODE, bool ROPE, int L, int C, bool FAST>
-__device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
-                                          const RowOut<MODE, L, C> &o) {
+template <int MODE, bool ROPE, int L, int C, int FAST>
+__device__ __forceinline__ void store_row(const KArgs &a, int li, int lane, int sub,
+                                          const RowOut<MODE, L, C> &o, uint8_t *stage,
+                                          const Stage<L, C> &sm) {
   constexpr int TPL = RopeShape<L>::TPL;
   // in FAST mode every row start is 16-byte aligned (k rows 4-byte aligned):
   // the alignment is a constant and the store helpers reduce to one store
   const int c_al = FAST ? 16 : a.c_align;
   const int a_al = FAST ? 4 : a.a_align;
   uint8_t *lsink = g_sink + 2 * kSinkHalf + 16 * lane;
+  using LY = Lay<L, C>;
+  constexpr int P = LY::P, K = LY::K;
   if constexpr (MODE == M_SPLIT) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
-      const int c = li + L * j;
+      const int c = LY::chunk(li, j);
       st_u128((FAST || c < a.nchunk) ? o.p0 + 16 * c : lsink, o.w[j], c_al);
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k) st_u32(o.p1 + 4 * ((li + L * k) & 31), o.ry[k], a_al);
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const int c = li + L * j;
+    for (int k = 0; k < K; ++k) {
+      const int c = P * (li + L * k);  // first chunk of the unit
       const bool in = FAST || c < a.nchunk;
-      st_u32(in ? o.p0 + 4 * c : lsink, o.w[j].x, c_al);
-      st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[j]);  // all 4 lanes of the group
+      if constexpr (P == 2)
+        st_u64(in ? o.p0 + 4 * c : lsink, make_uint2(o.w[k].x, o.w[k].y), c_al);
+      else
+        st_u32(in ? o.p0 + 4 * c : lsink, o.w[k].x, c_al);
+      st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[k]);  // every lane of the group
     }
-  } else {
+  } else if constexpr (FAST == 2) {
+    static_assert(MODE == M_FP8_BF16 && L >= 32 && P == 1, "staged stores: mode 0, L >= 32");
+    const int kc = a.kv_cache_col;
+    uint8_t *img = stage + sub * kc;
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int c = li + L * j;
+      *reinterpret_cast<uint2 *>(img + 8 * c) = make_uint2(o.w[j].x, o.w[j].y);
+    }
+    // zero the scale and pad area, then the scales over it
+    const int tail = a.nseg + 128;
+    if (li < (kc - tail) / 16) *reinterpret_cast<uint4 *>(img + tail + 16 * li) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      *reinterpret_cast<uint16_t *>(img + tail + 2 * (c >> 3)) = (uint16_t)o.sb[j];
+    }
+#pragma unroll
+    for (int k = 0; k < TPL; ++k)
+      *reinterpret_cast<uint32_t *>(img + a.nseg + 4 * ((li + L * k) & 31)) = o.ry[k];
+    // destination of each row (lane 0 and lane 32 hold them)
+    const uint64_t p0 = reinterpret_cast<uint64_t>(o.p0);
+    const uint64_t pa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(p0 >> 32), 0) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)p0, 0);
+    const uint64_t pb = L == 64 ? pa
+                                : ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(p0 >> 32), 32)
+                                   << 32) |
+                                      (uint32_t)__builtin_amdgcn_readlane((int)p0, 32);
+#pragma unroll
+    for (int i = 0; i < Stage<L, C>::NST; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(stage + sm.lds[i]);
+      // a global-memory pointer (an integer cast would otherwise give a
+      // flat store, which also counts against the LDS counter)
+      typedef __attribute__((address_space(1))) u32x4_t g_u32x4_t;
+      const u32x4_t w = {v.x, v.y, v.z, v.w};
+      *(g_u32x4_t *)((sm.row1[i] ? pb : pa) + (uint64_t)sm.off[i]) = w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int c = P * (li + L * k);  // first chunk of the unit
       const bool in = FAST || c < a.nchunk;
-      st_u64(in ? o.p0 + 8 * c : lsink, make_uint2(o.w[j].x, o.w[j].y), c_al);
+      if constexpr (P == 2)
+        st_u128(in ? o.p0 + 8 * c : lsink, o.w[k], c_al);
+      else
+        st_u64(in ? o.p0 + 8 * c : lsink, make_uint2(o.w[k].x, o.w[k].y), c_al);
       // every lane of the group writes the group's scale
       if constexpr (MODE == M_FP8_E8M0)
-        st_u8(in ? o.p0 + a.nseg + 128 + (c >> 3) : lsink + 8, o.sb[j]);
+        st_u8(in ? o.p0 + a.nseg + 128 + (c >> 3) : lsink + 8, o.sb[k]);
       else
-        st_u16(in ? o.p0 + a.nseg + 128 + 2 * (c >> 3) : lsink + 8, o.sb[j], c_al);
+        st_u16(in ? o.p0 + a.nseg + 128 + 2 * (c >> 3) : lsink + 8, o.sb[k], c_al);
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k)
@@ -626,19 +759,29 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
   }
 }
 
-template <int MODE, bool NORM, bool ROPE, int L, int C, bool FAST>
+template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
 __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   constexpr int R = 64 / L;    // rows per wave-iteration
-  constexpr int WIN = 64 / R;  // iterations covered by one slot window
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
   const int sub = lane / L;
   // gamma (the same for every row) staged once per block in LDS
-  extern __shared__ uint4 g_lds[];
+  extern __shared__ float4 g_lds[];
   if constexpr (NORM) {
-    for (int i = threadIdx.x; i < a.nchunk; i += 256) g_lds[i] = ld16_cached(a.gamma + 8 * i);
+    for (int i = threadIdx.x; i < L * C; i += 256) {
+      const int c = Lay<L, C>::chunk(i % L, i / L);
+      float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (c < a.nchunk) unpack8(ld16_cached(a.gamma + 8 * c), g);
+      g_lds[i] = make_float4(g[0], g[1], g[2], g[3]);
+      g_lds[i + L * C] = make_float4(g[4], g[5], g[6], g[7]);
+    }
     __syncthreads();
   }
+  // per-wave staging area for FAST == 2, after gamma
+  uint8_t *stage = reinterpret_cast<uint8_t *>(g_lds) + (NORM ? L * C * 32 : 0) +
+                   (threadIdx.x >> 6) * R * a.kv_cache_col;
+  Stage<L, C> sm;
+  if constexpr (FAST == 2) sm.init(lane, a.kv_cache_col);
   int blk = blockIdx.x;
   if (a.xcd_blocks > 0) blk = (blk & 7) * a.xcd_blocks + (blk >> 3);
   const int wave = __builtin_amdgcn_readfirstlane(blk * 4 + (int)(threadIdx.x >> 6));
@@ -694,7 +837,7 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it, slot), li, cur);
       if (slot < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, cur, g_lds, out);
       set_dest(slot, out);
-      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, sub, out, stage, sm);
     }
   } else {
     // Software pipeline, two rows ahead, with two register sets (A holds the
@@ -724,14 +867,14 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       set_dest(sA, out);
       sA = slot_pick(v2);
       load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it + 2, sA), li, bA);
-      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, sub, out, stage, sm);
       // ---- row it + 1 (B) ----
       v2 = slot_load(it + 4);
       if (sB < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, bB, g_lds, out);
       set_dest(sB, out);
       sB = slot_pick(v3);
       load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it + 3, sB), li, bB);
-      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, sub, out, stage, sm);
     }
   }
 }
@@ -741,7 +884,7 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
 // ------------------------------------------------------------------------
 typedef void (*kfn_t)(const KArgs);
 
-template <int MODE, bool NORM, bool ROPE, bool FAST>
+template <int MODE, bool NORM, bool ROPE, int FAST>
 kfn_t pick_layout_f(int L, int C) {
   if (L == 8) return epilog_kernel<MODE, NORM, ROPE, 8, 1, FAST>;
   if (L == 16) return epilog_kernel<MODE, NORM, ROPE, 16, 1, FAST>;
@@ -758,12 +901,16 @@ kfn_t pick_layout_f(int L, int C) {
 }
 
 template <int MODE, bool NORM, bool ROPE>
-kfn_t pick_layout(int L, int C, bool fast) {
-  return fast ? pick_layout_f<MODE, NORM, ROPE, true>(L, C)
-              : pick_layout_f<MODE, NORM, ROPE, false>(L, C);
+kfn_t pick_layout(int L, int C, int fast) {
+  if constexpr (MODE == M_FP8_BF16)
+    if (fast == 2)
+      return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1, 2>
+                    : epilog_kernel<MODE, NORM, ROPE, 32, 2, 2>;
+  return fast ? pick_layout_f<MODE, NORM, ROPE, 1>(L, C)
+              : pick_layout_f<MODE, NORM, ROPE, 0>(L, C);
 }
 
-kfn_t pick(int mode, bool norm, bool rope, int L, int C, bool fast) {
+kfn_t pick(int mode, bool norm, bool rope, int L, int C, int fast) {
   switch (mode) {
     case M_FP8_BF16:
       if (norm)
@@ -796,6 +943,30 @@ int device_cus() {
     cus[dev] = n;
   }
   return cus[dev];
+}
+
+// Blocks of 256 threads that one CU holds at once for a kernel instance (set
+// by its register and LDS use), cached per instance and LDS size.
+int blocks_per_cu(kfn_t fn, size_t lds) {
+  struct Entry {
+    kfn_t fn;
+    size_t lds;
+    int nb;
+  };
+  static Entry cache[128];
+  static int n = 0;
+  static std::mutex mu;
+  std::lock_guard<std::mutex> guard(mu);
+  for (int i = 0; i < n; ++i)
+    if (cache[i].fn == fn && cache[i].lds == lds) return cache[i].nb;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(fn), 256,
+                                                   lds) != hipSuccess ||
+      nb <= 0)
+    nb = 2;
+  if (nb > 8) nb = 8;
+  if (n < 128) cache[n++] = Entry{fn, lds, nb};
+  return nb;
 }
 
 }  // namespace kvepi
@@ -851,21 +1022,26 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
 
   const int rows_per_wave = 64 / L;
   const int64_t n_groups = (p.T + rows_per_wave - 1) / rows_per_wave;
+  // FAST: whole chunks per lane and 16-byte aligned rows (4-byte aligned k
+  // rows in the bf16 split mode); stores then need no alignment dispatch
+  // 2: mode 0 rows of at most 64 chunks also assemble their rows in LDS
+  const bool aligned = L * C == a.nchunk && a.c_align >= 16 &&
+                       (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
+  const int fast = !aligned ? 0 : (p.mode == KVEPI_MODE_FP8_BF16SCALE && L == 32) ? 2 : 1;
+  kfn_t fn = pick(p.mode, p.norm, p.rope, L, C, fast);
+  size_t lds = p.norm ? (size_t)L * C * 32 : 0;  // gamma as fp32, 32 KB at most
+  if (fast == 2) lds += (size_t)4 * (64 / L) * p.kv_cache_col;  // staging, 4 waves
+
+  // persistent waves: exactly as many blocks as the CUs hold at once
   const int cus = device_cus();
-  const int64_t max_waves = (int64_t)cus * 32;  // 8 blocks of 4 waves per CU
+  const int64_t max_waves = (int64_t)cus * blocks_per_cu(fn, lds) * 4;
   const int64_t waves = n_groups < max_waves ? n_groups : max_waves;
   const int64_t blocks = (waves + 3) / 4;
   a.nwaves = (int32_t)(blocks * 4);
   a.n_groups = (int32_t)n_groups;
   a.xcd_blocks = (blocks % 8 == 0) ? (int32_t)(blocks / 8) : 0;
 
-  // FAST: whole chunks per lane and 16-byte aligned rows (4-byte aligned k
-  // rows in the bf16 split mode); stores then need no alignment dispatch
-  const bool fast = L * C == a.nchunk && a.c_align >= 16 &&
-                    (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
-  kfn_t fn = pick(p.mode, p.norm, p.rope, L, C, fast);
   void *args[] = {&a};
-  const size_t lds = p.norm ? (size_t)p.nope * 2 : 0;  // gamma, 16 KB at most
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)blocks),
                                  dim3(256), args, lds, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVEPI_OK : KVEPI_ERR_RUNTIME;
