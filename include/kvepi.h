@@ -133,7 +133,7 @@ KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t gr
  *
  *  x             DEVICE, bf16 [num_tokens, d], rows x_row_stride elements
  *                apart; 16-byte aligned base, x_row_stride % 8 == 0 and
- *                x_row_stride >= d.  Leading dimensions of the caller's
+ *                d <= x_row_stride <= 2^27.  Leading dimensions of the caller's
  *                tensor are flattened into num_tokens
  *                ("aclnnKvCompressEpilog", 约束说明, slotMapping shape rule).
  *  gamma         DEVICE, bf16 [d-64], 16-byte aligned, or NULL for no

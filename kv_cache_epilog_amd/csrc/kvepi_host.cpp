@@ -96,7 +96,9 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
   if (num_tokens < 0 || num_tokens > INT32_MAX) return KVEPI_ERR_SHAPE;
   if (num_tokens > 0 && (x == nullptr || slot_mapping == nullptr))
     return KVEPI_ERR_NULLPTR;
-  if (x_row_stride < d || x_row_stride % 8 != 0) return KVEPI_ERR_LAYOUT;
+  // row offsets of x are kept in 32 bits on the device
+  if (x_row_stride < d || x_row_stride % 8 != 0 || x_row_stride > (INT64_C(1) << 27))
+    return KVEPI_ERR_LAYOUT;
   if (x != nullptr && !aligned(x, 16)) return KVEPI_ERR_LAYOUT;
   if (slot_mapping != nullptr && !aligned(slot_mapping, 4))
     return KVEPI_ERR_LAYOUT;

@@ -56,6 +56,7 @@ struct KArgs {
   const int32_t *slots;
   uint8_t *cache, *aux;
   int64_t x_stride;            // elements
+  uint32_t x_pitch;            // bytes between rows of x (2 * x_stride < 2^28)
   int64_t c_pitch, c_bstride;  // bytes
   int64_t a_pitch, a_bstride;  // bytes
   uint64_t bs_magic;           // slot / block_size == (slot * magic) >> shift
@@ -257,15 +258,15 @@ __device__ __forceinline__ uint8_t *row_addr(uint8_t *base, uint32_t s, const KA
 }
 
 // Streamed inputs (read once) use nontemporal loads.
-__device__ __forceinline__ uint4 ld16(const uint16_t *p) {
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ uint2 ld8(const uint16_t *p) {
+__device__ __forceinline__ uint2 ld8(const uint8_t *p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
   return make_uint2(v.x, v.y);
 }
-__device__ __forceinline__ uint32_t ld4(const uint16_t *p) {
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
 // gamma is shared by every row: a plain (cached) load.
@@ -302,7 +303,6 @@ __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
 // bytes per lane for lanes with nothing to store.
 constexpr int kSinkHalf = 16384;
 __device__ __attribute__((aligned(256))) uint8_t g_sink[2 * kSinkHalf + 64 * 16];
-__device__ int32_t kNoSlot = -1;  // read only; read in place of slots past the end
 enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4 };
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
@@ -340,35 +340,40 @@ struct RowBuf {
   uint32_t rs[HAS_ROPE_SEG && ROPE ? TPL : 1];  // sin pair
 };
 
-// Loads one row.  Every lane always issues the same loads (indices beyond
-// the row are clamped and their values cleared), so the number of memory
-// operations per iteration is fixed -- see the pipeline in the kernel.
+// Loads one row into registers.  xr, cr and sr are the wave-uniform bases of
+// the first row loaded by the wave in this iteration (x, cos, sin); dr is the
+// lane's row relative to it (0 for lanes of a skipped token, which read that
+// first row again).  Every lane always issues the same loads (chunk indices
+// beyond the row are clamped and their values cleared), so the number of
+// memory operations per iteration is fixed -- see the pipeline in the kernel.
 template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
-__device__ __forceinline__ void load_row(const KArgs &a, int64_t row, int li,
+__device__ __forceinline__ void load_row(const KArgs &a, const uint8_t *xr, const uint8_t *cr,
+                                         const uint8_t *sr, uint32_t dr, int li,
                                          RowBuf<MODE, ROPE, L, C> &b) {
-  const uint16_t *xr = a.x + row * a.x_stride;
+  const uint32_t xo = dr * a.x_pitch;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int c = Lay<L, C>::chunk(li, j);
     if constexpr (FAST) {
-      b.xw[j] = ld16(xr + 8 * c);
+      b.xw[j] = ld16(xr + (xo + 16u * (uint32_t)c));
     } else {
-      const uint4 v = ld16(xr + 8 * min(c, a.nchunk - 1));
+      const uint4 v = ld16(xr + (xo + 16u * (uint32_t)min(c, a.nchunk - 1)));
       b.xw[j] = c < a.nchunk ? v : make_uint4(0, 0, 0, 0);
     }
   }
   if constexpr (RowBuf<MODE, ROPE, L, C>::HAS_ROPE_SEG) {
     constexpr int TPL = RowBuf<MODE, ROPE, L, C>::TPL;
+    const uint32_t ro = xo + 2u * (uint32_t)a.nseg;
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
       const int tau = (li + L * k) & 31;
       if constexpr (ROPE) {
         const int p = tau & 15;
-        b.rx[k] = ld8(xr + a.nseg + 4 * p);
-        b.rc[k] = ld4(a.cos + row * 64 + 2 * tau);
-        b.rs[k] = ld4(a.sin + row * 64 + 2 * tau);
+        b.rx[k] = ld8(xr + (ro + 8u * (uint32_t)p));
+        b.rc[k] = ld4(cr + (128u * dr + 4u * (uint32_t)tau));
+        b.rs[k] = ld4(sr + (128u * dr + 4u * (uint32_t)tau));
       } else {
-        b.rx[k] = make_uint2(ld4(xr + a.nseg + 2 * tau), 0u);
+        b.rx[k] = make_uint2(ld4(xr + (ro + 4u * (uint32_t)tau)), 0u);
       }
     }
   }
@@ -622,32 +627,60 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
   }
 }
 
-// FAST == 2 (mode 0, rows of one or two per wave): the rows of a
-// wave-iteration are assembled in LDS and leave as 16-byte pieces, lane i
-// storing piece i (and i + 64, ...); lanes past the last piece repeat
-// earlier pieces (same bytes, same address).  This replaces the many narrow
-// stores of a row (codes, scales, rope, pad) by two wide ones.
-template <int L, int C>
-struct Stage {
-  static constexpr int R = 64 / L;
-  // the largest row of this layout: nope codes, rope, bf16 scales, pad to 32
-  static constexpr int KCMAX = ((8 * L * C + 128 + 2 * ((8 * L * C + 63) / 64) + 31) / 32) * 32;
-  static constexpr int NST = (R * KCMAX / 16 + 63) / 64;  // store instructions
-  int lds[NST];   // byte offset of the piece in the wave's staging area
-  int off[NST];   // byte offset of the piece in its row
-  bool row1[NST]; // piece of the second row
-  __device__ void init(int lane, int kc) {
-    const int np = kc / 16, npt = R * np;
+// FAST == 2 (mode 0, one or two rows per wave-iteration): each row is
+// assembled in LDS and leaves as one store of 16-byte pieces, lane i storing
+// piece i mod (kvCacheCol / 16) (lanes past the last piece repeat earlier
+// ones: same bytes, same address).  This replaces the many narrow stores of
+// a row (codes, scales, rope, pad) by one wide store per row.
+// The largest mode-0 row of a layout of L lanes x C chunks: nope codes,
+// rope, bf16 scales, padded to 32 bytes.
+constexpr int max_row_bytes(int L, int C) {
+  return ((8 * L * C + 128 + 2 * ((8 * L * C + 63) / 64) + 31) / 32) * 32;
+}
+
+// FAST == 2: writes the computed row into the wave's staging area (its own
+// image at stage + sub * kvCacheCol): codes, rope, scales, zero pad.
+template <int MODE, int L, int C>
+__device__ __forceinline__ void stage_write(const KArgs &a, int li, int sub,
+                                            const RowOut<MODE, L, C> &o, uint8_t *stage) {
+  static_assert(MODE == M_FP8_BF16 && L >= 32 && Lay<L, C>::P == 1, "staged rows: mode 0");
+  constexpr int TPL = RopeShape<L>::TPL;
+  const int kc = a.kv_cache_col;
+  uint8_t *img = stage + sub * kc;
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int p = lane + 64 * i;
-      const int q = p < npt ? p : p % npt;
-      lds[i] = 16 * q;
-      row1[i] = q >= np;
-      off[i] = 16 * (q >= np ? q - np : q);
-    }
+  for (int j = 0; j < C; ++j) {
+    const int c = li + L * j;
+    *reinterpret_cast<uint2 *>(img + 8 * c) = make_uint2(o.w[j].x, o.w[j].y);
   }
-};
+  // zero the scale and pad area, then the scales over it
+  const int tail = a.nseg + 128;
+  if (li < (kc - tail) / 16)
+    *reinterpret_cast<uint4 *>(img + tail + 16 * li) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int c = li + L * j;
+    *reinterpret_cast<uint16_t *>(img + tail + 2 * (c >> 3)) = (uint16_t)o.sb[j];
+  }
+#pragma unroll
+  for (int k = 0; k < TPL; ++k)
+    *reinterpret_cast<uint32_t *>(img + a.nseg + 4 * ((li + L * k) & 31)) = o.ry[k];
+}
+
+// FAST == 2: stores the staged rows of a wave-iteration, one instruction per
+// row, 16 bytes per lane; dst[r] is the destination of row r (wave-uniform),
+// off the lane's piece offset.  (Destinations are pointers derived from the
+// cache or the sink, never integers, so that the stores stay global ones.)
+template <int R>
+__device__ __forceinline__ void stage_store(const uint8_t *stage, int kc, uint32_t off,
+                                            uint8_t *const (&dst)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kc + off);
+    // a global-memory pointer (an integer cast would otherwise give a flat
+    // store, which also counts against the LDS counter)
+    *reinterpret_cast<uint4 *>(dst[r] + off) = v;
+  }
+}
 
 // Stores one computed row: exactly kvCacheCol bytes (plus the aux row).
 // Every lane issues every store, so that the number of memory operations per
@@ -656,9 +689,8 @@ struct Stage {
 // the same address, and lanes with nothing to write (chunks past the row)
 // write to a private slot of the sink.
 template <int MODE, bool ROPE, int L, int C, int FAST>
-__device__ __forceinline__ void store_row(const KArgs &a, int li, int lane, int sub,
-                                          const RowOut<MODE, L, C> &o, uint8_t *stage,
-                                          const Stage<L, C> &sm) {
+__device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
+                                          const RowOut<MODE, L, C> &o) {
   constexpr int TPL = RopeShape<L>::TPL;
   // in FAST mode every row start is 16-byte aligned (k rows 4-byte aligned):
   // the alignment is a constant and the store helpers reduce to one store
@@ -685,43 +717,6 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane, int 
       else
         st_u32(in ? o.p0 + 4 * c : lsink, o.w[k].x, c_al);
       st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[k]);  // every lane of the group
-    }
-  } else if constexpr (FAST == 2) {
-    static_assert(MODE == M_FP8_BF16 && L >= 32 && P == 1, "staged stores: mode 0, L >= 32");
-    const int kc = a.kv_cache_col;
-    uint8_t *img = stage + sub * kc;
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const int c = li + L * j;
-      *reinterpret_cast<uint2 *>(img + 8 * c) = make_uint2(o.w[j].x, o.w[j].y);
-    }
-    // zero the scale and pad area, then the scales over it
-    const int tail = a.nseg + 128;
-    if (li < (kc - tail) / 16) *reinterpret_cast<uint4 *>(img + tail + 16 * li) = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const int c = li + L * j;
-      *reinterpret_cast<uint16_t *>(img + tail + 2 * (c >> 3)) = (uint16_t)o.sb[j];
-    }
-#pragma unroll
-    for (int k = 0; k < TPL; ++k)
-      *reinterpret_cast<uint32_t *>(img + a.nseg + 4 * ((li + L * k) & 31)) = o.ry[k];
-    // destination of each row (lane 0 and lane 32 hold them)
-    const uint64_t p0 = reinterpret_cast<uint64_t>(o.p0);
-    const uint64_t pa = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(p0 >> 32), 0) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)p0, 0);
-    const uint64_t pb = L == 64 ? pa
-                                : ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(p0 >> 32), 32)
-                                   << 32) |
-                                      (uint32_t)__builtin_amdgcn_readlane((int)p0, 32);
-#pragma unroll
-    for (int i = 0; i < Stage<L, C>::NST; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(stage + sm.lds[i]);
-      // a global-memory pointer (an integer cast would otherwise give a
-      // flat store, which also counts against the LDS counter)
-      typedef __attribute__((address_space(1))) u32x4_t g_u32x4_t;
-      const u32x4_t w = {v.x, v.y, v.z, v.w};
-      *(g_u32x4_t *)((sm.row1[i] ? pb : pa) + (uint64_t)sm.off[i]) = w;
     }
   } else {
 #pragma unroll
@@ -759,9 +754,22 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane, int 
   }
 }
 
+// Wave-uniform description of one wave-iteration (R rows): which rows are
+// live, the first live row (the one skipped tokens read instead of their
+// own) and every row's slot.
+template <int R>
+struct IterInfo {
+  uint32_t live;   // bit r: row r is live
+  uint32_t g;      // row group (rows g * R + r)
+  uint32_t first;  // first live row, 0 if none
+  uint32_t sl[R];  // slot of each row
+  uint32_t own;    // (R > 2) slot of the lane's own row, per lane
+};
+
 template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
 __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
-  constexpr int R = 64 / L;    // rows per wave-iteration
+  constexpr int R = 64 / L;  // rows per wave-iteration
+  static_assert(FAST != 2 || (R <= 2 && max_row_bytes(L, C) <= 1024), "staged rows");
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
   const int sub = lane / L;
@@ -780,101 +788,153 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   // per-wave staging area for FAST == 2, after gamma
   uint8_t *stage = reinterpret_cast<uint8_t *>(g_lds) + (NORM ? L * C * 32 : 0) +
                    (threadIdx.x >> 6) * R * a.kv_cache_col;
-  Stage<L, C> sm;
-  if constexpr (FAST == 2) sm.init(lane, a.kv_cache_col);
+  const uint32_t piece = FAST == 2 ? 16u * (uint32_t)(lane % (a.kv_cache_col / 16)) : 0u;
   int blk = blockIdx.x;
   if (a.xcd_blocks > 0) blk = (blk & 7) * a.xcd_blocks + (blk >> 3);
   const int wave = __builtin_amdgcn_readfirstlane(blk * 4 + (int)(threadIdx.x >> 6));
   if (wave >= a.n_groups) return;
   const int n_it = (a.n_groups - wave + a.nwaves - 1) / a.nwaves;
-
   const uint32_t ns = (uint32_t)a.num_slots;
-  // Slots of iteration j: lane l loads the slot of row g(j) * R + l % R, where
-  // g(j) = wave + j * nwaves; beyond the wave's iterations or the tokens the
-  // value is -1.  Every lane issues the load.
-  // (out-of-range lanes read the constant -1 instead of being masked, so
-  // that nothing but the load touches the result until it is used)
-  auto slot_load = [&](int j) -> int {
-    const int64_t r = ((int64_t)wave + (int64_t)j * a.nwaves) * R + (lane % R);
-    const bool ok = j < n_it && r < a.T;
-    return __builtin_nontemporal_load(ok ? a.slots + r : &kNoSlot);
+
+  // Slots come in windows of L iterations: lane l of window w holds the
+  // slot of row sub = l % R of iteration j = w * L + l / R.  Lanes past the
+  // wave's rows read slot 0 (their value is never used).
+  auto win_load = [&](int w) -> int {
+    const int j = w * L + lane / R;
+    const int64_t r = ((int64_t)wave + (int64_t)j * a.nwaves) * R + lane % R;
+    return __builtin_nontemporal_load(a.slots + (j < n_it && r < a.T ? r : 0));
   };
-  auto slot_pick = [&](int v) -> uint32_t {
-    if constexpr (R == 1) {
-      return (uint32_t)__builtin_amdgcn_readfirstlane(v);
-    } else if constexpr (R == 2) {
-      const int s0 = __builtin_amdgcn_readlane(v, 0);
-      const int s1 = __builtin_amdgcn_readlane(v, 1);
-      return (uint32_t)(sub ? s1 : s0);
-    } else {
-      return (uint32_t)__builtin_amdgcn_ds_bpermute(4 * sub, v);
+  // iteration j's rows, from the window holding it
+  // (32-bit row arithmetic: for j < n_it every row index is below T + R)
+  auto prep = [&](int j, int win) -> IterInfo<R> {
+    IterInfo<R> t;
+    t.live = 0;
+    t.first = 0;
+    if constexpr (R > 2)
+      t.own = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((j % L) * R + sub), win);
+    t.g = (uint32_t)wave + (uint32_t)j * (uint32_t)a.nwaves;
+    const bool in = j < n_it;
+#pragma unroll
+    for (int r = R - 1; r >= 0; --r) {
+      const uint32_t sl = (uint32_t)__builtin_amdgcn_readlane(win, (j % L) * R + r);
+      const uint32_t row = t.g * R + r;
+      t.sl[r] = sl;
+      if (in && row < (uint32_t)a.T && sl < ns) {
+        t.live |= 1u << r;
+        t.first = row;  // the loop runs downwards: the last assignment is the first row
+      }
+    }
+    return t;
+  };
+  const uint32_t subbit = 1u << sub;
+  auto lane_live = [&](const IterInfo<R> &t) -> bool { return (t.live & subbit) != 0; };
+  // issues the loads of iteration j's rows
+  auto issue = [&](const IterInfo<R> &t, RowBuf<MODE, ROPE, L, C> &b) {
+    const uint32_t dr = lane_live(t) ? t.g * R + sub - t.first : 0u;
+    const uint8_t *xr = reinterpret_cast<const uint8_t *>(a.x) + (uint64_t)t.first * a.x_pitch;
+    const uint8_t *cr = reinterpret_cast<const uint8_t *>(a.cos) + (uint64_t)t.first * 128;
+    const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)t.first * 128;
+    load_row<MODE, NORM, ROPE, L, C, FAST>(a, xr, cr, sr, dr, li, b);
+  };
+  // computes iteration j's rows and stores them (after the caller has issued
+  // the next loads)
+  RowOut<MODE, L, C> out;
+  auto compute = [&](const IterInfo<R> &t, const RowBuf<MODE, ROPE, L, C> &b) {
+    if (lane_live(t)) {
+      compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, b, g_lds, out);
+      if constexpr (FAST == 2) stage_write<MODE, L, C>(a, li, sub, out, stage);
     }
   };
-  // source row of iteration j: its own row when the slot is valid, else row
-  // 0 (a cached dummy read, so that every iteration issues the same loads)
-  auto src_row = [&](int j, uint32_t slot) -> int64_t {
-    return slot < ns ? ((int64_t)wave + (int64_t)j * a.nwaves) * R + sub : 0;
+  // destination of row r (the sink when it is not live)
+  // (pointers, not integers, so that the compiler keeps them global)
+  auto dst = [&](const IterInfo<R> &t, int r) -> uint8_t * {
+    return (t.live >> r) & 1 ? row_addr(a.cache, t.sl[r], a, a.c_pitch, a.c_bstride) : g_sink;
   };
-  // destination of a row: its cache row, or the sink for a skipped token
-  auto set_dest = [&](uint32_t slot, RowOut<MODE, L, C> &o) {
-    if (slot < ns) {
-      o.p0 = row_addr(a.cache, slot, a, a.c_pitch, a.c_bstride);
-      if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT)
-        o.p1 = row_addr(a.aux, slot, a, a.a_pitch, a.a_bstride);
+  auto adst = [&](const IterInfo<R> &t, int r) -> uint8_t * {
+    return (t.live >> r) & 1 ? row_addr(a.aux, t.sl[r], a, a.a_pitch, a.a_bstride)
+                             : g_sink + kSinkHalf;
+  };
+  auto store = [&](const IterInfo<R> &t) {
+    if constexpr (FAST == 2) {
+      uint8_t *d[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) d[r] = dst(t, r);
+      stage_store<R>(stage, a.kv_cache_col, piece, d);
     } else {
-      o.p0 = g_sink;
-      o.p1 = g_sink + kSinkHalf;
+      uint8_t *d, *ad = nullptr;
+      if constexpr (R <= 2) {
+        // per-row destinations on the scalar unit, then picked per lane
+        d = dst(t, 0);
+        if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT) ad = adst(t, 0);
+        if constexpr (R == 2) {
+          d = sub ? dst(t, 1) : d;
+          if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT) ad = sub ? adst(t, 1) : ad;
+        }
+      } else {
+        // many rows per wave: each lane computes its own row's destination
+        const uint32_t sl = t.own;
+        const bool live = lane_live(t);
+        d = live ? row_addr(a.cache, sl, a, a.c_pitch, a.c_bstride) : g_sink;
+        if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT)
+          ad = live ? row_addr(a.aux, sl, a, a.a_pitch, a.a_bstride) : g_sink + kSinkHalf;
+      }
+      out.p0 = d;
+      out.p1 = ad;
+      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, out);
     }
   };
 
-  RowOut<MODE, L, C> out;
+  int win_cur = win_load(0), win_next = win_load(1);
+  // window of iteration j, loading the one after it on entering a window
+  auto window = [&](int j) -> int {
+    if (j % L == 0 && j > 0) {
+      win_cur = win_next;
+      win_next = win_load(j / L + 1);
+    }
+    return win_cur;
+  };
+
   if constexpr (C > 2) {
     // rows of more than two chunks per lane: no prefetch (their registers
     // are needed for the row itself)
     RowBuf<MODE, ROPE, L, C> cur;
     for (int it = 0; it < n_it; ++it) {
-      const uint32_t slot = slot_pick(slot_load(it));
-      load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it, slot), li, cur);
-      if (slot < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, cur, g_lds, out);
-      set_dest(slot, out);
-      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, sub, out, stage, sm);
+      const IterInfo<R> t = prep(it, window(it));
+      issue(t, cur);
+      compute(t, cur);
+      store(t);
     }
   } else {
-    // Software pipeline, two rows ahead, with two register sets (A holds the
-    // even iterations, B the odd ones).  gfx9 has a single in-order counter
-    // for vector loads and stores, so a wait for a load also waits for every
-    // store issued before it.  Each half-iteration j therefore computes row
-    // j (loaded two half-iterations earlier), then issues the loads of row
-    // j + 2 and only then the stores of row j; the wait before computing row
-    // j + 2 then leaves the stores of rows j and j + 1 in flight.  Every
-    // half-iteration issues the same memory operations (dummy loads of row 0
-    // and stores to a sink for skipped tokens and for the tail), so the
-    // compiler's wait counts are exact; slots are loaded three
-    // half-iterations ahead.
+    // Software pipeline, two iterations ahead, with two register sets (A
+    // holds the even iterations, B the odd ones).  gfx9 has a single in-order
+    // counter for vector loads and stores, so a wait for a load also waits
+    // for every store issued before it.  Each half-iteration j therefore
+    // computes iteration j (loaded two half-iterations earlier), then issues
+    // the loads of iteration j + 2 and only then the stores of iteration j;
+    // the wait before computing j + 2 then leaves the stores of j and j + 1
+    // in flight.  Every half-iteration issues the same memory operations
+    // (skipped tokens re-read a live row of their iteration and store to a
+    // sink), so the compiler's wait counts are exact.
     RowBuf<MODE, ROPE, L, C> bA, bB;
-    int v0 = slot_load(0), v1 = slot_load(1), v2 = slot_load(2), v3;
-    uint32_t sA = slot_pick(v0), sB = slot_pick(v1);
-    load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(0, sA), li, bA);
-    load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(1, sB), li, bB);
+    IterInfo<R> tA = prep(0, window(0));
+    issue(tA, bA);
+    IterInfo<R> tB = prep(1, window(1));
+    issue(tB, bB);
     // drain once before the loop: otherwise the loop's waits are sized for
     // the first trip, whose loads were issued in an order of the compiler's
     // choosing
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     for (int it = 0; it < n_it; it += 2) {
-      // ---- row it (A) ----
-      v3 = slot_load(it + 3);
-      if (sA < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, bA, g_lds, out);
-      set_dest(sA, out);
-      sA = slot_pick(v2);
-      load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it + 2, sA), li, bA);
-      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, sub, out, stage, sm);
-      // ---- row it + 1 (B) ----
-      v2 = slot_load(it + 4);
-      if (sB < ns) compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, bB, g_lds, out);
-      set_dest(sB, out);
-      sB = slot_pick(v3);
-      load_row<MODE, NORM, ROPE, L, C, FAST>(a, src_row(it + 3, sB), li, bB);
-      store_row<MODE, ROPE, L, C, FAST>(a, li, lane, sub, out, stage, sm);
+      compute(tA, bA);
+      const IterInfo<R> nA = prep(it + 2, window(it + 2));
+      issue(nA, bA);
+      store(tA);
+      tA = nA;
+      compute(tB, bB);
+      const IterInfo<R> nB = prep(it + 3, window(it + 3));
+      issue(nB, bB);
+      store(tB);
+      tB = nB;
     }
   }
 }
@@ -982,6 +1042,7 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   a.cache = p.cache;
   a.aux = p.aux;
   a.x_stride = p.x_stride;
+  a.x_pitch = (uint32_t)(p.x_stride * 2);
   a.c_pitch = p.c_pitch;
   a.c_bstride = p.c_bstride;
   a.a_pitch = p.a_pitch;

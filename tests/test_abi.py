@@ -127,6 +127,7 @@ BAD = [
     ("x misaligned", dict(x=P16 + 2), 3),
     ("x row stride < d", dict(xs=128), 3),
     ("x row stride not 16 B", dict(xs=260), 3),
+    ("x row stride over 2^27", dict(xs=(1 << 27) + 8), 3),
     ("slots misaligned", dict(slots=P16B + 2), 3),
     ("cos without sin", dict(cos=P16C), 4),
     ("negative eps", dict(gamma=P16C, eps=-1.0), 4),
