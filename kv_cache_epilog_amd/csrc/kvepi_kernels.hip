@@ -589,17 +589,27 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         // finite values and the NaN code for inf / inf).
         // m in [2^-71, 2^100] keeps m / 448 and the stored scale inside the
         // range of the fast division and reciprocal
+        // Fast path: m / 448 = fma(m, H, m * Lo) with H + Lo a double-length
+        // 1/448, and v / su = fma(v, rs, v * rl) with rs + rl a double-length
+        // 1/su: both are exactly the IEEE quotient for bf16 operands (their
+        // distance to a rounding boundary is far above the error), except
+        // that v / su below 2^-100 may differ -- where every code is +-0.
+        // rs is rounded downwards so that rl >= 0 and a zero v keeps its sign.
         const bool fastq = m >= 0x1p-71f && m <= 0x1p+100f;
-        const float s32 = fastq ? div_fast(m, 448.0f, 1.0f / 448.0f) : m / 448.0f;
+        constexpr float H448 = 1.0f / 448.0f;
+        constexpr float L448 = (float)(1.0 / 448.0 - (double)H448);
+        const float s32 = fastq ? __builtin_fmaf(m, H448, m * L448) : m / 448.0f;
         sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
         const float su = __uint_as_float(sbits << 16);
         if (fastq) {
-          const float rs = rcp_rn(su);
+          float rs = rcp_rn(su);
+          if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
+          const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
 #pragma unroll
           for (int e = 0; e < P; ++e) {
             float qv[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) qv[t] = div_fast(v[e][t], su, rs);
+            for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[e][t], rs, v[e][t] * rl);
             int w0 = 0, w1 = 0;
             w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
             w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
