@@ -846,6 +846,16 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
     const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)t.first * 128;
     load_row<MODE, NORM, ROPE, L, C, FAST>(a, xr, cr, sr, dr, li, b);
   };
+  // issues the loads of iteration j's own rows, whatever their slots (rows
+  // past the tokens read the last token's row)
+  auto issue_own = [&](int j, RowBuf<MODE, ROPE, L, C> &b) {
+    const uint32_t base = j < n_it ? ((uint32_t)wave + (uint32_t)j * (uint32_t)a.nwaves) * R : 0u;
+    const uint32_t dr = min((uint32_t)sub, (uint32_t)a.T - 1u - base);
+    const uint8_t *xr = reinterpret_cast<const uint8_t *>(a.x) + (uint64_t)base * a.x_pitch;
+    const uint8_t *cr = reinterpret_cast<const uint8_t *>(a.cos) + (uint64_t)base * 128;
+    const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)base * 128;
+    load_row<MODE, NORM, ROPE, L, C, FAST>(a, xr, cr, sr, dr, li, b);
+  };
   // computes iteration j's rows and stores them (after the caller has issued
   // the next loads)
   RowOut<MODE, L, C> out;
@@ -926,10 +936,14 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
     // (skipped tokens re-read a live row of their iteration and store to a
     // sink), so the compiler's wait counts are exact.
     RowBuf<MODE, ROPE, L, C> bA, bB;
+    // The first two iterations load every lane's own row before the slots
+    // are known (a skipped token's row is read for nothing), so that the
+    // row loads do not wait for the slot window: short launches are bound by
+    // this chain of memory latencies.
+    issue_own(0, bA);
+    issue_own(1, bB);
     IterInfo<R> tA = prep(0, window(0));
-    issue(tA, bA);
     IterInfo<R> tB = prep(1, window(1));
-    issue(tB, bB);
     // drain once before the loop: otherwise the loop's waits are sized for
     // the first trip, whose loads were issued in an order of the compiler's
     // choosing
