@@ -3,10 +3,9 @@
 // One kernel template covers every mode.  A token row is handled by a group
 // of L lanes of one 64-lane wavefront (64/L rows per wave-iteration: L = 32,
 // two rows per wave, for the d = 576 rows; L = 16, four rows, for the d = 128
-// indexer rows).  Each lane owns C 16-byte chunks of 8 bf16 values, in
-// units of two adjacent chunks when C >= 2 (see Lay), so that the codes of a
-// unit leave in one store and a quantisation group spans whole lanes.  The
-// path is bound by HBM bandwidth; the design keeps the VALU work and the
+// indexer rows).  Each lane owns C 16-byte chunks of 8 bf16 values, chunk
+// li + L*j, so every load instruction reads L*16 contiguous bytes of a row.
+// The path is bound by HBM bandwidth; the design keeps the VALU work and the
 // number of memory instructions per row small:
 //  - waves are persistent (one block per resident slot of the device); each
 //    wave loads its slots ahead and issues the loads of the row two steps
@@ -314,21 +313,15 @@ struct RopeShape {
   static constexpr int TPL = L >= 32 ? 1 : 32 / L;  // tasks per lane
 };
 
-// Chunk layout: each lane of a row owns C chunks of 16 bytes (8 values), in
-// units of P adjacent chunks (P = 2 when C >= 2, else 1).  Unit k of lane li
-// is u = li + L*k and covers chunks P*u .. P*u + P-1; register j = P*k + e
-// holds chunk P*u + e.  So a lane's code bytes of one unit are contiguous
-// (one store), the L units of a k form an aligned block of the row (the
-// RMSNorm tree and the quantisation groups stay lane-aligned), and every
-// pair of load instructions reads L*16*P contiguous bytes.
-template <int L, int C>
-struct Lay {
-  static constexpr int P = 1;
-  static constexpr int K = C / P;  // units per lane
-  __device__ static __forceinline__ int chunk(int li, int j) {
-    return P * (li + L * (j / P)) + (j % P);
-  }
-};
+// Chunk layout: lane li of a row owns C chunks of 16 bytes (8 values),
+// chunk li + L*j in register j.  Each load instruction then reads L*16
+// contiguous bytes of the row, the L lanes of a register j cover an aligned
+// block of the row (the RMSNorm tree and the quantisation groups stay
+// lane-aligned) and a lane's codes of one chunk are contiguous.
+template <int L>
+__device__ __forceinline__ int chunk_of(int li, int j) {
+  return li + L * j;
+}
 
 template <int MODE, bool ROPE, int L, int C>
 struct RowBuf {
@@ -353,7 +346,7 @@ __device__ __forceinline__ void load_row(const KArgs &a, const uint8_t *xr, cons
   const uint32_t xo = dr * a.x_pitch;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const int c = Lay<L, C>::chunk(li, j);
+    const int c = chunk_of<L>(li, j);
     if constexpr (FAST) {
       b.xw[j] = ld16(xr + (xo + 16u * (uint32_t)c));
     } else {
@@ -395,8 +388,6 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
                                             const float4 *g_lds, RowOut<MODE, L, C> &o) {
   // ---- RMSNorm -> packed bf16 yw ----
   uint4 yw[C];
-  using LY = Lay<L, C>;
-  constexpr int P = LY::P, K = LY::K;
   if constexpr (NORM) {
     float s8[C];
     float mn = __builtin_inff();  // smallest magnitude of the lane's values
@@ -411,22 +402,21 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       const float s45 = __builtin_fmaf(v[5], v[5], v[4] * v[4]);
       const float s67 = __builtin_fmaf(v[7], v[7], v[6] * v[6]);
       s8[j] = (s01 + s23) + (s45 + s67);
-      const int c = LY::chunk(li, j);
+      const int c = chunk_of<L>(li, j);
       if (FAST || c < a.nchunk) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) mn = __builtin_fminf(mn, __builtin_fabsf(v[q]));
       }
     }
-    // tree: the P chunks of a unit, then the L lanes (butterfly), then the
-    // K unit blocks
-    float part[K];
+    // tree: the 8 values of a chunk, then the L lanes (butterfly), then the
+    // C blocks of L chunks
+    float part[C];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      part[k] = grp_sum<L>(P == 2 ? s8[2 * k] + s8[2 * k + 1] : s8[k]);
+    for (int j = 0; j < C; ++j) part[j] = grp_sum<L>(s8[j]);
 #pragma unroll
-    for (int w = 1; w < K; w *= 2)
+    for (int w = 1; w < C; w *= 2)
 #pragma unroll
-      for (int k = 0; k < K; k += 2 * w) part[k] = part[k] + part[k + w];
+      for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
     const float ss = part[0];
     const float mean = a.inv_nseg != 0.0f ? ss * a.inv_nseg : ss / a.nseg_f;
     const float rms = __builtin_sqrtf(mean + a.eps);
@@ -505,81 +495,59 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float v[P][8];
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
 #pragma unroll
-      for (int e = 0; e < P; ++e) unpack8(yw[P * k + e], v[e]);
-      float m = __builtin_fmaxf(__builtin_fabsf(v[0][0]), __builtin_fabsf(v[0][1]));
-#pragma unroll
-      for (int e = 0; e < P; ++e)
-#pragma unroll
-        for (int q = e == 0 ? 2 : 0; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[e][q]));
-      m = grp_max<4 / P>(m);  // 32 values = 4 chunks
+      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
+      m = grp_max<4>(m);  // 32 values = 4 lanes
       const int E = e8m0_exp<2, 0x400000u>(m);  // FP4 max 6 = 1.5 * 2^2
-      uint32_t word[P];
+      uint32_t w = 0;
       if (E >= -100 && E <= 100) {
         const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
-#pragma unroll
-        for (int e = 0; e < P; ++e) {
-          uint32_t w = 0;
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][0], v[e][1], sc, 0);
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][2], v[e][3], sc, 1);
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][4], v[e][5], sc, 2);
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[e][6], v[e][7], sc, 3);
-          word[e] = w;
-        }
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], sc, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], sc, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], sc, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], sc, 3);
       } else {
         const float f = exp2_neg(E);
 #pragma unroll
-        for (int e = 0; e < P; ++e) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) w |= enc_e2m1_sw(v[e][q] * f) << (4 * q);
-          word[e] = w;
-        }
+        for (int q = 0; q < 8; ++q) w |= enc_e2m1_sw(v[q] * f) << (4 * q);
       }
-      o.w[k] = make_uint4(word[0], word[P - 1], 0u, 0u);
-      o.sb[k] = (uint32_t)(E + 127);
+      o.w[j] = make_uint4(w, 0u, 0u, 0u);
+      o.sb[j] = (uint32_t)(E + 127);
     }
   } else {  // FP8 modes
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float v[P][8];
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
 #pragma unroll
-      for (int e = 0; e < P; ++e) unpack8(yw[P * k + e], v[e]);
-      float m = __builtin_fmaxf(__builtin_fabsf(v[0][0]), __builtin_fabsf(v[0][1]));
-#pragma unroll
-      for (int e = 0; e < P; ++e)
-#pragma unroll
-        for (int q = e == 0 ? 2 : 0; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[e][q]));
-      m = grp_max<8 / P>(m);  // 64 values = 8 chunks
-      uint32_t cw[2 * P];
+      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
+      m = grp_max<8>(m);  // 64 values = 8 lanes
+      uint32_t cw[2];
       uint32_t sbits;
       if constexpr (MODE == M_FP8_E8M0) {
         const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
         sbits = (uint32_t)(E + 127);
         if (E >= -100 && E <= 100) {
           const float sc = __uint_as_float(sbits << 23);
-#pragma unroll
-          for (int e = 0; e < P; ++e) {
-            s16x2_t w0 = {0, 0}, w1 = {0, 0};
-            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[e][0], v[e][1], sc, false);
-            w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[e][2], v[e][3], sc, true);
-            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[e][4], v[e][5], sc, false);
-            w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[e][6], v[e][7], sc, true);
-            cw[2 * e] = __builtin_bit_cast(uint32_t, w0);
-            cw[2 * e + 1] = __builtin_bit_cast(uint32_t, w1);
-          }
+          s16x2_t w0 = {0, 0}, w1 = {0, 0};
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[0], v[1], sc, false);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[2], v[3], sc, true);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[4], v[5], sc, false);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[6], v[7], sc, true);
+          cw[0] = __builtin_bit_cast(uint32_t, w0);
+          cw[1] = __builtin_bit_cast(uint32_t, w1);
         } else {
           const float f = exp2_neg(E);
+          uint32_t q[8];
 #pragma unroll
-          for (int e = 0; e < P; ++e) {
-            uint32_t q[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) q[t] = enc_e4m3_sw(v[e][t] * f);
-            cw[2 * e] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-            cw[2 * e + 1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-          }
+          for (int t = 0; t < 8; ++t) q[t] = enc_e4m3_sw(v[t] * f);
+          cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
         }
       } else {
         // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
@@ -605,32 +573,26 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
           float rs = rcp_rn(su);
           if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
           const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
+          float qv[8];
 #pragma unroll
-          for (int e = 0; e < P; ++e) {
-            float qv[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[e][t], rs, v[e][t] * rl);
-            int w0 = 0, w1 = 0;
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], w1, false);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
-            cw[2 * e] = (uint32_t)w0;
-            cw[2 * e + 1] = (uint32_t)w1;
-          }
+          for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[t], rs, v[t] * rl);
+          int w0 = 0, w1 = 0;
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], w1, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
+          cw[0] = (uint32_t)w0;
+          cw[1] = (uint32_t)w1;
         } else {
+          uint32_t q[8];
 #pragma unroll
-          for (int e = 0; e < P; ++e) {
-            uint32_t q[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) q[t] = su > 0.0f ? enc_e4m3_sw(v[e][t] / su) : 0u;
-            cw[2 * e] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-            cw[2 * e + 1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-          }
+          for (int t = 0; t < 8; ++t) q[t] = su > 0.0f ? enc_e4m3_sw(v[t] / su) : 0u;
+          cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
         }
       }
-      o.w[k] = make_uint4(cw[0], cw[1], cw[2 * P - 2], cw[2 * P - 1]);
-      o.sb[k] = sbits;
+      o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
+      o.sb[j] = sbits;
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
@@ -653,7 +615,7 @@ constexpr int max_row_bytes(int L, int C) {
 template <int MODE, int L, int C>
 __device__ __forceinline__ void stage_write(const KArgs &a, int li, int sub,
                                             const RowOut<MODE, L, C> &o, uint8_t *stage) {
-  static_assert(MODE == M_FP8_BF16 && L >= 32 && Lay<L, C>::P == 1, "staged rows: mode 0");
+  static_assert(MODE == M_FP8_BF16 && L >= 32, "staged rows: mode 0");
   constexpr int TPL = RopeShape<L>::TPL;
   const int kc = a.kv_cache_col;
   uint8_t *img = stage + sub * kc;
@@ -707,41 +669,33 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
   const int c_al = FAST ? 16 : a.c_align;
   const int a_al = FAST ? 4 : a.a_align;
   uint8_t *lsink = g_sink + 2 * kSinkHalf + 16 * lane;
-  using LY = Lay<L, C>;
-  constexpr int P = LY::P, K = LY::K;
   if constexpr (MODE == M_SPLIT) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
-      const int c = LY::chunk(li, j);
+      const int c = chunk_of<L>(li, j);
       st_u128((FAST || c < a.nchunk) ? o.p0 + 16 * c : lsink, o.w[j], c_al);
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k) st_u32(o.p1 + 4 * ((li + L * k) & 31), o.ry[k], a_al);
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int c = P * (li + L * k);  // first chunk of the unit
+    for (int j = 0; j < C; ++j) {
+      const int c = chunk_of<L>(li, j);
       const bool in = FAST || c < a.nchunk;
-      if constexpr (P == 2)
-        st_u64(in ? o.p0 + 4 * c : lsink, make_uint2(o.w[k].x, o.w[k].y), c_al);
-      else
-        st_u32(in ? o.p0 + 4 * c : lsink, o.w[k].x, c_al);
-      st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[k]);  // every lane of the group
+      st_u32(in ? o.p0 + 4 * c : lsink, o.w[j].x, c_al);
+      st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[j]);  // every lane of the group
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int c = P * (li + L * k);  // first chunk of the unit
+    for (int j = 0; j < C; ++j) {
+      const int c = chunk_of<L>(li, j);
       const bool in = FAST || c < a.nchunk;
-      if constexpr (P == 2)
-        st_u128(in ? o.p0 + 8 * c : lsink, o.w[k], c_al);
-      else
-        st_u64(in ? o.p0 + 8 * c : lsink, make_uint2(o.w[k].x, o.w[k].y), c_al);
+      st_u64(in ? o.p0 + 8 * c : lsink, make_uint2(o.w[j].x, o.w[j].y), c_al);
       // every lane of the group writes the group's scale
       if constexpr (MODE == M_FP8_E8M0)
-        st_u8(in ? o.p0 + a.nseg + 128 + (c >> 3) : lsink + 8, o.sb[k]);
+        st_u8(in ? o.p0 + a.nseg + 128 + (c >> 3) : lsink + 8, o.sb[j]);
       else
-        st_u16(in ? o.p0 + a.nseg + 128 + 2 * (c >> 3) : lsink + 8, o.sb[k], c_al);
+        st_u16(in ? o.p0 + a.nseg + 128 + 2 * (c >> 3) : lsink + 8, o.sb[j], c_al);
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k)
@@ -787,7 +741,7 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   extern __shared__ float4 g_lds[];
   if constexpr (NORM) {
     for (int i = threadIdx.x; i < L * C; i += 256) {
-      const int c = Lay<L, C>::chunk(i % L, i / L);
+      const int c = chunk_of<L>(i % L, i / L);
       float g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (c < a.nchunk) unpack8(ld16_cached(a.gamma + 8 * c), g);
       g_lds[i] = make_float4(g[0], g[1], g[2], g[3]);
