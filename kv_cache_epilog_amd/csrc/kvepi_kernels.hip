@@ -156,6 +156,34 @@ __device__ __forceinline__ float rcp_rn(float b) {
   return __builtin_fmaf(e, y0, y0);
 }
 
+// sqrt(x) correctly rounded for x in [2^-96, 2^127]: the hardware square
+// root, within one ulp there, corrected by the signs of the residuals of its
+// two neighbours (checked against the library square root on the GPU for
+// every fp32 value of that range).
+__device__ __forceinline__ float sqrt_rn(float x) {
+  const float s = __builtin_amdgcn_sqrtf(x);
+  const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+  const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+  const float rm = __builtin_fmaf(-sm, s, x);
+  const float rp = __builtin_fmaf(-sp, s, x);
+  const float r = rm <= 0.0f ? sm : s;
+  return rp > 0.0f ? sp : r;
+}
+
+// max(|a|, |b|, |c|) in one instruction (the compiler's fmaxf chain adds
+// canonicalisations for inputs it cannot prove to be canonical).
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float amax8(const float (&v)[8]) {
+  float m = max3_abs(v[0], v[1], v[2]);
+  m = max3_abs(m, v[3], v[4]);
+  m = max3_abs(m, v[5], v[6]);
+  return max3_abs(m, v[7], v[7]);
+}
+
 // E4M3FN code of q: round to nearest even, |q| > 448 saturates to 448,
 // sign kept (also for zero); a NaN gives 0x7F.
 __device__ __forceinline__ uint32_t enc_e4m3_sw(float q) {
@@ -419,7 +447,11 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
     const float ss = part[0];
     const float mean = a.inv_nseg != 0.0f ? ss * a.inv_nseg : ss / a.nseg_f;
-    const float rms = __builtin_sqrtf(mean + a.eps);
+    const float xs = mean + a.eps;
+    // (a wave-uniform choice, so only one of the two square roots runs)
+    const float rms = __builtin_amdgcn_ballot_w64(!(xs >= 0x1p-96f && xs <= 0x1p+127f)) == 0
+                          ? sqrt_rn(xs)
+                          : __builtin_sqrtf(xs);
     // The fast division needs a normal rms with a normal reciprocal, every
     // quotient normal (|x| >= 2^(e(rms) - 252) guarantees it) and an exact
     // FMA residual (|x| >= 2^-100).  Rows holding a smaller magnitude --
@@ -498,9 +530,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int j = 0; j < C; ++j) {
       float v[8];
       unpack8(yw[j], v);
-      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
-#pragma unroll
-      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
+      float m = amax8(v);
       m = grp_max<4>(m);  // 32 values = 4 lanes
       const int E = e8m0_exp<2, 0x400000u>(m);  // FP4 max 6 = 1.5 * 2^2
       uint32_t w = 0;
@@ -523,9 +553,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int j = 0; j < C; ++j) {
       float v[8];
       unpack8(yw[j], v);
-      float m = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
-#pragma unroll
-      for (int q = 2; q < 8; ++q) m = __builtin_fmaxf(m, __builtin_fabsf(v[q]));
+      float m = amax8(v);
       m = grp_max<8>(m);  // 64 values = 8 lanes
       uint32_t cw[2];
       uint32_t sbits;
