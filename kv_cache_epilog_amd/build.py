@@ -39,5 +39,26 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+HW_CHECK_SRC = os.path.join(ROOT, "tests", "hw_check.hip")
+HW_CHECK_BIN = os.path.join(ROOT, "tests", "hw_check")
+
+
+def build_hw_check(verbose: bool = False) -> str:
+    """Builds tests/hw_check, the GPU check of the hardware instructions the
+    kernels rely on (run by a GPU test; a separate program, not linked into
+    the library)."""
+    tmp = HW_CHECK_BIN + ".tmp"
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared", "-fvisibility=hidden")]
+    cmd = [hipcc(), *flags, "-I", CSRC, "-o", tmp, HW_CHECK_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}")
+    os.replace(tmp, HW_CHECK_BIN)
+    return HW_CHECK_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_hw_check(verbose=True))

@@ -1,0 +1,106 @@
+// hw_check.hip -- GPU check of the gfx950 instructions the epilog's fast paths
+// rely on, against IEEE arithmetic or the kernel's own software encoders
+// (kvepi_arith.h), over every input the kernels can give them:
+//   rcp     rcp_rn(b) == 1/b for every fp32 significand, exponents [-100, 100]
+//   sqrt    sqrt_rn(x) == sqrtf(x) for every fp32 x in [2^-96, 2^127]
+//   fp8     v_cvt_pk_fp8_f32(q) == E4M3 encoder, every fp32 |q| <= 448
+//   fp8s    v_cvt_scalef32_pk_fp8_f32(v, 2^E) == E4M3 encoder of v / 2^E, every
+//           bf16 v with |v / 2^E| <= 448, E in [-100, 100]
+//   fp4s    v_cvt_scalef32_pk_fp4_f32(v, 2^E) == E2M1 encoder of v / 2^E, every
+//           bf16 v with |v / 2^E| <= 6, E in [-100, 100]
+// Prints one line per check and exits with status 1 if anything differs.
+// Every launch covers at most 2^28 indices and each thread checks its index
+// against the count; results go to a 64-word counter buffer.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "kvepi_arith.h"
+
+using namespace kvepi;
+
+__global__ void k_rcp(uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t mant = i & 0x7FFFFFu;
+  const int e = (int)(i >> 23) - 100;  // exponent in [-100, 100]
+  const float b = __uint_as_float((uint32_t)(e + 127) << 23 | mant);
+  if (rcp_rn(b) != 1.0f / b) atomicAdd(bad, 1u);
+}
+
+__global__ void k_sqrt(uint32_t base, uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float x = __uint_as_float(base + i);
+  if (sqrt_rn(x) != __builtin_sqrtf(x)) atomicAdd(bad, 1u);
+}
+
+__global__ void k_fp8(uint32_t base, uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float q = __uint_as_float(base + i);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, -q, 0, false);
+  if ((w & 0xFFu) != enc_e4m3_sw(q) || ((w >> 8) & 0xFFu) != enc_e4m3_sw(-q)) atomicAdd(bad, 1u);
+}
+
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+
+// index = (E + 100) * 65536 + bf16 bits
+__global__ void k_scaled(uint32_t n, int fp4, unsigned *bad, unsigned *count) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int E = (int)(i >> 16) - 100;
+  const float v = __uint_as_float((i & 0xFFFFu) << 16);
+  const float f = exp2_neg(E);
+  const float q = v * f;  // exact: a power-of-two scaling of a bf16 value
+  const float lim = fp4 ? 6.0f : 448.0f;
+  if (!(__builtin_fabsf(q) <= lim)) return;  // also skips NaN
+  const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
+  uint32_t got, want;
+  if (fp4) {
+    got = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, -v, sc, 0) & 0xFFu;
+    want = enc_e2m1_sw(q) | (enc_e2m1_sw(-q) << 4);
+  } else {
+    s16x2_t w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v, -v, sc, false);
+    got = (uint32_t)(uint16_t)w[0];
+    want = enc_e4m3_sw(q) | (enc_e4m3_sw(-q) << 8);
+  }
+  atomicAdd(count, 1u);
+  if (got != want) atomicAdd(bad, 1u);
+}
+
+static void launch_range(void (*fn)(uint32_t, uint32_t, unsigned *), uint64_t lo, uint64_t hi,
+                         unsigned *bad) {
+  for (uint64_t b = lo; b <= hi; b += (1ull << 28)) {
+    const uint32_t n = (uint32_t)((hi + 1 - b) < (1ull << 28) ? (hi + 1 - b) : (1ull << 28));
+    hipLaunchKernelGGL(fn, dim3((n + 255) / 256), dim3(256), 0, 0, (uint32_t)b, n, bad);
+  }
+}
+
+int main() {
+  unsigned *d = nullptr;
+  if (hipMalloc(&d, 64 * sizeof(unsigned)) != hipSuccess) return 2;
+  (void)hipMemset(d, 0, 64 * sizeof(unsigned));
+  const uint32_t n_rcp = 201u << 23;
+  hipLaunchKernelGGL(k_rcp, dim3((n_rcp + 255) / 256), dim3(256), 0, 0, n_rcp, d + 0);
+  launch_range(k_sqrt, 0x0F800000u, 0x7F000000u, d + 1);      // [2^-96, 2^127]
+  launch_range(k_fp8, 0x00000000u, 0x43E00000u, d + 2);       // [0, 448]
+  const uint32_t n_sc = 201u << 16;
+  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 0, d + 3, d + 4);
+  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 1, d + 5, d + 6);
+  const hipError_t e = hipDeviceSynchronize();
+  unsigned h[7] = {0};
+  (void)hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
+  (void)hipFree(d);
+  if (e != hipSuccess) {
+    printf("hip error %d\n", (int)e);
+    return 2;
+  }
+  printf("rcp: %u mismatches of %u\n", h[0], n_rcp);
+  printf("sqrt: %u mismatches of %u\n", h[1], 0x7F000000u - 0x0F800000u + 1u);
+  printf("fp8: %u mismatches of %u\n", h[2], 0x43E00000u + 1u);
+  printf("fp8s: %u mismatches of %u\n", h[3], h[4]);
+  printf("fp4s: %u mismatches of %u\n", h[5], h[6]);
+  return (h[0] | h[1] | h[2] | h[3] | h[5]) ? 1 : 0;
+}
