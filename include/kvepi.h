@@ -170,7 +170,11 @@ KVEPI_API kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, in
  * The current HIP device must be the one holding the buffers.  Returns
  * KVEPI_ERR_WORKSPACE if workspace_bytes is below the stage-one size and
  * KVEPI_ERR_RUNTIME if the launch is refused (for example on a device that
- * is not gfx950). */
+ * is not gfx950).
+ * The launch uses one persistent workgroup per resident slot of the device.
+ * The environment variable KVEPI_MAX_WAVES (a multiple of 4, read at every
+ * call) caps the number of wavefronts; it exists for tests of the kernel's
+ * multi-iteration paths and never changes the result. */
 KVEPI_API kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
                        int64_t x_row_stride, const void *gamma,
                        const void *cos, const void *sin,

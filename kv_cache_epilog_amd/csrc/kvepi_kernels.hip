@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdlib.h>
+
 #include <mutex>
 
 #include "kvepi_arith.h"
@@ -1007,7 +1009,13 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
 
   // persistent waves: exactly as many blocks as the CUs hold at once
   const int cus = device_cus();
-  const int64_t max_waves = (int64_t)cus * blocks_per_cu(fn, lds) * 4;
+  int64_t max_waves = (int64_t)cus * blocks_per_cu(fn, lds) * 4;
+  // KVEPI_MAX_WAVES (a multiple of 4, read at every launch) caps the grid:
+  // tests use it to run many iterations per wave on small inputs
+  if (const char *cap = getenv("KVEPI_MAX_WAVES")) {
+    const long v = strtol(cap, nullptr, 10);
+    if (v >= 4 && v < max_waves) max_waves = v & ~3L;
+  }
   const int64_t waves = n_groups < max_waves ? n_groups : max_waves;
   const int64_t blocks = (waves + 3) / 4;
   a.nwaves = (int32_t)(blocks * 4);

@@ -219,3 +219,26 @@ def test_scale_exponent_sweep(mode):
     w = _small(mode, T, d, seed=21, skip=0.0, x=xb)
     n = check(w)
     assert n == 0
+
+
+@pytest.mark.parametrize("waves", [4, 8, 64])
+@pytest.mark.parametrize("case", ["fused576", "mode1_576", "mxfp4_128", "split576", "mode0_2112",
+                                  "mode0_256"])
+def test_many_iterations_per_wave(case, waves, monkeypatch):
+    # a capped grid makes each wave run hundreds of iterations: slot windows
+    # are reloaded many times and the pipeline runs through its steady state
+    monkeypatch.setenv("KVEPI_MAX_WAVES", str(waves))
+    T = 3001
+    if case == "fused576":
+        w = _small(0, T, 576, seed=31, bs=64, stride_extra=96, norm=True, rope=True)
+    elif case == "mode1_576":
+        w = _small(1, T, 576, seed=32, bs=17, row_sigma=2.0)
+    elif case == "mxfp4_128":
+        w = _small(3, T, 128, seed=33, bs=128, row_sigma=1.0)
+    elif case == "split576":
+        w = _small(4, T, 576, seed=34, bs=5, norm=True, rope=True)
+    elif case == "mode0_2112":
+        w = _small(0, 600, 2112, seed=35, bs=9, norm=True, rope=True)
+    else:
+        w = _small(0, T, 256, seed=36, bs=16)
+    check(w)
