@@ -815,40 +815,41 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       store(t);
     }
   } else {
-    // Software pipeline, two iterations ahead, with two register sets (A
-    // holds the even iterations, B the odd ones).  gfx9 has a single in-order
+    // Software pipeline, D iterations ahead, with D register sets (set d
+    // holds the iterations j with j % D == d).  gfx9 has a single in-order
     // counter for vector loads and stores, so a wait for a load also waits
-    // for every store issued before it.  Each half-iteration j therefore
-    // computes iteration j (loaded two half-iterations earlier), then issues
-    // the loads of iteration j + 2 and only then the stores of iteration j;
-    // the wait before computing j + 2 then leaves the stores of j and j + 1
-    // in flight.  Every half-iteration issues the same memory operations
+    // for every store issued before it.  Each step j therefore computes
+    // iteration j (loaded D steps earlier), then issues the loads of
+    // iteration j + D and only then the stores of iteration j; the wait
+    // before computing j + 1 then leaves the stores of the last D - 1
+    // iterations in flight.  Every step issues the same memory operations
     // (skipped tokens re-read a live row of their iteration and store to a
-    // sink), so the compiler's wait counts are exact.
-    RowBuf<MODE, ROPE, L, C> bA, bB;
-    // The first two iterations load every lane's own row before the slots
-    // are known (a skipped token's row is read for nothing), so that the
-    // row loads do not wait for the slot window: short launches are bound by
+    // sink), so the compiler's wait counts are exact.  (Three or four sets
+    // measured slower or no faster: registers are the scarcer resource.)
+    constexpr int D = 2;
+    RowBuf<MODE, ROPE, L, C> buf[D];
+    IterInfo<R> t[D];
+    // The first D iterations load every lane's own row before the slots are
+    // known (a skipped token's row is read for nothing), so that the row
+    // loads do not wait for the slot window: short launches are bound by
     // this chain of memory latencies.
-    issue_own(0, bA);
-    issue_own(1, bB);
-    IterInfo<R> tA = prep(0, window(0));
-    IterInfo<R> tB = prep(1, window(1));
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_own(d, buf[d]);
+#pragma unroll
+    for (int d = 0; d < D; ++d) t[d] = prep(d, window(d));
     // drain once before the loop: otherwise the loop's waits are sized for
     // the first trip, whose loads were issued in an order of the compiler's
     // choosing
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    for (int it = 0; it < n_it; it += 2) {
-      compute(tA, bA);
-      const IterInfo<R> nA = prep(it + 2, window(it + 2));
-      issue(nA, bA);
-      store(tA);
-      tA = nA;
-      compute(tB, bB);
-      const IterInfo<R> nB = prep(it + 3, window(it + 3));
-      issue(nB, bB);
-      store(tB);
-      tB = nB;
+    for (int it = 0; it < n_it; it += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        compute(t[d], buf[d]);
+        const IterInfo<R> nt = prep(it + d + D, window(it + d + D));
+        issue(nt, buf[d]);
+        store(t[d]);
+        t[d] = nt;
+      }
     }
   }
 }
