@@ -24,6 +24,8 @@ MODE_FP8_BF16SCALE = 0
 MODE_FP8_E8M0 = 1
 MODE_MXFP4 = 3
 MODE_BF16_SPLIT = 4
+MODE_MXFP8 = 5
+MODE_FP8_ROW = 6
 
 PREFILL = 0xAB
 
@@ -140,7 +142,7 @@ def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
          group_size: Optional[int] = None, x: Optional[np.ndarray] = None) -> Workload:
     rng = np.random.default_rng(seed)
     if group_size is None:
-        group_size = 32 if mode == MODE_MXFP4 else 64
+        group_size = {MODE_MXFP4: 32, MODE_MXFP8: 32, MODE_FP8_ROW: 0}.get(mode, 64)
     if x is None:
         x = normal_rows(rng, T, d, row_sigma, outlier_frac)
     gamma = cos = sin = None

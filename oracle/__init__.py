@@ -25,6 +25,8 @@ MODE_FP8_BF16SCALE = 0
 MODE_FP8_E8M0 = 1
 MODE_MXFP4 = 3
 MODE_BF16_SPLIT = 4
+MODE_MXFP8 = 5
+MODE_FP8_ROW = 6
 
 _lib = None
 
@@ -160,11 +162,15 @@ def quant_row(mode: int, v_bf16, group_size: int):
     v = _c(v_bf16, np.uint16)
     _, kc, sc = row_bytes(mode, v.size, group_size)
     out = np.empty(kc, np.uint8)
-    sout = np.empty(sc, np.uint8)
+    sout = np.empty(4 * sc, np.uint8)
     rc = lib().kvo_quant_row(mode, _ptr(v), v.size, group_size, _ptr(out), _ptr(sout))
     if rc != 0:
         raise ValueError("quant_row rejected its arguments")
-    return (out, sout) if mode == MODE_MXFP4 else (out, None)
+    if mode in (MODE_MXFP4, MODE_MXFP8):
+        return out, sout[:sc]
+    if mode == MODE_FP8_ROW:
+        return out, sout[:4].view(np.float32)  # the fp32 scale
+    return out, None
 
 
 # ---- whole epilog ---------------------------------------------------------

@@ -247,6 +247,17 @@ int kvo_row_bytes(int mode, int64_t d, int32_t group_size, int64_t *concat_col,
     cc = (d + 1) / 2;
     kc = cc;
     sc = (d + 31) / 32;
+  } else if (mode == KVO_MODE_MXFP8) {
+    if (group_size != 32 || d % 32 != 0 || d < 32 || d > 8192) return -1;
+    cc = d;
+    kc = d;
+    sc = (d + 31) / 32;
+  } else if (mode == KVO_MODE_FP8_ROW) {
+    /* the whole row is one group: group_size 0 (or d) */
+    if ((group_size != 0 && group_size != d) || d % 32 != 0 || d < 32 || d > 8192) return -1;
+    cc = d;
+    kc = d;
+    sc = 1; /* one FLOAT per row */
   } else if (mode == KVO_MODE_BF16_SPLIT) {
     if (d % 64 != 0 || d <= 64 || d > 8192) return -1;
     cc = d - 64; /* ckv elements per row */
@@ -334,6 +345,36 @@ int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
     }
     return 0;
   }
+  if (mode == KVO_MODE_MXFP8) {
+    /* "indexer_quant_cache" mxfp8: groups of 32, e8m0 scale, E4M3 codes */
+    for (int64_t g = 0; g < sc; ++g) {
+      int64_t i0 = g * 32, i1 = i0 + 32 < d ? i0 + 32 : d;
+      float amax = 0.0f;
+      for (int64_t i = i0; i < i1; ++i) {
+        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        if (a > amax) amax = a;
+      }
+      int E = kvo_e8m0_exponent(amax, 448.0f);
+      scale_out[g] = (uint8_t)(E + 127);
+      float s_use = ldexpf(1.0f, E);
+      for (int64_t i = i0; i < i1; ++i) out[i] = kvo_enc_e4m3(kvo_bf16_to_f32(v[i]) / s_use);
+    }
+    return 0;
+  }
+  if (mode == KVO_MODE_FP8_ROW) {
+    /* "indexer_quant_cache" fp8: the whole row one group; the scale
+     * max|x| / 448 is kept as FLOAT and the codes divide by it */
+    float amax = 0.0f;
+    for (int64_t i = 0; i < d; ++i) {
+      float a = fabsf(kvo_bf16_to_f32(v[i]));
+      if (a > amax) amax = a;
+    }
+    float s = amax / 448.0f;
+    memcpy(scale_out, &s, 4); /* little-endian fp32 */
+    for (int64_t i = 0; i < d; ++i)
+      out[i] = s == 0.0f ? 0x00 : kvo_enc_e4m3(kvo_bf16_to_f32(v[i]) / s);
+    return 0;
+  }
   return -1;
 }
 
@@ -355,10 +396,11 @@ int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
   int64_t cc, kc, sc;
   if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
   if ((cos == NULL) != (sin == NULL)) return -1;
-  if (mode == KVO_MODE_MXFP4 && (gamma || cos)) return -1;
+  const int indexer = mode == KVO_MODE_MXFP4 || mode == KVO_MODE_MXFP8 ||
+                      mode == KVO_MODE_FP8_ROW;
+  if (indexer && (gamma || cos)) return -1;
   if (mode == KVO_MODE_BF16_SPLIT && (!gamma || !cos)) return -1;
-  if ((mode == KVO_MODE_MXFP4 || mode == KVO_MODE_BF16_SPLIT) && !aux)
-    return -1;
+  if ((indexer || mode == KVO_MODE_BF16_SPLIT) && !aux) return -1;
   int64_t num_slots = cache->block_num * cache->block_size;
   int64_t nope = d - 64;
   uint16_t *v = (uint16_t *)malloc((size_t)d * sizeof(uint16_t));
@@ -368,10 +410,13 @@ int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
     int64_t s = slot_mapping[t];
     if (s < 0 || s >= num_slots) continue; /* -1: token skipped */
     const uint16_t *xr = x + t * x_row_stride;
-    if (mode == KVO_MODE_MXFP4) {
+    if (indexer) {
       kvo_quant_row(mode, xr, d, group_size, row, srow);
       memcpy(row_ptr(cache, s, 1), row, (size_t)kc);
-      memcpy(row_ptr(aux, s, 1), srow, (size_t)sc);
+      if (mode == KVO_MODE_FP8_ROW)
+        memcpy(row_ptr(aux, s, 4), srow, 4);
+      else
+        memcpy(row_ptr(aux, s, 1), srow, (size_t)sc);
       continue;
     }
     if (gamma)

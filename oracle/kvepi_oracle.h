@@ -19,7 +19,9 @@
  *  - "aclnnKvRmsNormRopeCache", 计算公式 (1) interleaveRope and (2) rmsNorm.
  *  - "indexer_quant_cache", 接口功能 / 约束: MX-FP4 groups of 32 with an e8m0
  *    scale written to a separate cache_scale tensor; rows not hit keep their
- *    values.
+ *    values.  The same page's mxfp8 mode (E4M3 codes, groups of 32, e8m0
+ *    scale) and fp8 mode (E4M3 codes, the whole row one group, one FLOAT
+ *    scale per row in cache_scale).
  *
  * Arithmetic: IEEE fp32 (the precision the quantiser's division is defined
  * in), evaluated in the order written, compiled with -ffp-contract=off.  The
@@ -42,6 +44,8 @@ extern "C" {
 #define KVO_MODE_FP8_E8M0 1      /* group-64 E4M3 codes, e8m0 scale        */
 #define KVO_MODE_MXFP4 3         /* group-32 E2M1 nibbles, e8m0 scale row  */
 #define KVO_MODE_BF16_SPLIT 4    /* RMSNorm -> ckv cache, RoPE -> k cache  */
+#define KVO_MODE_MXFP8 5         /* group-32 E4M3 codes, e8m0 scale row    */
+#define KVO_MODE_FP8_ROW 6       /* whole-row E4M3 codes, fp32 scale       */
 
 /* ---- number formats ---------------------------------------------------- */
 float kvo_bf16_to_f32(uint16_t h);
@@ -73,8 +77,9 @@ int kvo_row_bytes(int mode, int64_t d, int32_t group_size, int64_t *concat_col,
 
 /* Quantise one prepared row v[0..d) (bf16 bits: nope segment already
  * normalised if RMSNorm is on, rope segment already rotated if RoPE is on)
- * into out[0..kv_cache_col) (modes 0/1) or out[0..d/2) plus
- * scale_out[0..d/32) (MX-FP4). */
+ * into out[0..kv_cache_col) (modes 0/1), out[0..d/2) plus scale_out[0..d/32)
+ * (MX-FP4), out[0..d) plus scale_out[0..d/32) (MX-FP8) or out[0..d) plus
+ * the 4 little-endian bytes of the fp32 scale in scale_out (FP8 row). */
 int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
                   uint8_t *out, uint8_t *scale_out);
 
@@ -87,8 +92,9 @@ typedef struct {
 } kvo_cache;
 
 /* Runs the epilog for tokens t = 0..T-1 in order.  gamma (length d-64) and
- * cos/sin ([T,64]) may be NULL.  aux is the cache_scale tensor (MX-FP4) or
- * the k cache (BF16 split).  Returns 0, or -1 on an argument it rejects. */
+ * cos/sin ([T,64]) may be NULL.  aux is the cache_scale tensor (MX-FP4,
+ * MX-FP8: bytes; FP8 row: fp32 elements) or the k cache (BF16 split).
+ * Returns 0, or -1 on an argument it rejects. */
 int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
                int64_t x_row_stride, const uint16_t *gamma,
                const uint16_t *cos, const uint16_t *sin, float eps,

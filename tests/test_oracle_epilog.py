@@ -31,8 +31,11 @@ def run_oracle(w):
 def expected_rows(w, t):
     """Row bytes for token t from the per-row steps."""
     x = w.x[t]
-    if w.mode == kvgen.MODE_MXFP4:
+    if w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_MXFP8):
         return oracle.quant_row(w.mode, x, w.group_size)
+    if w.mode == kvgen.MODE_FP8_ROW:
+        out, s = oracle.quant_row(w.mode, x, w.group_size)
+        return out, s.view(np.uint8)
     nope = w.d - 64
     v = x.copy()
     if w.gamma is not None:
