@@ -83,12 +83,23 @@ typedef enum kvepi_status {
  *  4  bf16 split: RMSNorm output -> cache (ckv, headDim >= d-64 bf16),
  *     RoPE output -> cache_aux (k, headDim >= 64 bf16)
  *     ("aclnnKvRmsNormRopeCache", 接口功能).
+ *  5  MX-FP8: E4M3 codes of the whole row, one byte each, one e8m0 scale
+ *     (amax <= 448 * 2^E) per group of 32 written to cache_aux (uint8)
+ *     ("indexer_quant_cache", mxfp8 mode).
+ *  6  FP8 per row: the whole row is one group; E4M3 codes of x / s with
+ *     s = amax / 448 in fp32 (a zero row: s = 0, all codes 0), s written as
+ *     one little-endian fp32 value to cache_aux, whose elements are 4-byte
+ *     floats ("indexer_quant_cache", fp8 mode: cache_scale is FLOAT).
+ * Modes 3, 5 and 6 are the indexer modes: they take neither gamma nor
+ * cos/sin and need cache_aux.
  */
 #define KVEPI_MODE_FP8_BF16SCALE 0
 #define KVEPI_MODE_FP8_E8M0 1
 #define KVEPI_MODE_HIF8_FP4 2
 #define KVEPI_MODE_MXFP4 3
 #define KVEPI_MODE_BF16_SPLIT 4
+#define KVEPI_MODE_MXFP8 5
+#define KVEPI_MODE_FP8_ROW 6
 
 /* A paged cache [block_num, block_size, 1, head_dim] ("aclnnKvCompressEpilog",
  * 约束说明: four dimensions, dimension -2 fixed at 1, only the block
@@ -96,7 +107,8 @@ typedef enum kvepi_status {
  * laid out loosely but are contiguous inside).
  *  data          DEVICE pointer to element [0,0,0,0]; any byte alignment.
  *  head_dim      elements per row (uint8 caches: bytes; bf16 caches for mode
- *                4: 2-byte elements).
+ *                4: 2-byte elements; the mode-6 scale cache: 4-byte floats).
+ *                data must be aligned to the element size.
  *  block_stride  elements between consecutive blocks, >= block_size*head_dim.
  * Slot s lives at data + ((s / block_size) * block_stride +
  * (s % block_size) * head_dim) * element_size.  num_slots = block_num *
@@ -114,16 +126,17 @@ typedef struct kvepi_cache {
  * for mode 0 and 1 for mode 1; kvCacheCol = concatCol for mode 1 and
  * concatCol rounded up to 32 bytes for mode 0; e.g. d=256 in mode 1 gives
  * 323.  "indexer_quant_cache", 约束: MX-FP4 codes take ceil(d/2) bytes and
- * scaleCol = ceil(d/32), e.g. d=128 gives 4.)
+ * scaleCol = ceil(d/32), e.g. d=128 gives 4; MX-FP8 codes take d bytes with
+ * the same scaleCol; the per-row FP8 mode takes d bytes and scaleCol = 1.)
  *   concat_col    bytes of data per row (mode 4: ckv elements per row)
  *   kv_cache_col  bytes written per row, the minimum headDim (mode 4: d-64)
- *   scale_col     scale entries per row (mode 3: the minimum cache_aux
- *                 headDim; mode 4: 64, the k-cache elements per row)
+ *   scale_col     scale entries per row (modes 3, 5, 6: the minimum
+ *                 cache_aux headDim; mode 4: 64, the k-cache elements per row)
  * Any out-pointer may be NULL.  Errors: KVEPI_ERR_UNSUPPORTED for an unknown
  * mode or mode 2, KVEPI_ERR_SHAPE for d outside the mode's range
- * (modes 0/1/4: d % 64 == 0 and 64 < d <= 8192; mode 3: d % 32 == 0 and
- * 32 <= d <= 8192), KVEPI_ERR_PARAM for a group size other than 64 (modes
- * 0/1) or 32 (mode 3). */
+ * (modes 0/1/4: d % 64 == 0 and 64 < d <= 8192; modes 3/5/6: d % 32 == 0
+ * and 32 <= d <= 8192), KVEPI_ERR_PARAM for a group size other than 64
+ * (modes 0/1), 32 (modes 3/5) or 0 or d (mode 6). */
 KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t group_size,
                              int64_t *concat_col, int64_t *kv_cache_col,
                              int64_t *scale_col);
@@ -137,10 +150,11 @@ KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t gr
  *                tensor are flattened into num_tokens
  *                ("aclnnKvCompressEpilog", 约束说明, slotMapping shape rule).
  *  gamma         DEVICE, bf16 [d-64], 16-byte aligned, or NULL for no
- *                RMSNorm (required in mode 4, rejected in mode 3).
+ *                RMSNorm (required in mode 4, rejected in modes 3, 5, 6).
  *  cos, sin      DEVICE, bf16 [num_tokens, 64] contiguous, 16-byte aligned,
  *                both or neither; NULL for no RoPE (the rope columns are then
- *                copied unchanged).  Required in mode 4, rejected in mode 3.
+ *                copied unchanged).  Required in mode 4, rejected in modes
+ *                3, 5, 6.
  *  slot_mapping  DEVICE, int32 [num_tokens], 4-byte aligned.  -1 skips the
  *                token; any value outside [0, num_slots) is skipped too.
  *                Valid values must be distinct; with duplicates the result of
@@ -148,11 +162,13 @@ KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t gr
  *                约束说明).
  *  cache         HOST struct describing the main cache (uint8; bf16 in mode
  *                4).  headDim >= kv_cache_col.
- *  cache_aux     HOST struct, NULL except in mode 3 (cache_scale, uint8,
- *                headDim >= scale_col) and mode 4 (k cache, bf16,
- *                headDim >= 64); same block_num and block_size as cache.
+ *  cache_aux     HOST struct, NULL except in modes 3 and 5 (cache_scale,
+ *                uint8, headDim >= scale_col), mode 6 (cache_scale, fp32,
+ *                headDim >= 1) and mode 4 (k cache, bf16, headDim >= 64);
+ *                same block_num and block_size as cache.
  *  quant_mode    KVEPI_MODE_*.
- *  group_size    64 (modes 0, 1), 32 (mode 3), ignored in mode 4.
+ *  group_size    64 (modes 0, 1), 32 (modes 3, 5), 0 or d (mode 6),
+ *                ignored in mode 4.
  *  eps           RMSNorm epsilon, finite and >= 0 (used only with gamma).
  *  workspace_bytes  HOST out-parameter.
  * num_tokens == 0 is valid and makes kvepi_run a no-op. */

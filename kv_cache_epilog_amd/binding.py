@@ -26,6 +26,8 @@ KVEPI_MODE_FP8_E8M0 = 1
 KVEPI_MODE_HIF8_FP4 = 2
 KVEPI_MODE_MXFP4 = 3
 KVEPI_MODE_BF16_SPLIT = 4
+KVEPI_MODE_MXFP8 = 5
+KVEPI_MODE_FP8_ROW = 6
 
 
 class KvepiError(RuntimeError):

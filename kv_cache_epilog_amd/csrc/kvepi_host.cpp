@@ -46,6 +46,21 @@ kvepi_status row_geometry(int32_t mode, int64_t d, int32_t group_size,
       *kc = *cc;
       *sc = (d + 31) / 32;
       return KVEPI_OK;
+    case KVEPI_MODE_MXFP8:
+      if (d % 32 != 0 || d < 32 || d > 8192) return KVEPI_ERR_SHAPE;
+      if (group_size != 32) return KVEPI_ERR_PARAM;
+      *cc = d;
+      *kc = d;
+      *sc = d / 32;
+      return KVEPI_OK;
+    case KVEPI_MODE_FP8_ROW:
+      // the whole row is one group: group_size 0 or d
+      if (d % 32 != 0 || d < 32 || d > 8192) return KVEPI_ERR_SHAPE;
+      if (group_size != 0 && group_size != d) return KVEPI_ERR_PARAM;
+      *cc = d;
+      *kc = d;
+      *sc = 1;
+      return KVEPI_OK;
     case KVEPI_MODE_BF16_SPLIT:
       if (d % 64 != 0 || d <= 64 || d > 8192) return KVEPI_ERR_SHAPE;
       *cc = d - 64;
@@ -70,7 +85,7 @@ kvepi_status check_cache(const kvepi_cache *c, int64_t elem, int64_t min_cols,
   if (c->head_dim > (INT64_C(1) << 40) / c->block_size) return KVEPI_ERR_SHAPE;
   if (c->block_stride < c->block_size * c->head_dim) return KVEPI_ERR_LAYOUT;
   if (c->block_stride > (INT64_C(1) << 46) / c->block_num) return KVEPI_ERR_SHAPE;
-  if (elem == 2 && !aligned(c->data, 2)) return KVEPI_ERR_LAYOUT;
+  if (!aligned(c->data, (uintptr_t)elem)) return KVEPI_ERR_LAYOUT;
   *pitch = c->head_dim * elem;
   *bstride = c->block_stride * elem;
   *align = min_align(pow2_align(reinterpret_cast<uintptr_t>(c->data)),
@@ -106,8 +121,9 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
   const bool has_norm = gamma != nullptr;
   const bool has_rope = cos != nullptr || sin != nullptr;
   if (has_rope && (cos == nullptr || sin == nullptr)) return KVEPI_ERR_PARAM;
-  if (quant_mode == KVEPI_MODE_MXFP4 && (has_norm || has_rope))
-    return KVEPI_ERR_UNSUPPORTED;
+  const bool indexer = quant_mode == KVEPI_MODE_MXFP4 || quant_mode == KVEPI_MODE_MXFP8 ||
+                       quant_mode == KVEPI_MODE_FP8_ROW;
+  if (indexer && (has_norm || has_rope)) return KVEPI_ERR_UNSUPPORTED;
   if (quant_mode == KVEPI_MODE_BF16_SPLIT && (!has_norm || !has_rope))
     return KVEPI_ERR_PARAM;
   if (has_norm && (!isfinite(eps) || eps < 0.0f)) return KVEPI_ERR_PARAM;
@@ -115,17 +131,19 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
   if (has_rope && (!aligned(cos, 16) || !aligned(sin, 16)))
     return KVEPI_ERR_LAYOUT;
 
-  const bool needs_aux =
-      quant_mode == KVEPI_MODE_MXFP4 || quant_mode == KVEPI_MODE_BF16_SPLIT;
+  const bool needs_aux = indexer || quant_mode == KVEPI_MODE_BF16_SPLIT;
   if (needs_aux && cache_aux == nullptr) return KVEPI_ERR_NULLPTR;
   if (!needs_aux && cache_aux != nullptr) return KVEPI_ERR_PARAM;
 
+  // element sizes: bf16 caches in the split mode, fp32 scales in the
+  // per-row FP8 mode, bytes otherwise
   const int64_t elem = quant_mode == KVEPI_MODE_BF16_SPLIT ? 2 : 1;
+  const int64_t aux_elem = quant_mode == KVEPI_MODE_FP8_ROW ? 4 : elem;
   kvepi_plan q{};
   st = check_cache(cache, elem, kc, &q.c_pitch, &q.c_bstride, &q.c_align);
   if (st != KVEPI_OK) return st;
   if (needs_aux) {
-    st = check_cache(cache_aux, elem, sc, &q.a_pitch, &q.a_bstride, &q.a_align);
+    st = check_cache(cache_aux, aux_elem, sc, &q.a_pitch, &q.a_bstride, &q.a_align);
     if (st != KVEPI_OK) return st;
     if (cache_aux->block_num != cache->block_num ||
         cache_aux->block_size != cache->block_size)
@@ -138,7 +156,7 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
     q.rope = has_rope;
     q.T = num_tokens;
     q.d = d;
-    q.nope = quant_mode == KVEPI_MODE_MXFP4 ? d : d - 64;
+    q.nope = indexer ? d : d - 64;
     q.x_stride = x_row_stride;
     q.x = static_cast<const uint16_t *>(x);
     q.gamma = static_cast<const uint16_t *>(gamma);

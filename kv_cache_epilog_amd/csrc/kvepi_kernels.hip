@@ -128,14 +128,20 @@ __device__ __forceinline__ float grp_sum(float v) {
   return v;
 }
 
-// Max of non-negative floats over aligned groups of G (<= 8) lanes, as
-// unsigned integers (same order for non-negative IEEE values).
+// Max of non-negative floats over aligned groups of G lanes, as unsigned
+// integers (same order for non-negative IEEE values); the lane pairings are
+// those of grp_sum.
 template <int G>
 __device__ __forceinline__ float grp_max(float f) {
   uint32_t v = __float_as_uint(f);
   if constexpr (G >= 2) v = max(v, dpp_u<0xB1>(v));
   if constexpr (G >= 4) v = max(v, dpp_u<0x4E>(v));
   if constexpr (G >= 8) v = max(v, dpp_u<0x141>(v));
+  if constexpr (G >= 16) v = max(v, dpp_u<0x140>(v));
+  if constexpr (G >= 32) v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  if constexpr (G >= 64)
+    v = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+            (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
   return __uint_as_float(v);
 }
 
@@ -238,7 +244,11 @@ __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
 // bytes per lane for lanes with nothing to store.
 constexpr int kSinkHalf = 16384;
 __device__ __attribute__((aligned(256))) uint8_t g_sink[2 * kSinkHalf + 64 * 16];
-enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4 };
+enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4, M_MXFP8 = 5, M_FP8_ROW = 6 };
+// the indexer modes quantise the whole row (no rope segment)
+constexpr bool whole_row(int m) { return m == M_MXFP4 || m == M_MXFP8 || m == M_FP8_ROW; }
+// modes writing a second cache (scales or the k rows)
+constexpr bool has_aux(int m) { return m != M_FP8_BF16 && m != M_FP8_E8M0; }
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
 // y[32h + 2p] and y[32h + 2p + 1] from the interleaved pairs 2p and 2p+1
@@ -261,7 +271,7 @@ __device__ __forceinline__ int chunk_of(int li, int j) {
 
 template <int MODE, bool ROPE, int L, int C>
 struct RowBuf {
-  static constexpr bool HAS_ROPE_SEG = MODE != M_MXFP4;
+  static constexpr bool HAS_ROPE_SEG = !whole_row(MODE);
   static constexpr int TPL = RopeShape<L>::TPL;
   uint4 xw[C];
   uint2 rx[HAS_ROPE_SEG ? TPL : 1];             // x[4p .. 4p+3] (or 2 copied values)
@@ -315,8 +325,51 @@ struct RowOut {
   uint8_t *p0, *p1;
   uint4 w[C];
   uint32_t sb[C];
-  uint32_t ry[MODE == M_MXFP4 ? 1 : RopeShape<L>::TPL];
+  uint32_t ry[whole_row(MODE) ? 1 : RopeShape<L>::TPL];
 };
+
+// E4M3 codes of v / 2^E (E the group's e8m0 exponent, -127..127) as two
+// words of four codes.
+__device__ __forceinline__ void codes_e8m0_fp8(const float (&v)[8], int E, uint32_t (&cw)[2]) {
+  if (E >= -100 && E <= 100) {
+    const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
+    s16x2_t w0 = {0, 0}, w1 = {0, 0};
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[0], v[1], sc, false);
+    w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[2], v[3], sc, true);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[4], v[5], sc, false);
+    w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[6], v[7], sc, true);
+    cw[0] = __builtin_bit_cast(uint32_t, w0);
+    cw[1] = __builtin_bit_cast(uint32_t, w1);
+  } else {
+    const float f = exp2_neg(E);
+    uint32_t q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = enc_e4m3_sw(v[t] * f);
+    cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+    cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+  }
+}
+
+// E4M3 codes of eight quotients, each in [-512, 512] or NaN (hardware
+// convert: round to nearest even, saturating at 448).
+__device__ __forceinline__ void codes_fp8(const float (&q)[8], uint32_t (&cw)[2]) {
+  int w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
+  cw[0] = (uint32_t)w0;
+  cw[1] = (uint32_t)w1;
+}
+
+// m / 448 correctly rounded for a bf16 m in [2^-71, 2^100]: fma(m, H, m*Lo)
+// with H + Lo a double-length 1/448 (tests/fastdiv_check.c compares it with
+// the IEEE quotient for every such m).
+__device__ __forceinline__ float div448_fast(float m) {
+  constexpr float H448 = 1.0f / 448.0f;
+  constexpr float L448 = (float)(1.0 / 448.0 - (double)H448);
+  return __builtin_fmaf(m, H448, m * L448);
+}
 
 template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
 __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
@@ -456,6 +509,57 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       o.w[j] = make_uint4(w, 0u, 0u, 0u);
       o.sb[j] = (uint32_t)(E + 127);
     }
+  } else if constexpr (MODE == M_MXFP8) {
+    // "indexer_quant_cache" mxfp8: e8m0 scale per group of 32, E4M3 codes
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      const float m = grp_max<4>(amax8(v));  // 32 values = 4 lanes
+      const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
+      uint32_t cw[2];
+      codes_e8m0_fp8(v, E, cw);
+      o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
+      o.sb[j] = (uint32_t)(E + 127);
+    }
+  } else if constexpr (MODE == M_FP8_ROW) {
+    // "indexer_quant_cache" fp8: the whole row is one group; its scale
+    // amax / 448 is kept in fp32 and the codes divide by it.  The fast path
+    // (amax in [2^-71, 2^100], so that the scale and its reciprocal are
+    // normal and inside the range of rcp_rn) divides with div_fast, exact
+    // for bf16 numerators wherever a code can be nonzero; elsewhere the row
+    // divides exactly (a zero row has scale 0 and all codes 0).
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      m = __builtin_fmaxf(m, amax8(v));
+    }
+    m = grp_max<L>(m);
+    const bool fastq = m >= 0x1p-71f && m <= 0x1p+100f;
+    const float s = fastq ? div448_fast(m) : m / 448.0f;
+    const float rcp = rcp_rn(s);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      uint32_t cw[2];
+      if (fastq) {
+        float q[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) q[t] = div_fast(v[t], s, rcp);
+        codes_fp8(q, cw);
+      } else {
+        uint32_t q[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) q[t] = s > 0.0f ? enc_e4m3_sw(v[t] / s) : 0u;
+        cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+      }
+      o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
+    }
+    o.sb[0] = __float_as_uint(s);
   } else {  // FP8 modes
 #pragma unroll
     for (int j = 0; j < C; ++j) {
@@ -468,23 +572,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       if constexpr (MODE == M_FP8_E8M0) {
         const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
         sbits = (uint32_t)(E + 127);
-        if (E >= -100 && E <= 100) {
-          const float sc = __uint_as_float(sbits << 23);
-          s16x2_t w0 = {0, 0}, w1 = {0, 0};
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[0], v[1], sc, false);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, v[2], v[3], sc, true);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[4], v[5], sc, false);
-          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, v[6], v[7], sc, true);
-          cw[0] = __builtin_bit_cast(uint32_t, w0);
-          cw[1] = __builtin_bit_cast(uint32_t, w1);
-        } else {
-          const float f = exp2_neg(E);
-          uint32_t q[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) q[t] = enc_e4m3_sw(v[t] * f);
-          cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-          cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-        }
+        codes_e8m0_fp8(v, E, cw);
       } else {
         // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
         // stored value.  Far from 1 a residual or the reciprocal of the fast
@@ -500,9 +588,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         // that v / su below 2^-100 may differ -- where every code is +-0.
         // rs is rounded downwards so that rl >= 0 and a zero v keeps its sign.
         const bool fastq = m >= 0x1p-71f && m <= 0x1p+100f;
-        constexpr float H448 = 1.0f / 448.0f;
-        constexpr float L448 = (float)(1.0 / 448.0 - (double)H448);
-        const float s32 = fastq ? __builtin_fmaf(m, H448, m * L448) : m / 448.0f;
+        const float s32 = fastq ? div448_fast(m) : m / 448.0f;
         sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
         const float su = __uint_as_float(sbits << 16);
         if (fastq) {
@@ -512,13 +598,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
           float qv[8];
 #pragma unroll
           for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[t], rs, v[t] * rl);
-          int w0 = 0, w1 = 0;
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], w0, false);
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], w0, true);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4], qv[5], w1, false);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(qv[6], qv[7], w1, true);
-          cw[0] = (uint32_t)w0;
-          cw[1] = (uint32_t)w1;
+          codes_fp8(qv, cw);
         } else {
           uint32_t q[8];
 #pragma unroll
@@ -621,6 +701,17 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
       st_u32(in ? o.p0 + 4 * c : lsink, o.w[j].x, c_al);
       st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[j]);  // every lane of the group
     }
+  } else if constexpr (MODE == M_MXFP8 || MODE == M_FP8_ROW) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = chunk_of<L>(li, j);
+      const bool in = FAST || c < a.nchunk;
+      st_u64(in ? o.p0 + 8 * c : lsink, make_uint2(o.w[j].x, o.w[j].y), c_al);
+      if constexpr (MODE == M_MXFP8)
+        st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[j]);  // every lane of the group
+    }
+    // every lane of the row writes the row's fp32 scale
+    if constexpr (MODE == M_FP8_ROW) st_u32(o.p1, o.sb[0], a.a_align);
   } else {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
@@ -775,17 +866,17 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       if constexpr (R <= 2) {
         // per-row destinations on the scalar unit, then picked per lane
         d = dst(t, 0);
-        if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT) ad = adst(t, 0);
+        if constexpr (has_aux(MODE)) ad = adst(t, 0);
         if constexpr (R == 2) {
           d = sub ? dst(t, 1) : d;
-          if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT) ad = sub ? adst(t, 1) : ad;
+          if constexpr (has_aux(MODE)) ad = sub ? adst(t, 1) : ad;
         }
       } else {
         // many rows per wave: each lane computes its own row's destination
         const uint32_t sl = t.own;
         const bool live = lane_live(t);
         d = live ? row_addr(a.cache, sl, a, a.c_pitch, a.c_bstride) : g_sink;
-        if constexpr (MODE == M_MXFP4 || MODE == M_SPLIT)
+        if constexpr (has_aux(MODE))
           ad = live ? row_addr(a.aux, sl, a, a.a_pitch, a.a_bstride) : g_sink + kSinkHalf;
       }
       out.p0 = d;
@@ -901,6 +992,10 @@ kfn_t pick(int mode, bool norm, bool rope, int L, int C, int fast) {
                   : pick_layout<M_FP8_E8M0, false, false>(L, C, fast);
     case M_MXFP4:
       return pick_layout<M_MXFP4, false, false>(L, C, fast);
+    case M_MXFP8:
+      return pick_layout<M_MXFP8, false, false>(L, C, fast);
+    case M_FP8_ROW:
+      return pick_layout<M_FP8_ROW, false, false>(L, C, fast);
     default:
       return pick_layout<M_SPLIT, true, true>(L, C, fast);
   }
@@ -983,7 +1078,7 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
                 ? (int32_t)((p.kv_cache_col - p.concat_col) / 16)
                 : -1;
   a.c_align = p.c_align;
-  a.a_align = p.mode == KVEPI_MODE_MXFP4 || p.mode == KVEPI_MODE_BF16_SPLIT ? p.a_align : 16;
+  a.a_align = p.aux != nullptr ? p.a_align : 16;
   a.eps = p.eps;
   a.nseg_f = (float)p.nope;
   a.inv_nseg = (p.nope & (p.nope - 1)) == 0 ? 1.0f / (float)p.nope : 0.0f;

@@ -35,10 +35,13 @@ def cache_tensor(spec: kvgen.CacheSpec, init: np.ndarray, device, offset: int = 
         view = flat.as_strided((spec.block_num, spec.block_size, 1, spec.head_dim),
                                (spec.block_stride, spec.head_dim, spec.head_dim, 1), offset)
     else:
-        assert offset % 2 == 0
-        b = flat.view(torch.bfloat16)
+        # bf16 (2-byte) or fp32 (4-byte) elements
+        e = spec.elem_bytes
+        assert offset % e == 0
+        n = flat.numel() // e * e
+        b = flat[:n].view(torch.bfloat16 if e == 2 else torch.float32)
         view = b.as_strided((spec.block_num, spec.block_size, 1, spec.head_dim),
-                            (spec.block_stride, spec.head_dim, spec.head_dim, 1), offset // 2)
+                            (spec.block_stride, spec.head_dim, spec.head_dim, 1), offset // e)
     return view, flat
 
 
@@ -96,6 +99,8 @@ def _code_positions(w: kvgen.Workload):
         ncode = w.d - 64
     elif w.mode == kvgen.MODE_MXFP4:
         ncode = w.d // 2
+    elif w.mode in (kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
+        ncode = w.d
     else:
         return np.zeros(0, np.int64), 0
     blk, pos = np.divmod(hit, w.cache.block_size)

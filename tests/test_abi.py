@@ -62,7 +62,9 @@ def test_row_bytes_page_values(row):
 
 @pytest.mark.parametrize("mode,d,g,status", [
     (2, 256, 64, 5), (7, 256, 64, 5), (0, 100, 64, 2), (0, 64, 64, 2), (1, 8256, 64, 2),
-    (0, 256, 32, 4), (3, 48, 32, 2), (3, 128, 64, 4), (3, 8224, 32, 2)])
+    (0, 256, 32, 4), (3, 48, 32, 2), (3, 128, 64, 4), (3, 8224, 32, 2),
+    (5, 48, 32, 2), (5, 128, 64, 4), (5, 8224, 32, 2), (6, 96, 32, 4), (6, 48, 0, 2),
+    (6, 128, 64, 4)])
 def test_row_bytes_rejects(mode, d, g, status):
     with pytest.raises(B.KvepiError) as e:
         B.kvepi_row_bytes(mode, d, g)
@@ -106,6 +108,11 @@ def test_valid_call_reports_zero_workspace():
     aux = _cache(data=0x60000, hd=4)
     assert call(1, d=128, mode=3, group=32, cache=_cache(hd=64), aux=aux) == (0, 0)
     assert call(1, d=576, mode=1, cache=_cache(hd=648)) == (0, 0)
+    assert call(1, d=128, mode=5, group=32, cache=_cache(hd=128), aux=aux) == (0, 0)
+    assert call(1, d=128, mode=6, group=0, cache=_cache(hd=128),
+                aux=_cache(data=0x60000, hd=1)) == (0, 0)
+    assert call(1, d=128, mode=6, group=128, cache=_cache(hd=128),
+                aux=_cache(data=0x60004, hd=3)) == (0, 0)
     ckv = _cache(hd=512)
     k = _cache(data=0x70000, hd=64)
     assert call(1, d=576, mode=4, cache=ckv, aux=k, gamma=P16C, cos=P16D,
@@ -145,6 +152,20 @@ BAD = [
                                           aux=_cache(hd=3)), 2),
     ("mxfp4 cache_scale other block count", dict(mode=3, d=128, group=32,
                                                  cache=_cache(hd=64), aux=_cache(bn=4, hd=4)), 2),
+    ("mxfp8 without cache_scale", dict(mode=5, d=128, group=32, cache=_cache(hd=128)), 1),
+    ("mxfp8 with rope", dict(mode=5, d=128, group=32, cache=_cache(hd=128), cos=P16C,
+                             sin=P16D, aux=_cache(hd=4)), 5),
+    ("mxfp8 cache too narrow", dict(mode=5, d=128, group=32, cache=_cache(hd=127),
+                                    aux=_cache(hd=4)), 2),
+    ("mxfp8 cache_scale too narrow", dict(mode=5, d=128, group=32, cache=_cache(hd=128),
+                                          aux=_cache(hd=3)), 2),
+    ("fp8 row with gamma", dict(mode=6, d=128, group=0, cache=_cache(hd=128), gamma=P16C,
+                                aux=_cache(hd=1)), 5),
+    ("fp8 row without cache_scale", dict(mode=6, d=128, group=0, cache=_cache(hd=128)), 1),
+    ("fp8 row scale cache misaligned", dict(mode=6, d=128, group=0, cache=_cache(hd=128),
+                                            aux=_cache(data=0x60002, hd=1)), 3),
+    ("fp8 row group size", dict(mode=6, d=128, group=32, cache=_cache(hd=128),
+                                aux=_cache(hd=1)), 4),
     ("split without rope", dict(mode=4, d=576, gamma=P16C, cache=_cache(hd=512),
                                 aux=_cache(hd=64)), 4),
     ("split k cache too narrow", dict(mode=4, d=576, gamma=P16C, cos=P16D, sin=P16D,

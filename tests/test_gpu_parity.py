@@ -17,14 +17,18 @@ pytestmark = pytest.mark.gpu
 def _small(mode, T, d, *, seed, bs=16, head=None, stride_extra=0, aux_head=None,
            norm=False, rope=False, skip=0.1, row_sigma=0.0, **kw):
     import oracle
-    _, kc, sc = oracle.row_bytes(mode, d, 32 if mode == 3 else 64) if mode != 4 else (0, d - 64, 64)
+    group = {3: 32, 5: 32, 6: 0}.get(mode, 64)
+    _, kc, sc = oracle.row_bytes(mode, d, group) if mode != 4 else (0, d - 64, 64)
     head = head or kc
     nblk = (T + bs - 1) // bs + 2
     cache = CacheSpec(nblk, bs, head, bs * head + stride_extra, 2 if mode == 4 else 1)
     aux = None
-    if mode == 3:
+    if mode in (3, 5):
         ah = aux_head or sc
         aux = CacheSpec(nblk, bs, ah, bs * ah + stride_extra)
+    elif mode == 6:
+        ah = aux_head or 1
+        aux = CacheSpec(nblk, bs, ah, bs * ah + stride_extra, 4)
     elif mode == 4:
         ah = aux_head or 64
         aux = CacheSpec(nblk, bs, ah, bs * ah + stride_extra, 2)
@@ -73,6 +77,14 @@ def test_mxfp4_sweep(d):
     check(w)
 
 
+@pytest.mark.parametrize("mode", [5, 6])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 160, 256, 512, 1024, 4096, 8192])
+def test_indexer_fp8_sweep(mode, d):
+    w = _small(mode, 400 if d <= 1024 else 60, d, seed=d + mode, bs=3, stride_extra=5,
+               row_sigma=2.0)
+    assert check(w) == 0
+
+
 # ---- layouts and alignment ----------------------------------------------------------
 
 @pytest.mark.parametrize("offset", [0, 1, 2, 4, 8])
@@ -91,6 +103,18 @@ def test_mode0_odd_head_dim(offset):
 @pytest.mark.parametrize("offset,aux_offset", [(0, 0), (1, 3), (4, 1)])
 def test_mxfp4_odd_layout(offset, aux_offset):
     w = _small(3, 300, 128, seed=13, bs=11, head=67, aux_head=5, stride_extra=1)
+    check(w, offset=offset, aux_offset=aux_offset)
+
+
+@pytest.mark.parametrize("offset,aux_offset", [(0, 0), (1, 3), (4, 1)])
+def test_mxfp8_odd_layout(offset, aux_offset):
+    w = _small(5, 300, 128, seed=23, bs=11, head=131, aux_head=5, stride_extra=1)
+    check(w, offset=offset, aux_offset=aux_offset)
+
+
+@pytest.mark.parametrize("offset,aux_offset", [(0, 0), (1, 4), (6, 12)])
+def test_fp8_row_odd_layout(offset, aux_offset):
+    w = _small(6, 300, 256, seed=24, bs=7, head=259, aux_head=3, stride_extra=1)
     check(w, offset=offset, aux_offset=aux_offset)
 
 
@@ -130,9 +154,9 @@ def test_zero_tokens_is_noop():
     assert np.all(flat.cpu().numpy() == kvgen.PREFILL)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 3, 4])
+@pytest.mark.parametrize("mode", [0, 1, 3, 4, 5, 6])
 def test_all_skipped_and_out_of_range(mode):
-    d = 128 if mode == 3 else 576
+    d = 128 if mode in (3, 5, 6) else 576
     w = _small(mode, 200, d, seed=17, norm=mode == 4, rope=mode == 4)
     w.slots[:100] = -1
     w.slots[100:] = w.cache.num_slots + np.arange(100)
@@ -144,12 +168,12 @@ def test_all_skipped_and_out_of_range(mode):
         assert np.all(agot == kvgen.PREFILL)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 3, 4])
+@pytest.mark.parametrize("mode", [0, 1, 3, 4, 5, 6])
 def test_special_values(mode):
     # zero rows and groups, negative zeros, bf16 subnormals, huge values and
     # exact ties: exercises the exact-division fallbacks and code rounding.
     rng = np.random.default_rng(18)
-    d = 128 if mode == 3 else 576
+    d = 128 if mode in (3, 5, 6) else 576
     T = 64
     x = rng.standard_normal((T, d))
     x[0] = 0.0
@@ -188,6 +212,10 @@ def _exponent_sweep_rows(mode, T, d, seed):
         G, nseg, vmax = 32, d, 6.0
         mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
         kmax = 125
+    elif mode == 5:
+        G, nseg, vmax = 32, d, 448.0
+        mids = [2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 9.5, 13.5, 17.0, 240.0, 416.0]
+        kmax = 119
     else:
         G, nseg, vmax = 64, d - 64, 448.0
         mids = [2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 9.5, 13.5, 17.0, 240.0, 416.0]
@@ -209,21 +237,43 @@ def _exponent_sweep_rows(mode, T, d, seed):
     return kvgen.to_bf16(x)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 3])
+@pytest.mark.parametrize("mode", [0, 1, 3, 5])
 def test_scale_exponent_sweep(mode):
     # every e8m0 / bf16 power-of-two scale, both sides of the range where the
     # kernel uses the hardware converts and fast division, with exact ties
-    d = 128 if mode == 3 else 576
-    T = 400 if mode == 3 else 200
+    d = 128 if mode in (3, 5) else 576
+    T = 400 if mode in (3, 5) else 200
     xb = _exponent_sweep_rows(mode, T, d, seed=20 + mode)
     w = _small(mode, T, d, seed=21, skip=0.0, x=xb)
     n = check(w)
     assert n == 0
 
 
+def test_fp8_row_amax_sweep():
+    # per-row FP8: row maxima over the whole bf16 range (the fast path covers
+    # [2^-71, 2^100]), rows whose scale is a power of two (exact code ties),
+    # and random rows whose scale is not
+    rng = np.random.default_rng(25)
+    d, T = 128, 600
+    x = rng.standard_normal((T, d))
+    for r in range(T):
+        k = -141 + (r * 7) % 268  # 2^k spans subnormal to near the bf16 max
+        amax = 448.0 * 2.0 ** min(k, 118)
+        if r % 3 == 0:
+            # the scale is exactly 2^k: code midpoints are exact ties
+            mids = np.array([2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 9.5, 13.5, 240.0])
+            v = rng.choice(mids, d) * np.where(rng.random(d) < 0.5, -1.0, 1.0)
+        else:
+            v = np.clip(rng.standard_normal(d) * 100, -447, 447) * (1 + rng.random() / 7)
+        v[r % d] = 448.0 if r % 2 else -448.0
+        x[r] = v * 2.0 ** min(k, 118) if r % 3 == 0 else v / 448.0 * amax
+    w = _small(6, T, d, seed=26, skip=0.0, x=kvgen.to_bf16(x))
+    assert check(w) == 0
+
+
 @pytest.mark.parametrize("waves", [4, 8, 64])
 @pytest.mark.parametrize("case", ["fused576", "mode1_576", "mxfp4_128", "split576", "mode0_2112",
-                                  "mode0_256"])
+                                  "mode0_256", "mxfp8_128", "fp8row_128", "fp8row_1024"])
 def test_many_iterations_per_wave(case, waves, monkeypatch):
     # a capped grid makes each wave run hundreds of iterations: slot windows
     # are reloaded many times and the pipeline runs through its steady state
@@ -237,6 +287,12 @@ def test_many_iterations_per_wave(case, waves, monkeypatch):
         w = _small(3, T, 128, seed=33, bs=128, row_sigma=1.0)
     elif case == "split576":
         w = _small(4, T, 576, seed=34, bs=5, norm=True, rope=True)
+    elif case == "mxfp8_128":
+        w = _small(5, T, 128, seed=37, bs=128, row_sigma=1.0)
+    elif case == "fp8row_128":
+        w = _small(6, T, 128, seed=38, bs=64, row_sigma=1.0)
+    elif case == "fp8row_1024":
+        w = _small(6, 700, 1024, seed=39, bs=16, row_sigma=1.0)
     elif case == "mode0_2112":
         w = _small(0, 600, 2112, seed=35, bs=9, norm=True, rope=True)
     else:
