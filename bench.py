@@ -43,9 +43,9 @@ def algorithmic_bytes(w: kvgen.Workload) -> int:
     rope = 2 * 2 * 64 if w.cos is not None else 0
     if w.mode == kvgen.MODE_BF16_SPLIT:
         written = 2 * (w.d - 64) + 2 * 64
-    elif w.mode == kvgen.MODE_MXFP4:
+    elif w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
         _, kc, sc = kvepi_row_bytes(w.mode, w.d, w.group_size)
-        written = kc + sc
+        written = kc + sc * w.aux.elem_bytes  # codes + the cache_scale row
     else:
         _, kc, _ = kvepi_row_bytes(w.mode, w.d, w.group_size)
         written = kc
@@ -150,6 +150,8 @@ def upload(w: kvgen.Workload, dev):
         flat = torch.from_numpy(init).to(dev)
         if spec.elem_bytes == 2:
             flat = flat.view(torch.bfloat16)
+        elif spec.elem_bytes == 4:
+            flat = flat.view(torch.float32)
         view = flat.as_strided((spec.block_num, spec.block_size, 1, spec.head_dim),
                                (spec.block_stride, spec.head_dim, spec.head_dim, 1))
         return view, flat
@@ -197,7 +199,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4,
-                    help="workload index (default 4: the d=576 fused epilog)")
+                    choices=range(len(kvgen.CONFIG_NAMES)),
+                    help="workload index (default 4: the d=576 fused epilog; 5 and 6: "
+                         "the MX-FP8 and per-row FP8 indexer modes)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",

@@ -160,7 +160,9 @@ def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
 # ---- the five named workloads ---------------------------------------------
 
 CONFIG_NAMES = ("mode0_tiny_d256", "rmsnorm_rope_bf16_d576", "mode1_prefill_d576",
-                "mxfp4_indexer_d128", "fused_epilog_d576")
+                "mxfp4_indexer_d128", "fused_epilog_d576",
+                # the other indexer modes at the MX-FP4 indexer's shape
+                "mxfp8_indexer_d128", "fp8row_indexer_d128")
 
 
 def config(i: int) -> Workload:
@@ -196,4 +198,18 @@ def config(i: int) -> Workload:
         return make(CONFIG_NAMES[4], MODE_FP8_BF16SCALE, 262144, 576, seed=4,
                     cache=CacheSpec(2048, 128, 672, 128 * 672 * 5 // 4),
                     norm=True, rope=True, max_pos=131072, skip_frac=0.03)
+    if i == 5:
+        # MX-FP8 indexer at the shape of 3: codes [1024,128,1,128] u8 +
+        # e8m0 cache_scale [1024,128,1,4]
+        return make(CONFIG_NAMES[5], MODE_MXFP8, 131072, 128, seed=5,
+                    cache=CacheSpec(1024, 128, 128, 128 * 128),
+                    aux=CacheSpec(1024, 128, 4, 128 * 4),
+                    row_sigma=1.0, skip_frac=0.01)
+    if i == 6:
+        # per-row FP8 indexer at the shape of 3: codes [1024,128,1,128] u8 +
+        # fp32 cache_scale [1024,128,1,1]
+        return make(CONFIG_NAMES[6], MODE_FP8_ROW, 131072, 128, seed=6,
+                    cache=CacheSpec(1024, 128, 128, 128 * 128),
+                    aux=CacheSpec(1024, 128, 1, 128 * 1, 4),
+                    row_sigma=1.0, skip_frac=0.01)
     raise IndexError(i)

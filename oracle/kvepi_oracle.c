@@ -10,6 +10,12 @@
  * All floating point is IEEE binary32 evaluated in source order (x86-64 SSE,
  * no excess precision, no contraction); binary64 is used only where a value
  * is exact in it (comparisons against fmax*2^E, scaled code search).
+ *
+ * Parity unpinned: the codes of quantMode 0 and of the indexer fp8 mode
+ * divide each value by the scale as it is stored (bf16 in quantMode 0, fp32
+ * in the fp8 mode), not by the unrounded amax / 448.  The pages print no
+ * example that tells the two apart; the tests pin this choice only where the
+ * two agree (power-of-two scales).
  */
 #include "kvepi_oracle.h"
 

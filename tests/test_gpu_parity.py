@@ -36,9 +36,9 @@ def _small(mode, T, d, *, seed, bs=16, head=None, stride_extra=0, aux_head=None,
                       norm=norm, rope=rope, skip_frac=skip, row_sigma=row_sigma, **kw)
 
 
-# ---- the five named workloads at full size ----------------------------------
+# ---- the named workloads at full size ----------------------------------
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", range(7))
 def test_config_parity(i):
     w = kvgen.config(i)
     n = check(w, label=f"config {i} {w.name}")
