@@ -84,6 +84,16 @@ def lib() -> ctypes.CDLL:
         L.kvo_epilog.argtypes = [ctypes.c_int, I64, I64, P, I64, P, P, P, F, P, I32,
                                  ctypes.POINTER(_Cache), ctypes.POINTER(_Cache)]
         L.kvo_epilog.restype = ctypes.c_int
+        L.kvo_fp16_to_f32.argtypes = [ctypes.c_uint16]
+        L.kvo_fp16_to_f32.restype = F
+        L.kvo_quant_row_x.argtypes = [ctypes.c_int, P, I64, I32, ctypes.c_int, P, P]
+        L.kvo_quant_row_x.restype = ctypes.c_int
+        L.kvo_token_slot.argtypes = [ctypes.c_int, P, I64, I64, I64, I64]
+        L.kvo_token_slot.restype = I64
+        L.kvo_epilog_ex.argtypes = [ctypes.c_int, I64, I64, P, I64, ctypes.c_int, P, P, P, F,
+                                    P, ctypes.c_int, I64, I32, ctypes.POINTER(_Cache),
+                                    ctypes.POINTER(_Cache)]
+        L.kvo_epilog_ex.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -158,12 +168,19 @@ def row_bytes(mode: int, d: int, group_size: int):
     return cc.value, kc.value, sc.value
 
 
-def quant_row(mode: int, v_bf16, group_size: int):
+def fp16_to_f32(h: int) -> float:
+    return float(lib().kvo_fp16_to_f32(int(h)))
+
+
+def quant_row(mode: int, v_bf16, group_size: int, *, x_fp16: bool = False):
+    """Quantise one row of 16-bit values (bf16 bits, or fp16 bits with
+    x_fp16 in the indexer modes)."""
     v = _c(v_bf16, np.uint16)
     _, kc, sc = row_bytes(mode, v.size, group_size)
     out = np.empty(kc, np.uint8)
     sout = np.empty(4 * sc, np.uint8)
-    rc = lib().kvo_quant_row(mode, _ptr(v), v.size, group_size, _ptr(out), _ptr(sout))
+    rc = lib().kvo_quant_row_x(mode, _ptr(v), v.size, group_size, int(x_fp16), _ptr(out),
+                               _ptr(sout))
     if rc != 0:
         raise ValueError("quant_row rejected its arguments")
     if mode in (MODE_MXFP4, MODE_MXFP8):
@@ -175,19 +192,37 @@ def quant_row(mode: int, v_bf16, group_size: int):
 
 # ---- whole epilog ---------------------------------------------------------
 
+INDEX_SLOT, INDEX_BATCH, INDEX_BLOCK, INDEX_BATCH_START = 0, 1, 2, 3
+
+
+def token_slot(index_mode: int, index, t: int, seq_len: int, block_num: int,
+               block_size: int) -> int:
+    idx = _c(index, np.int32)
+    return int(lib().kvo_token_slot(index_mode, _ptr(idx), t, seq_len, block_num, block_size))
+
+
 def epilog(mode: int, x, slot_mapping, cache_bytes, cache_geom, *, group_size: int,
            gamma=None, cos=None, sin=None, eps: float = 1e-6, aux_bytes=None,
-           aux_geom=None):
+           aux_geom=None, x_fp16: bool = False, index_mode: int = INDEX_SLOT,
+           seq_len: int = 0):
     """Run the oracle in place on host byte buffers.
 
     cache_geom / aux_geom: (block_num, block_size, head_dim, block_stride) in
     elements of the cache dtype.  x is uint16 [T, d] (row stride = its
-    row stride in elements)."""
+    row stride in elements; fp16 bits with x_fp16).  slot_mapping is the
+    index array of index_mode (T entries for INDEX_SLOT and INDEX_BATCH,
+    B * ceil(seq_len / block_size) for INDEX_BLOCK, B for
+    INDEX_BATCH_START, with B = T / seq_len)."""
     x = np.asarray(x, np.uint16)
     assert x.ndim == 2 and x.strides[1] == 2
     T, d = x.shape
     slots = _c(slot_mapping, np.int32)
-    assert slots.size == T
+    if index_mode in (INDEX_SLOT, INDEX_BATCH):
+        assert slots.size == T
+    else:
+        B = T // seq_len
+        n = B * (-(-seq_len // int(cache_geom[1]))) if index_mode == INDEX_BLOCK else B
+        assert slots.size == n
     assert cache_bytes.dtype == np.uint8 and cache_bytes.flags.c_contiguous
     gamma = None if gamma is None else _c(gamma, np.uint16)
     cos = None if cos is None else _c(cos, np.uint16)
@@ -197,9 +232,10 @@ def epilog(mode: int, x, slot_mapping, cache_bytes, cache_geom, *, group_size: i
     if aux_bytes is not None:
         assert aux_bytes.dtype == np.uint8 and aux_bytes.flags.c_contiguous
         a = _Cache(aux_bytes.ctypes.data, *[int(v) for v in aux_geom])
-    rc = lib().kvo_epilog(mode, T, d, x.ctypes.data_as(ctypes.c_void_p),
-                          x.strides[0] // 2, _ptr(gamma), _ptr(cos), _ptr(sin),
-                          ctypes.c_float(eps), _ptr(slots), group_size,
-                          ctypes.byref(c), ctypes.byref(a) if a is not None else None)
+    rc = lib().kvo_epilog_ex(mode, T, d, x.ctypes.data_as(ctypes.c_void_p),
+                             x.strides[0] // 2, int(x_fp16), _ptr(gamma), _ptr(cos),
+                             _ptr(sin), ctypes.c_float(eps), _ptr(slots), index_mode,
+                             seq_len, group_size, ctypes.byref(c),
+                             ctypes.byref(a) if a is not None else None)
     if rc != 0:
         raise ValueError("oracle epilog rejected its arguments")

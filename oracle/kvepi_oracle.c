@@ -34,6 +34,22 @@ float kvo_bf16_to_f32(uint16_t h) {
   return f;
 }
 
+/* IEEE binary16 ("indexer_quant_cache" 接口功能: the indexer also takes
+ * float16 activations), decoded from its definition: sign, 5-bit exponent
+ * with bias 15, 10-bit fraction; exponent 0 holds the subnormals f * 2^-24,
+ * exponent 31 the infinities and NaNs.  Every value is exact in binary32. */
+float kvo_fp16_to_f32(uint16_t h) {
+  const int sign = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+  float mag;
+  if (e == 0)
+    mag = ldexpf((float)f, -24);
+  else if (e == 31)
+    mag = f == 0 ? INFINITY : NAN;
+  else
+    mag = ldexpf((float)(1024 + f), e - 25);
+  return sign ? -mag : mag;
+}
+
 static uint32_t f32_bits(float f) {
   uint32_t u;
   memcpy(&u, &f, 4);
@@ -291,10 +307,18 @@ static void put_u16le(uint8_t *p, uint16_t v) {
  * 约束说明 (nope codes | rope at 16 bit | one scale per group | zero padding
  * to kvCacheCol), and "indexer_quant_cache" mxfp4 (codes of the whole row,
  * two per byte, scales to cache_scale). */
-int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
-                  uint8_t *out, uint8_t *scale_out) {
+/* value i of an input row: bf16, or (indexer modes) fp16 bits */
+static float in_f32(const uint16_t *v, int64_t i, int fp16) {
+  return fp16 ? kvo_fp16_to_f32(v[i]) : kvo_bf16_to_f32(v[i]);
+}
+
+int kvo_quant_row_x(int mode, const uint16_t *v, int64_t d, int32_t group_size, int x_fp16,
+                    uint8_t *out, uint8_t *scale_out) {
   int64_t cc, kc, sc;
   if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
+  const int fp16 = x_fp16 != 0;
+  if (fp16 && mode != KVO_MODE_MXFP4 && mode != KVO_MODE_MXFP8 && mode != KVO_MODE_FP8_ROW)
+    return -1; /* fp16 rows only in the indexer modes */
   if (mode == KVO_MODE_FP8_BF16SCALE || mode == KVO_MODE_FP8_E8M0) {
     int64_t nope = d - 64;
     memset(out, 0, (size_t)kc);
@@ -302,7 +326,7 @@ int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
       int64_t i0 = g * 64, i1 = i0 + 64 < nope ? i0 + 64 : nope;
       float amax = 0.0f;
       for (int64_t i = i0; i < i1; ++i) {
-        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        float a = fabsf(in_f32(v, i, fp16));
         if (a > amax) amax = a;
       }
       float s_use;
@@ -320,7 +344,7 @@ int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
         if (s_use == 0.0f) {
           out[i] = 0x00;
         } else {
-          float q = kvo_bf16_to_f32(v[i]) / s_use;
+          float q = in_f32(v, i, fp16) / s_use;
           out[i] = kvo_enc_e4m3(q);
         }
       }
@@ -334,14 +358,14 @@ int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
       int64_t i0 = g * 32, i1 = i0 + 32 < d ? i0 + 32 : d;
       float amax = 0.0f;
       for (int64_t i = i0; i < i1; ++i) {
-        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        float a = fabsf(in_f32(v, i, fp16));
         if (a > amax) amax = a;
       }
       int E = kvo_e8m0_exponent(amax, 6.0f);
       scale_out[g] = (uint8_t)(E + 127);
       float s_use = ldexpf(1.0f, E);
       for (int64_t i = i0; i < i1; ++i) {
-        uint8_t c = kvo_enc_e2m1(kvo_bf16_to_f32(v[i]) / s_use);
+        uint8_t c = kvo_enc_e2m1(in_f32(v, i, fp16) / s_use);
         /* element 2j in the low nibble, 2j+1 in the high nibble */
         if (i % 2 == 0)
           out[i / 2] = (uint8_t)((out[i / 2] & 0xF0) | c);
@@ -357,13 +381,13 @@ int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
       int64_t i0 = g * 32, i1 = i0 + 32 < d ? i0 + 32 : d;
       float amax = 0.0f;
       for (int64_t i = i0; i < i1; ++i) {
-        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        float a = fabsf(in_f32(v, i, fp16));
         if (a > amax) amax = a;
       }
       int E = kvo_e8m0_exponent(amax, 448.0f);
       scale_out[g] = (uint8_t)(E + 127);
       float s_use = ldexpf(1.0f, E);
-      for (int64_t i = i0; i < i1; ++i) out[i] = kvo_enc_e4m3(kvo_bf16_to_f32(v[i]) / s_use);
+      for (int64_t i = i0; i < i1; ++i) out[i] = kvo_enc_e4m3(in_f32(v, i, fp16) / s_use);
     }
     return 0;
   }
@@ -372,16 +396,21 @@ int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
      * max|x| / 448 is kept as FLOAT and the codes divide by it */
     float amax = 0.0f;
     for (int64_t i = 0; i < d; ++i) {
-      float a = fabsf(kvo_bf16_to_f32(v[i]));
+      float a = fabsf(in_f32(v, i, fp16));
       if (a > amax) amax = a;
     }
     float s = amax / 448.0f;
     memcpy(scale_out, &s, 4); /* little-endian fp32 */
     for (int64_t i = 0; i < d; ++i)
-      out[i] = s == 0.0f ? 0x00 : kvo_enc_e4m3(kvo_bf16_to_f32(v[i]) / s);
+      out[i] = s == 0.0f ? 0x00 : kvo_enc_e4m3(in_f32(v, i, fp16) / s);
     return 0;
   }
   return -1;
+}
+
+int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
+                  uint8_t *out, uint8_t *scale_out) {
+  return kvo_quant_row_x(mode, v, d, group_size, 0, out, scale_out);
 }
 
 /* ======================================================================== */
@@ -394,30 +423,84 @@ static uint8_t *row_ptr(const kvo_cache *c, int64_t slot, int64_t esz) {
   return c->data + (blk * c->block_stride + pos * c->head_dim) * esz;
 }
 
+/* Cache row of token t, or -1 when the token is skipped.  Tokens are
+ * batch-major (t = b * seq_len + s) in the index modes other than SLOT.
+ *  SLOT:  index[t] is the token's slot ("aclnnKvCompressEpilog" 约束说明;
+ *         "aclnnKvRmsNormRopeCache" index constraints, PA_BNSD/PA_NZ;
+ *         "indexer_quant_cache" 约束).
+ *  BATCH: index [B, S]; index[b, s] is the row inside batch b's own
+ *         block_size rows ("aclnnKvRmsNormRopeCache" index constraints,
+ *         Norm: values in [-1, Scache), repeats across batches allowed).
+ *  BLOCK: index [B, ceil(S / block_size)]; entry c names the block (value /
+ *         block_size) that takes tokens c*block_size .. of the batch, token
+ *         s at row s % block_size of it ("aclnnKvRmsNormRopeCache" index
+ *         constraints, PA_BLK_BNSD/PA_BLK_NZ: value / BlockSize distinct).
+ *  BATCH_START: index [B]; token s of batch b goes to row index[b] + s of
+ *         batch b's rows (the blog on aclnnDequantRopeQuantKvcache, cache
+ *         modes: the contiguous mode's offset).
+ * -1, and any value that would leave the cache, skip the token. */
+int64_t kvo_token_slot(int index_mode, const int32_t *index, int64_t t, int64_t seq_len,
+                       int64_t block_num, int64_t block_size) {
+  const int64_t num_slots = block_num * block_size;
+  if (index_mode == KVO_INDEX_SLOT) {
+    int64_t v = index[t];
+    return (v >= 0 && v < num_slots) ? v : -1;
+  }
+  if (seq_len <= 0) return -1;
+  const int64_t b = t / seq_len, s = t % seq_len;
+  if (index_mode == KVO_INDEX_BATCH) {
+    int64_t v = index[t];
+    if (v < 0 || v >= block_size || b >= block_num) return -1;
+    return b * block_size + v;
+  }
+  if (index_mode == KVO_INDEX_BLOCK) {
+    const int64_t nc = (seq_len + block_size - 1) / block_size;
+    int64_t v = index[b * nc + s / block_size];
+    if (v < 0 || v >= num_slots) return -1;
+    return (v / block_size) * block_size + s % block_size;
+  }
+  if (index_mode == KVO_INDEX_BATCH_START) {
+    int64_t v = index[b];
+    if (v < 0 || v + s >= block_size || b >= block_num) return -1;
+    return b * block_size + v + s;
+  }
+  return -1;
+}
+
 int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
                int64_t x_row_stride, const uint16_t *gamma,
                const uint16_t *cos, const uint16_t *sin, float eps,
                const int32_t *slot_mapping, int32_t group_size,
                const kvo_cache *cache, const kvo_cache *aux) {
+  return kvo_epilog_ex(mode, T, d, x, x_row_stride, 0, gamma, cos, sin, eps, slot_mapping,
+                       KVO_INDEX_SLOT, 0, group_size, cache, aux);
+}
+
+int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_row_stride,
+                  int x_fp16, const uint16_t *gamma, const uint16_t *cos, const uint16_t *sin,
+                  float eps, const int32_t *index, int index_mode, int64_t seq_len,
+                  int32_t group_size, const kvo_cache *cache, const kvo_cache *aux) {
   int64_t cc, kc, sc;
   if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
+  if (index_mode != KVO_INDEX_SLOT && (seq_len <= 0 || T % seq_len != 0)) return -1;
   if ((cos == NULL) != (sin == NULL)) return -1;
   const int indexer = mode == KVO_MODE_MXFP4 || mode == KVO_MODE_MXFP8 ||
                       mode == KVO_MODE_FP8_ROW;
   if (indexer && (gamma || cos)) return -1;
   if (mode == KVO_MODE_BF16_SPLIT && (!gamma || !cos)) return -1;
   if ((indexer || mode == KVO_MODE_BF16_SPLIT) && !aux) return -1;
-  int64_t num_slots = cache->block_num * cache->block_size;
+  if (x_fp16 && !indexer) return -1;
   int64_t nope = d - 64;
   uint16_t *v = (uint16_t *)malloc((size_t)d * sizeof(uint16_t));
   uint8_t *row = (uint8_t *)malloc((size_t)kc + 64);
   uint8_t *srow = (uint8_t *)malloc((size_t)sc + 64);
   for (int64_t t = 0; t < T; ++t) {
-    int64_t s = slot_mapping[t];
-    if (s < 0 || s >= num_slots) continue; /* -1: token skipped */
+    int64_t s = kvo_token_slot(index_mode, index, t, seq_len, cache->block_num,
+                               cache->block_size);
+    if (s < 0) continue; /* -1: token skipped */
     const uint16_t *xr = x + t * x_row_stride;
     if (indexer) {
-      kvo_quant_row(mode, xr, d, group_size, row, srow);
+      kvo_quant_row_x(mode, xr, d, group_size, x_fp16, row, srow);
       memcpy(row_ptr(cache, s, 1), row, (size_t)kc);
       if (mode == KVO_MODE_FP8_ROW)
         memcpy(row_ptr(aux, s, 4), srow, 4);

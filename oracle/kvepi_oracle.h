@@ -49,6 +49,7 @@ extern "C" {
 
 /* ---- number formats ---------------------------------------------------- */
 float kvo_bf16_to_f32(uint16_t h);
+float kvo_fp16_to_f32(uint16_t h);     /* IEEE binary16, exact           */
 uint16_t kvo_f32_to_bf16(float f);     /* round to nearest, ties to even   */
 uint8_t kvo_enc_e4m3(float v);         /* OCP E4M3FN, RNE, saturate to 448 */
 uint8_t kvo_enc_e2m1(float v);         /* OCP E2M1 nibble, RNE, sat. to 6  */
@@ -82,6 +83,9 @@ int kvo_row_bytes(int mode, int64_t d, int32_t group_size, int64_t *concat_col,
  * the 4 little-endian bytes of the fp32 scale in scale_out (FP8 row). */
 int kvo_quant_row(int mode, const uint16_t *v, int64_t d, int32_t group_size,
                   uint8_t *out, uint8_t *scale_out);
+/* The same with x_fp16 != 0 reading v as IEEE binary16 (indexer modes). */
+int kvo_quant_row_x(int mode, const uint16_t *v, int64_t d, int32_t group_size, int x_fp16,
+                    uint8_t *out, uint8_t *scale_out);
 
 /* ---- whole epilog ------------------------------------------------------ */
 /* Cache geometry: [block_num, block_size, 1, head_dim] with head_dim and
@@ -100,6 +104,21 @@ int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
                const uint16_t *cos, const uint16_t *sin, float eps,
                const int32_t *slot_mapping, int32_t group_size,
                const kvo_cache *cache, const kvo_cache *aux);
+
+/* How a token finds its cache row (see kvo_token_slot). */
+#define KVO_INDEX_SLOT 0        /* index[T]: one slot per token              */
+#define KVO_INDEX_BATCH 1       /* index[B,S]: row within the batch's rows   */
+#define KVO_INDEX_BLOCK 2       /* index[B,ceil(S/bs)]: one block per chunk  */
+#define KVO_INDEX_BATCH_START 3 /* index[B]: first row of the batch's tokens */
+int64_t kvo_token_slot(int index_mode, const int32_t *index, int64_t t, int64_t seq_len,
+                       int64_t block_num, int64_t block_size);
+
+/* kvo_epilog with fp16 rows (x_fp16, indexer modes only) and the index
+ * modes above; T must be a multiple of seq_len outside the SLOT mode. */
+int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_row_stride,
+                  int x_fp16, const uint16_t *gamma, const uint16_t *cos, const uint16_t *sin,
+                  float eps, const int32_t *index, int index_mode, int64_t seq_len,
+                  int32_t group_size, const kvo_cache *cache, const kvo_cache *aux);
 
 #ifdef __cplusplus
 }
