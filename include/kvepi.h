@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KVEPI_VERSION 100 /* 1.0.0 */
+#define KVEPI_VERSION 110 /* 1.1.0: options (fp16 rows, index modes) */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KVEPI_API __attribute__((visibility("default")))
@@ -198,6 +198,73 @@ KVEPI_API kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
                        const kvepi_cache *cache_aux, int32_t quant_mode,
                        int32_t group_size, float eps, void *workspace,
                        uint64_t workspace_bytes, void *stream);
+
+/* ---- options: fp16 rows and index modes (version 1.1) -------------------
+ *
+ * The _ex entry points take the arguments of kvepi_get_workspace / kvepi_run
+ * plus an options struct (HOST pointer; NULL = every field 0, which is
+ * exactly the behaviour of the entry points above).
+ *
+ *  x_dtype     KVEPI_X_BF16, or KVEPI_X_FP16: x holds IEEE binary16 values
+ *              ("indexer_quant_cache" 接口功能: float16 or bfloat16 x); only
+ *              in the indexer modes 3, 5, 6, otherwise KVEPI_ERR_UNSUPPORTED.
+ *  index_mode  how the int32 array passed as slot_mapping places token t
+ *              (tokens are batch-major, t = b * seq_len + s, B = T / seq_len):
+ *    KVEPI_INDEX_SLOT        [T]: the token's slot, as above.
+ *    KVEPI_INDEX_BATCH       [B, seq_len]: row index[b, s] of batch b's rows,
+ *                            which are block b of the cache (block_size rows:
+ *                            the cache is [Bcache, Scache, 1, headDim] with
+ *                            Bcache = block_num >= B, Scache = block_size);
+ *                            values in [-1, Scache), repeats across batches
+ *                            allowed ("aclnnKvRmsNormRopeCache", index
+ *                            constraints, Norm mode).
+ *    KVEPI_INDEX_BLOCK       [B, ceil(seq_len / block_size)]: entry c names
+ *                            the block (value / block_size) taking tokens
+ *                            c*block_size .. of batch b, token s at row
+ *                            s % block_size of it; the blocks named must be
+ *                            distinct ("aclnnKvRmsNormRopeCache", index
+ *                            constraints, PA_BLK modes).
+ *    KVEPI_INDEX_BATCH_START [B]: token s of batch b goes to row index[b] + s
+ *                            of batch b's rows (block b); needs
+ *                            seq_len <= block_size (the blog on
+ *                            aclnnDequantRopeQuantKvcache, cache modes,
+ *                            contiguous mode).
+ *              -1, and any value that would place a token outside the cache
+ *              (or outside its batch's rows), skips the token(s).
+ *  seq_len     tokens per batch for the index modes other than SLOT: >= 1,
+ *              dividing num_tokens; B must not exceed block_num in the
+ *              BATCH and BATCH_START modes (KVEPI_ERR_SHAPE otherwise).
+ */
+#define KVEPI_X_BF16 0
+#define KVEPI_X_FP16 1
+#define KVEPI_INDEX_SLOT 0
+#define KVEPI_INDEX_BATCH 1
+#define KVEPI_INDEX_BLOCK 2
+#define KVEPI_INDEX_BATCH_START 3
+
+typedef struct kvepi_options {
+  int32_t x_dtype;
+  int32_t index_mode;
+  int64_t seq_len;
+} kvepi_options;
+
+KVEPI_API kvepi_status kvepi_get_workspace_ex(const void *x, int64_t num_tokens, int64_t d,
+                                    int64_t x_row_stride, const void *gamma,
+                                    const void *cos, const void *sin,
+                                    const int32_t *slot_mapping,
+                                    const kvepi_cache *cache,
+                                    const kvepi_cache *cache_aux,
+                                    int32_t quant_mode, int32_t group_size,
+                                    float eps, const kvepi_options *options,
+                                    uint64_t *workspace_bytes);
+
+KVEPI_API kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d,
+                          int64_t x_row_stride, const void *gamma,
+                          const void *cos, const void *sin,
+                          const int32_t *slot_mapping, const kvepi_cache *cache,
+                          const kvepi_cache *cache_aux, int32_t quant_mode,
+                          int32_t group_size, float eps, const kvepi_options *options,
+                          void *workspace, uint64_t workspace_bytes, void *stream);
 
 /* Static text for a status code (never NULL). */
 KVEPI_API const char *kvepi_status_str(kvepi_status status);

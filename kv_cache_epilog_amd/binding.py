@@ -29,6 +29,13 @@ KVEPI_MODE_BF16_SPLIT = 4
 KVEPI_MODE_MXFP8 = 5
 KVEPI_MODE_FP8_ROW = 6
 
+KVEPI_X_BF16 = 0
+KVEPI_X_FP16 = 1
+KVEPI_INDEX_SLOT = 0
+KVEPI_INDEX_BATCH = 1
+KVEPI_INDEX_BLOCK = 2
+KVEPI_INDEX_BATCH_START = 3
+
 
 class KvepiError(RuntimeError):
     def __init__(self, status: int, where: str):
@@ -40,6 +47,11 @@ class kvepi_cache(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("block_num", ctypes.c_int64),
                 ("block_size", ctypes.c_int64), ("head_dim", ctypes.c_int64),
                 ("block_stride", ctypes.c_int64)]
+
+
+class kvepi_options(ctypes.Structure):
+    _fields_ = [("x_dtype", ctypes.c_int32), ("index_mode", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -63,6 +75,13 @@ def lib() -> ctypes.CDLL:
         L.kvepi_run.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F, P,
                                 ctypes.c_uint64, P]
         L.kvepi_run.restype = ctypes.c_int
+        OP = ctypes.POINTER(kvepi_options)
+        L.kvepi_get_workspace_ex.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F,
+                                             OP, P]
+        L.kvepi_get_workspace_ex.restype = ctypes.c_int
+        L.kvepi_run_ex.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F, OP, P,
+                                   ctypes.c_uint64, P]
+        L.kvepi_run_ex.restype = ctypes.c_int
         L.kvepi_status_str.argtypes = [ctypes.c_int]
         L.kvepi_status_str.restype = ctypes.c_char_p
         L.kvepi_version.argtypes = []
@@ -98,7 +117,7 @@ def _ptr(t) -> Optional[int]:
 def _x_view(x):
     """x [..., d] -> (ptr, T, d, row_stride) without copying."""
     if x.dim() < 1 or x.element_size() != 2:
-        raise ValueError("x must be a 16-bit (bf16) tensor")
+        raise ValueError("x must be a 16-bit (bf16 or fp16) tensor")
     d = x.shape[-1]
     if x.stride(-1) != 1:
         raise ValueError("x rows must be contiguous")
@@ -122,9 +141,12 @@ def cache_desc(cache) -> kvepi_cache:
                        cache.stride(0))
 
 
-def _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin, cache_aux, eps):
+def _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin, cache_aux, eps,
+          index_mode=KVEPI_INDEX_SLOT):
     xp, T, d, xs = _x_view(x)
-    if slot_mapping.numel() != T:
+    # one entry per token in the SLOT and BATCH index modes (the other modes'
+    # array lengths follow from seq_len and the block size)
+    if index_mode in (KVEPI_INDEX_SLOT, KVEPI_INDEX_BATCH) and slot_mapping.numel() != T:
         raise ValueError("slot_mapping must have one entry per token row")
     if slot_mapping.element_size() != 4 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int32 tensor")
@@ -138,13 +160,24 @@ def _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin, cache
             int(quant_mode), int(group_size), ctypes.c_float(eps)), (c, a)
 
 
+def _options(x, index_mode: int, seq_len: int) -> kvepi_options:
+    """x's dtype (fp16 or the bf16 default) and the index mode."""
+    import torch
+    return kvepi_options(KVEPI_X_FP16 if x.dtype == torch.float16 else KVEPI_X_BF16,
+                         int(index_mode), int(seq_len))
+
+
 def kvepi_get_workspace(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
                         gamma=None, cos=None, sin=None, cache_aux=None,
-                        eps: float = 1e-6) -> int:
+                        eps: float = 1e-6, index_mode: int = KVEPI_INDEX_SLOT,
+                        seq_len: int = 0) -> int:
+    """Stage one.  x may be bf16 or (indexer modes) fp16; index_mode and
+    seq_len select how slot_mapping places the tokens (see kvepi_options)."""
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
-                        cache_aux, eps)
+                        cache_aux, eps, index_mode)
+    opt = _options(x, index_mode, seq_len)
     ws = ctypes.c_uint64()
-    st = lib().kvepi_get_workspace(*args, ctypes.byref(ws))
+    st = lib().kvepi_get_workspace_ex(*args, ctypes.byref(opt), ctypes.byref(ws))
     if st != KVEPI_OK:
         raise KvepiError(st, "kvepi_get_workspace")
     return ws.value
@@ -152,16 +185,21 @@ def kvepi_get_workspace(x, slot_mapping, cache, quant_mode: int, group_size: int
 
 def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
               gamma=None, cos=None, sin=None, cache_aux=None, eps: float = 1e-6,
+              index_mode: int = KVEPI_INDEX_SLOT, seq_len: int = 0,
               workspace=None, stream=None) -> None:
     """Enqueue the epilog on `stream` (a torch.cuda.Stream; default: torch's
-    current stream).  Updates cache / cache_aux in place, asynchronously."""
+    current stream).  Updates cache / cache_aux in place, asynchronously.
+    x may be bf16 or (indexer modes) fp16; index_mode and seq_len select how
+    slot_mapping places the tokens (see kvepi_options)."""
     import torch
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
-                        cache_aux, eps)
+                        cache_aux, eps, index_mode)
+    opt = _options(x, index_mode, seq_len)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     ws_ptr = None if workspace is None else _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().kvepi_run(*args, ws_ptr, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+    st = lib().kvepi_run_ex(*args, ctypes.byref(opt), ws_ptr, ws_bytes,
+                            ctypes.c_void_p(stream.cuda_stream))
     if st != KVEPI_OK:
         raise KvepiError(st, "kvepi_run")

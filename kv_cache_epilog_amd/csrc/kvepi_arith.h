@@ -44,6 +44,16 @@ __device__ __forceinline__ float sqrt_rn(float x) {
   return rp > 0.0f ? sp : r;
 }
 
+// The fp16 halves of a 32-bit word as fp32 (exact; v_cvt_f32_f16, which
+// keeps fp16 subnormals: tests/hw_check.hip compares it with a bit-level
+// decode of every pattern).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
 // max(|a|, |b|, |c|) in one instruction (the compiler's fmaxf chain adds
 // canonicalisations for inputs it cannot prove to be canonical).
 __device__ __forceinline__ float max3_abs(float a, float b, float c) {

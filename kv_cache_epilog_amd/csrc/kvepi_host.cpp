@@ -102,8 +102,13 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
                             const int32_t *slot_mapping,
                             const kvepi_cache *cache,
                             const kvepi_cache *cache_aux, int32_t quant_mode,
-                            int32_t group_size, float eps, kvepi_plan *p) {
+                            int32_t group_size, float eps, const kvepi_options *opt,
+                            kvepi_plan *p) {
   if (quant_mode == KVEPI_MODE_HIF8_FP4) return KVEPI_ERR_UNSUPPORTED;
+  const kvepi_options o = opt != nullptr ? *opt : kvepi_options{0, 0, 0};
+  if (o.x_dtype != KVEPI_X_BF16 && o.x_dtype != KVEPI_X_FP16) return KVEPI_ERR_PARAM;
+  if (o.index_mode < KVEPI_INDEX_SLOT || o.index_mode > KVEPI_INDEX_BATCH_START)
+    return KVEPI_ERR_PARAM;
   int64_t cc = 0, kc = 0, sc = 0;
   kvepi_status st = row_geometry(quant_mode, d, group_size, &cc, &kc, &sc);
   if (st != KVEPI_OK) return st;
@@ -124,6 +129,11 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
   const bool indexer = quant_mode == KVEPI_MODE_MXFP4 || quant_mode == KVEPI_MODE_MXFP8 ||
                        quant_mode == KVEPI_MODE_FP8_ROW;
   if (indexer && (has_norm || has_rope)) return KVEPI_ERR_UNSUPPORTED;
+  if (o.x_dtype == KVEPI_X_FP16 && !indexer) return KVEPI_ERR_UNSUPPORTED;
+  // batch-major tokens for the index modes other than SLOT
+  if (o.index_mode != KVEPI_INDEX_SLOT &&
+      (o.seq_len < 1 || o.seq_len > INT32_MAX || num_tokens % o.seq_len != 0))
+    return KVEPI_ERR_SHAPE;
   if (quant_mode == KVEPI_MODE_BF16_SPLIT && (!has_norm || !has_rope))
     return KVEPI_ERR_PARAM;
   if (has_norm && (!isfinite(eps) || eps < 0.0f)) return KVEPI_ERR_PARAM;
@@ -149,11 +159,20 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
         cache_aux->block_size != cache->block_size)
       return KVEPI_ERR_SHAPE;
   }
+  if (o.index_mode == KVEPI_INDEX_BATCH || o.index_mode == KVEPI_INDEX_BATCH_START) {
+    // batch b owns block b: Bcache >= B
+    if (num_tokens / o.seq_len > cache->block_num) return KVEPI_ERR_SHAPE;
+    if (o.index_mode == KVEPI_INDEX_BATCH_START && o.seq_len > cache->block_size)
+      return KVEPI_ERR_SHAPE;
+  }
 
   if (p != nullptr) {
     q.mode = quant_mode;
     q.norm = has_norm;
     q.rope = has_rope;
+    q.x_fp16 = o.x_dtype == KVEPI_X_FP16;
+    q.index_mode = o.index_mode;
+    q.seq_len = o.index_mode == KVEPI_INDEX_SLOT ? 0 : o.seq_len;
     q.T = num_tokens;
     q.d = d;
     q.nope = indexer ? d : d - 64;
@@ -191,6 +210,44 @@ kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t group_size,
   return KVEPI_OK;
 }
 
+kvepi_status kvepi_get_workspace_ex(const void *x, int64_t num_tokens, int64_t d,
+                                    int64_t x_row_stride, const void *gamma,
+                                    const void *cos, const void *sin,
+                                    const int32_t *slot_mapping,
+                                    const kvepi_cache *cache,
+                                    const kvepi_cache *cache_aux,
+                                    int32_t quant_mode, int32_t group_size,
+                                    float eps, const kvepi_options *options,
+                                    uint64_t *workspace_bytes) {
+  if (workspace_bytes == nullptr) return KVEPI_ERR_NULLPTR;
+  kvepi_status st =
+      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
+                     slot_mapping, cache, cache_aux, quant_mode, group_size,
+                     eps, options, nullptr);
+  if (st != KVEPI_OK) return st;
+  *workspace_bytes = 0;
+  return KVEPI_OK;
+}
+
+kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d,
+                          int64_t x_row_stride, const void *gamma,
+                          const void *cos, const void *sin,
+                          const int32_t *slot_mapping, const kvepi_cache *cache,
+                          const kvepi_cache *cache_aux, int32_t quant_mode,
+                          int32_t group_size, float eps, const kvepi_options *options,
+                          void *workspace, uint64_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;  // the epilog needs no workspace (size 0)
+  kvepi_plan plan;
+  kvepi_status st =
+      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
+                     slot_mapping, cache, cache_aux, quant_mode, group_size,
+                     eps, options, &plan);
+  if (st != KVEPI_OK) return st;
+  if (plan.T == 0) return KVEPI_OK;
+  return kvepi_launch(plan, stream);
+}
+
 kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, int64_t d,
                                  int64_t x_row_stride, const void *gamma,
                                  const void *cos, const void *sin,
@@ -199,14 +256,9 @@ kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, int64_t d,
                                  const kvepi_cache *cache_aux,
                                  int32_t quant_mode, int32_t group_size,
                                  float eps, uint64_t *workspace_bytes) {
-  if (workspace_bytes == nullptr) return KVEPI_ERR_NULLPTR;
-  kvepi_status st =
-      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
-                     slot_mapping, cache, cache_aux, quant_mode, group_size,
-                     eps, nullptr);
-  if (st != KVEPI_OK) return st;
-  *workspace_bytes = 0;
-  return KVEPI_OK;
+  return kvepi_get_workspace_ex(x, num_tokens, d, x_row_stride, gamma, cos, sin, slot_mapping,
+                                cache, cache_aux, quant_mode, group_size, eps, nullptr,
+                                workspace_bytes);
 }
 
 kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
@@ -216,16 +268,9 @@ kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
                        const kvepi_cache *cache_aux, int32_t quant_mode,
                        int32_t group_size, float eps, void *workspace,
                        uint64_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;  // the epilog needs no workspace (size 0)
-  kvepi_plan plan;
-  kvepi_status st =
-      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
-                     slot_mapping, cache, cache_aux, quant_mode, group_size,
-                     eps, &plan);
-  if (st != KVEPI_OK) return st;
-  if (plan.T == 0) return KVEPI_OK;
-  return kvepi_launch(plan, stream);
+  return kvepi_run_ex(x, num_tokens, d, x_row_stride, gamma, cos, sin, slot_mapping, cache,
+                      cache_aux, quant_mode, group_size, eps, nullptr, workspace,
+                      workspace_bytes, stream);
 }
 
 const char *kvepi_status_str(kvepi_status s) {

@@ -72,6 +72,11 @@ struct KArgs {
   int32_t c_align, a_align;
   float eps, inv_nseg;  // inv_nseg != 0: nseg is a power of two, mean = ss*inv
   float nseg_f;
+  int32_t index_mode;  // KVEPI_INDEX_*: how a token's cache row is found
+  int32_t seq_len;     // tokens per batch (index modes other than SLOT)
+  uint64_t sq_magic;   // row / seq_len == (row * sq_magic) >> sq_shift
+  int32_t sq_shift;
+  int32_t n_chunk_b;   // index entries per batch in the block-index mode
   int32_t nwaves;      // waves in the grid
   int32_t n_groups;    // row groups (wave-iterations) = ceil(T / rows per wave)
   int32_t xcd_blocks;  // blocks per XCD for the XCD-major remap, 0 = off
@@ -226,11 +231,27 @@ __device__ __forceinline__ void gamma8(const float4 *g_lds, int e, float (&g)[8]
   g[4] = hi.x; g[5] = hi.y; g[6] = hi.z; g[7] = hi.w;
 }
 
+// the same for fp16 rows (XF16) or bf16 rows
+template <bool XF16>
+__device__ __forceinline__ void unpack8x(const uint4 w, float (&v)[8]);
+
 __device__ __forceinline__ void unpack8(const uint4 w, float (&v)[8]) {
   v[0] = lo_f(w.x); v[1] = hi_f(w.x);
   v[2] = lo_f(w.y); v[3] = hi_f(w.y);
   v[4] = lo_f(w.z); v[5] = hi_f(w.z);
   v[6] = lo_f(w.w); v[7] = hi_f(w.w);
+}
+
+template <bool XF16>
+__device__ __forceinline__ void unpack8x(const uint4 w, float (&v)[8]) {
+  if constexpr (XF16) {
+    v[0] = f16_lo(w.x); v[1] = f16_hi(w.x);
+    v[2] = f16_lo(w.y); v[3] = f16_hi(w.y);
+    v[4] = f16_lo(w.z); v[5] = f16_hi(w.z);
+    v[6] = f16_lo(w.w); v[7] = f16_hi(w.w);
+  } else {
+    unpack8(w, v);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -371,7 +392,7 @@ __device__ __forceinline__ float div448_fast(float m) {
   return __builtin_fmaf(m, H448, m * L448);
 }
 
-template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
+template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST, bool XF16>
 __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
                                             const RowBuf<MODE, ROPE, L, C> &b,
                                             const float4 *g_lds, RowOut<MODE, L, C> &o) {
@@ -490,7 +511,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
-      unpack8(yw[j], v);
+      unpack8x<XF16>(yw[j], v);
       float m = amax8(v);
       m = grp_max<4>(m);  // 32 values = 4 lanes
       const int E = e8m0_exp<2, 0x400000u>(m);  // FP4 max 6 = 1.5 * 2^2
@@ -514,7 +535,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
-      unpack8(yw[j], v);
+      unpack8x<XF16>(yw[j], v);
       const float m = grp_max<4>(amax8(v));  // 32 values = 4 lanes
       const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
       uint32_t cw[2];
@@ -533,7 +554,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
-      unpack8(yw[j], v);
+      unpack8x<XF16>(yw[j], v);
       m = __builtin_fmaxf(m, amax8(v));
     }
     m = grp_max<L>(m);
@@ -543,7 +564,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
-      unpack8(yw[j], v);
+      unpack8x<XF16>(yw[j], v);
       uint32_t cw[2];
       if (fastq) {
         float q[8];
@@ -757,8 +778,9 @@ struct IterInfo {
   uint32_t own;    // (R > 2) slot of the lane's own row, per lane
 };
 
-template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST>
+template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST, bool XF16 = false>
 __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
+  static_assert(!XF16 || whole_row(MODE), "fp16 rows: indexer modes");
   constexpr int R = 64 / L;  // rows per wave-iteration
   static_assert(FAST != 2 || (R <= 2 && max_row_bytes(L, C) <= 1024), "staged rows");
   const int lane = threadIdx.x & 63;
@@ -787,13 +809,42 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   const int n_it = (a.n_groups - wave + a.nwaves - 1) / a.nwaves;
   const uint32_t ns = (uint32_t)a.num_slots;
 
+  // Slot of token row r < T from the index array; 0xFFFFFFFF (past every
+  // slot) skips the token.  SLOT: index[r]; the other modes first split r
+  // into batch b and position s (r = b * seq_len + s).
+  //  BATCH:       row index[r] of batch b's rows (b * block_size ...);
+  //  BLOCK:       entry b * n_chunk_b + s / block_size names the block, the
+  //               row in it is s % block_size;
+  //  BATCH_START: row index[b] + s of batch b's rows.
+  auto token_slot = [&](uint32_t r) -> uint32_t {
+    const uint32_t bs = (uint32_t)a.block_size;
+    auto blk_of = [&](uint32_t v) -> uint32_t {
+      return a.bs_log2 >= 0 ? v >> a.bs_log2 : (uint32_t)(((uint64_t)v * a.bs_magic) >> a.bs_shift);
+    };
+    const uint32_t b = (uint32_t)(((uint64_t)r * a.sq_magic) >> a.sq_shift);
+    const uint32_t s = r - b * (uint32_t)a.seq_len;
+    if (a.index_mode == KVEPI_INDEX_BATCH) {
+      const uint32_t v = (uint32_t)a.slots[r];
+      return v < bs ? b * bs + v : 0xFFFFFFFFu;
+    }
+    if (a.index_mode == KVEPI_INDEX_BLOCK) {
+      const uint32_t c = blk_of(s);
+      const uint32_t v = (uint32_t)a.slots[b * (uint32_t)a.n_chunk_b + c];
+      return v < ns ? blk_of(v) * bs + (s - c * bs) : 0xFFFFFFFFu;
+    }
+    const uint32_t v = (uint32_t)a.slots[b];  // KVEPI_INDEX_BATCH_START
+    return v < bs && v + s < bs ? b * bs + v + s : 0xFFFFFFFFu;
+  };
   // Slots come in windows of L iterations: lane l of window w holds the
   // slot of row sub = l % R of iteration j = w * L + l / R.  Lanes past the
   // wave's rows read slot 0 (their value is never used).
   auto win_load = [&](int w) -> int {
     const int j = w * L + lane / R;
     const int64_t r = ((int64_t)wave + (int64_t)j * a.nwaves) * R + lane % R;
-    return __builtin_nontemporal_load(a.slots + (j < n_it && r < a.T ? r : 0));
+    const bool in = j < n_it && r < a.T;
+    if (a.index_mode == KVEPI_INDEX_SLOT)
+      return __builtin_nontemporal_load(a.slots + (in ? r : 0));
+    return in ? (int)token_slot((uint32_t)r) : 0;
   };
   // iteration j's rows, from the window holding it
   // (32-bit row arithmetic: for j < n_it every row index is below T + R)
@@ -842,7 +893,7 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   RowOut<MODE, L, C> out;
   auto compute = [&](const IterInfo<R> &t, const RowBuf<MODE, ROPE, L, C> &b) {
     if (lane_live(t)) {
-      compute_row<MODE, NORM, ROPE, L, C, FAST>(a, li, sub, b, g_lds, out);
+      compute_row<MODE, NORM, ROPE, L, C, FAST, XF16>(a, li, sub, b, g_lds, out);
       if constexpr (FAST == 2) stage_write<MODE, L, C>(a, li, sub, out, stage);
     }
   };
@@ -950,20 +1001,30 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
 // ------------------------------------------------------------------------
 typedef void (*kfn_t)(const KArgs);
 
-template <int MODE, bool NORM, bool ROPE, int FAST>
+template <int MODE, bool NORM, bool ROPE, int FAST, bool XF16 = false>
 kfn_t pick_layout_f(int L, int C) {
-  if (L == 8) return epilog_kernel<MODE, NORM, ROPE, 8, 1, FAST>;
-  if (L == 16) return epilog_kernel<MODE, NORM, ROPE, 16, 1, FAST>;
+  if (L == 8) return epilog_kernel<MODE, NORM, ROPE, 8, 1, FAST, XF16>;
+  if (L == 16) return epilog_kernel<MODE, NORM, ROPE, 16, 1, FAST, XF16>;
   if (L == 32)
-    return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1, FAST>
-                  : epilog_kernel<MODE, NORM, ROPE, 32, 2, FAST>;
+    return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1, FAST, XF16>
+                  : epilog_kernel<MODE, NORM, ROPE, 32, 2, FAST, XF16>;
   switch (C) {
-    case 1: return epilog_kernel<MODE, NORM, ROPE, 64, 1, FAST>;
-    case 2: return epilog_kernel<MODE, NORM, ROPE, 64, 2, FAST>;
-    case 4: return epilog_kernel<MODE, NORM, ROPE, 64, 4, FAST>;
-    case 8: return epilog_kernel<MODE, NORM, ROPE, 64, 8, FAST>;
-    default: return epilog_kernel<MODE, NORM, ROPE, 64, 16, FAST>;
+    case 1: return epilog_kernel<MODE, NORM, ROPE, 64, 1, FAST, XF16>;
+    case 2: return epilog_kernel<MODE, NORM, ROPE, 64, 2, FAST, XF16>;
+    case 4: return epilog_kernel<MODE, NORM, ROPE, 64, 4, FAST, XF16>;
+    case 8: return epilog_kernel<MODE, NORM, ROPE, 64, 8, FAST, XF16>;
+    default: return epilog_kernel<MODE, NORM, ROPE, 64, 16, FAST, XF16>;
   }
+}
+
+// indexer modes: bf16 or fp16 rows
+template <int MODE>
+kfn_t pick_indexer(int L, int C, int fast, bool xf16) {
+  if (xf16)
+    return fast ? pick_layout_f<MODE, false, false, 1, true>(L, C)
+                : pick_layout_f<MODE, false, false, 0, true>(L, C);
+  return fast ? pick_layout_f<MODE, false, false, 1>(L, C)
+              : pick_layout_f<MODE, false, false, 0>(L, C);
 }
 
 template <int MODE, bool NORM, bool ROPE>
@@ -976,7 +1037,7 @@ kfn_t pick_layout(int L, int C, int fast) {
               : pick_layout_f<MODE, NORM, ROPE, 0>(L, C);
 }
 
-kfn_t pick(int mode, bool norm, bool rope, int L, int C, int fast) {
+kfn_t pick(int mode, bool norm, bool rope, bool xf16, int L, int C, int fast) {
   switch (mode) {
     case M_FP8_BF16:
       if (norm)
@@ -991,11 +1052,11 @@ kfn_t pick(int mode, bool norm, bool rope, int L, int C, int fast) {
       return rope ? pick_layout<M_FP8_E8M0, false, true>(L, C, fast)
                   : pick_layout<M_FP8_E8M0, false, false>(L, C, fast);
     case M_MXFP4:
-      return pick_layout<M_MXFP4, false, false>(L, C, fast);
+      return pick_indexer<M_MXFP4>(L, C, fast, xf16);
     case M_MXFP8:
-      return pick_layout<M_MXFP8, false, false>(L, C, fast);
+      return pick_indexer<M_MXFP8>(L, C, fast, xf16);
     case M_FP8_ROW:
-      return pick_layout<M_FP8_ROW, false, false>(L, C, fast);
+      return pick_indexer<M_FP8_ROW>(L, C, fast, xf16);
     default:
       return pick_layout<M_SPLIT, true, true>(L, C, fast);
   }
@@ -1068,6 +1129,17 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   a.block_size = (int32_t)p.block_size;
   a.bs_log2 = (INT64_C(1) << l) == p.block_size ? l : -1;
   a.T = (int32_t)p.T;
+  a.index_mode = p.index_mode;
+  a.seq_len = p.index_mode == KVEPI_INDEX_SLOT ? 1 : (int32_t)p.seq_len;
+  {
+    // row / seq_len for row < 2^31, as for the block size below
+    int ls = 0;
+    while ((INT64_C(1) << ls) < a.seq_len) ++ls;
+    const unsigned __int128 n2 = (unsigned __int128)1 << (31 + ls);
+    a.sq_magic = (uint64_t)((n2 + (unsigned __int128)a.seq_len - 1) / (unsigned __int128)a.seq_len);
+    a.sq_shift = 31 + ls;
+  }
+  a.n_chunk_b = (int32_t)((a.seq_len + p.block_size - 1) / p.block_size);
   a.num_slots = (int32_t)p.num_slots;
   a.nseg = (int32_t)p.nope;
   a.nchunk = (int32_t)(p.nope / 8);
@@ -1099,7 +1171,7 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   const bool aligned = L * C == a.nchunk && a.c_align >= 16 &&
                        (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
   const int fast = !aligned ? 0 : (p.mode == KVEPI_MODE_FP8_BF16SCALE && L == 32) ? 2 : 1;
-  kfn_t fn = pick(p.mode, p.norm, p.rope, L, C, fast);
+  kfn_t fn = pick(p.mode, p.norm, p.rope, p.x_fp16, L, C, fast);
   size_t lds = p.norm ? (size_t)L * C * 32 : 0;  // gamma as fp32, 32 KB at most
   if (fast == 2) lds += (size_t)4 * (64 / L) * p.kv_cache_col;  // staging, 4 waves
 

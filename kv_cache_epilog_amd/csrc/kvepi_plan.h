@@ -11,6 +11,9 @@ struct kvepi_plan {
   int32_t mode;  // KVEPI_MODE_*
   bool norm;     // gamma given
   bool rope;     // cos/sin given
+  bool x_fp16;   // x holds fp16 values (indexer modes)
+  int32_t index_mode;  // KVEPI_INDEX_*
+  int64_t seq_len;     // tokens per batch (index modes other than SLOT)
   int64_t T, d, nope, x_stride;
   const uint16_t *x, *gamma, *cos, *sin;
   const int32_t *slots;
@@ -34,7 +37,8 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
                             const int32_t *slot_mapping,
                             const kvepi_cache *cache,
                             const kvepi_cache *cache_aux, int32_t quant_mode,
-                            int32_t group_size, float eps, kvepi_plan *plan);
+                            int32_t group_size, float eps, const kvepi_options *options,
+                            kvepi_plan *plan);
 
 // Enqueue the kernel for a validated plan (T > 0).
 kvepi_status kvepi_launch(const kvepi_plan &plan, void *stream);

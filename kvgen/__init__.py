@@ -89,6 +89,9 @@ class Workload:
     aux: Optional[CacheSpec] = None
     aux_init: Optional[np.ndarray] = None
     notes: dict = field(default_factory=dict)
+    x_fp16: bool = False   # x holds fp16 bits (indexer modes)
+    index_mode: int = 0    # 0: slots holds one slot per token; 1-3: see below
+    seq_len: int = 0       # tokens per batch for index modes 1-3
 
     @property
     def hits(self) -> int:
@@ -107,6 +110,45 @@ def slot_mapping(rng, T: int, num_slots: int, skip_frac: float = 0.0,
     if k:
         s[rng.choice(T, size=k, replace=False)] = -1
     return s
+
+
+def to_fp16(a) -> np.ndarray:
+    """fp16 bit patterns of float values (numpy's round to nearest even)."""
+    return np.asarray(a, np.float64).astype(np.float16).view(np.uint16)
+
+
+def fp16_rows(rng, T: int, d: int, row_sigma: float = 0.0) -> np.ndarray:
+    """fp16 x ~ N(0,1) * per-row lognormal(0, row_sigma), clipped to the
+    finite fp16 range."""
+    x = rng.standard_normal((T, d))
+    if row_sigma > 0:
+        x *= rng.lognormal(0.0, row_sigma, size=(T, 1))
+    return to_fp16(np.clip(x, -65504.0, 65504.0))
+
+
+def index_array(rng, index_mode: int, B: int, S: int, block_num: int, block_size: int,
+                skip_frac: float = 0.0) -> np.ndarray:
+    """A valid index array for the batch-major index modes (tokens b*S + s):
+    1 (per-batch rows): index[b, s] a random choice of distinct rows < block_size;
+    2 (per-chunk blocks): one distinct block per chunk of block_size tokens,
+      at a random row of it; 3 (per-batch start): index[b] in [0, block_size - S].
+    round(skip_frac * len) entries are set to -1."""
+    if index_mode == 1:
+        assert S <= block_size and B <= block_num
+        idx = np.concatenate([rng.permutation(block_size)[:S] for _ in range(B)])
+    elif index_mode == 2:
+        nc = -(-S // block_size)
+        assert B * nc <= block_num
+        blk = rng.permutation(block_num)[:B * nc]
+        idx = blk * block_size + rng.integers(0, block_size, blk.size)
+    else:
+        assert S <= block_size and B <= block_num
+        idx = rng.integers(0, block_size - S + 1, B)
+    idx = idx.astype(np.int32)
+    k = int(round(skip_frac * idx.size))
+    if k:
+        idx[rng.choice(idx.size, size=k, replace=False)] = -1
+    return idx
 
 
 def rope_tables(rng, T: int, max_pos: int, theta: float = 10000.0, dk: int = 64):

@@ -21,6 +21,8 @@
  *  3. m / 448 for bf16 m, from the constants H = RN(1/448), Lo = RN(1/448 - H):
  *       q = fma(m, H, m*Lo)
  *     must equal the IEEE quotient for every bf16 m in [2^-71, 2^100].
+ *  4. the same for every positive finite fp16 m (fp16 rows of the indexer's
+ *     fp8 mode; all of them lie in [2^-24, 65504], inside that range).
  * Prints the number of mismatches of each part and exits non-zero if any.
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math fastdiv_check.c -lm
  */
@@ -85,8 +87,18 @@ int main(void) {
       if (q != m / 448.0f) ++bad3;
     }
   }
+  /* 4: fp16 m / 448, m decoded from its fields (exponent 0: f * 2^-24) */
+  long long bad4 = 0, n4 = 0;
+  for (uint32_t h = 1; h < 0x7C00u; ++h) {
+    const uint32_t e = h >> 10, f = h & 0x3FFu;
+    const float m = e == 0 ? ldexpf((float)f, -24) : ldexpf((float)(1024 + f), (int)e - 25);
+    const float q = fmaf(m, H, m * Lo);
+    ++n4;
+    if (q != m / 448.0f) ++bad4;
+  }
   printf("markstein x/r: %lld of %lld differ\n", bad1, n1);
   printf("bf16/bf16 double reciprocal: %lld of %lld differ\n", bad2, n2);
   printf("m/448 double constant: %lld of %lld differ\n", bad3, n3);
-  return (bad1 || bad2 || bad3) ? 1 : 0;
+  printf("fp16 m/448 double constant: %lld of %lld differ\n", bad4, n4);
+  return (bad1 || bad2 || bad3 || bad4) ? 1 : 0;
 }

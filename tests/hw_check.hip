@@ -11,6 +11,12 @@
 //           bf16 v with |v / 2^E| <= 448, E in [-100, 100]
 //   fp4s    v_cvt_scalef32_pk_fp4_f32(v, 2^E) == E2M1 encoder of v / 2^E, every
 //           bf16 v with |v / 2^E| <= 6, E in [-100, 100]
+//   f16     f16_lo / f16_hi (v_cvt_f32_f16) == a bit-level binary16 decode, every
+//           pattern
+//   fp8s16, fp4s16  the scaled converts as above, every fp16 v
+//   div16   div_fast(a, b, rcp_rn(b)) == a / b for every fp16 significand a
+//           against every fp32 significand b (quotient in (1/2, 2); exponents
+//           are a pure scaling while the quotient stays normal)
 // Prints one line per check and exits with status 1 if anything differs.
 // Every launch covers at most 2^28 indices and each thread checks its index
 // against the count; results go to a 64-word counter buffer.
@@ -48,12 +54,51 @@ __global__ void k_fp8(uint32_t base, uint32_t n, unsigned *bad) {
 
 typedef short s16x2_t __attribute__((ext_vector_type(2)));
 
-// index = (E + 100) * 65536 + bf16 bits
-__global__ void k_scaled(uint32_t n, int fp4, unsigned *bad, unsigned *count) {
+// binary16 from its definition: sign, 5-bit exponent (bias 15), 10-bit
+// fraction; exponent 0: f * 2^-24; exponent 31: infinity or NaN
+__device__ float f16_ref(uint32_t h) {
+  const uint32_t e = (h >> 10) & 0x1Fu, f = h & 0x3FFu;
+  float mag;
+  if (e == 0)
+    mag = (float)f * 0x1p-24f;
+  else if (e == 31)
+    mag = f == 0 ? __builtin_inff() : __builtin_nanf("");
+  else
+    mag = __uint_as_float((e + 112u) << 23 | f << 13);
+  return (h & 0x8000u) ? -mag : mag;
+}
+
+__global__ void k_f16(uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = i | ((i ^ 0x5A5Au) << 16);
+  const float lo = f16_lo(w), hi = f16_hi(w);
+  const float rl = f16_ref(i), rh = f16_ref(i ^ 0x5A5Au);
+  const bool ok_lo = (lo != lo && rl != rl) || __float_as_uint(lo) == __float_as_uint(rl);
+  const bool ok_hi = (hi != hi && rh != rh) || __float_as_uint(hi) == __float_as_uint(rh);
+  if (!ok_lo || !ok_hi) atomicAdd(bad, 1u);
+}
+
+// one fp32 divisor significand per thread, every fp16 numerator significand
+__global__ void k_div16(uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float b = __uint_as_float(0x3F800000u | i);
+  const float y = rcp_rn(b);
+  unsigned nb = 0;
+  for (uint32_t m = 0; m < 1024; ++m) {
+    const float a = __uint_as_float(0x3F800000u | (m << 13));
+    if (div_fast(a, b, y) != a / b) ++nb;
+  }
+  if (nb) atomicAdd(bad, nb);
+}
+
+// index = (E + 100) * 65536 + bf16 (or fp16) bits
+__global__ void k_scaled(uint32_t n, int fp4, int f16, unsigned *bad, unsigned *count) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int E = (int)(i >> 16) - 100;
-  const float v = __uint_as_float((i & 0xFFFFu) << 16);
+  const float v = f16 ? f16_lo(i & 0xFFFFu) : __uint_as_float((i & 0xFFFFu) << 16);
   const float f = exp2_neg(E);
   const float q = v * f;  // exact: a power-of-two scaling of a bf16 value
   const float lim = fp4 ? 6.0f : 448.0f;
@@ -90,10 +135,16 @@ int main() {
   launch_range(k_sqrt, 0x0F800000u, 0x7F000000u, d + 1);      // [2^-96, 2^127]
   launch_range(k_fp8, 0x00000000u, 0x43E40000u, d + 2);       // [0, 456]
   const uint32_t n_sc = 201u << 16;
-  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 0, d + 3, d + 4);
-  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 1, d + 5, d + 6);
+  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 0, 0, d + 3, d + 4);
+  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 1, 0, d + 5, d + 6);
+  hipLaunchKernelGGL(k_f16, dim3(65536 / 256), dim3(256), 0, 0, 65536u, d + 7);
+  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 0, 1, d + 8, d + 9);
+  hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 1, 1, d + 10,
+                     d + 11);
+  const uint32_t n_div = 1u << 23;
+  hipLaunchKernelGGL(k_div16, dim3(n_div / 256), dim3(256), 0, 0, n_div, d + 12);
   const hipError_t e = hipDeviceSynchronize();
-  unsigned h[7] = {0};
+  unsigned h[13] = {0};
   (void)hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
   (void)hipFree(d);
   if (e != hipSuccess) {
@@ -105,5 +156,9 @@ int main() {
   printf("fp8: %u mismatches of %u\n", h[2], 0x43E40000u + 1u);
   printf("fp8s: %u mismatches of %u\n", h[3], h[4]);
   printf("fp4s: %u mismatches of %u\n", h[5], h[6]);
-  return (h[0] | h[1] | h[2] | h[3] | h[5]) ? 1 : 0;
+  printf("f16: %u mismatches of %u\n", h[7], 65536u);
+  printf("fp8s16: %u mismatches of %u\n", h[8], h[9]);
+  printf("fp4s16: %u mismatches of %u\n", h[10], h[11]);
+  printf("div16: %u mismatches of %llu\n", h[12], 1024ull << 23);
+  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12]) ? 1 : 0;
 }

@@ -56,6 +56,8 @@ def run_gpu(w: kvgen.Workload, device="cuda:0", offset: int = 0, aux_offset: int
         x = to_dev_bf16(xb, device)[:, :w.d]
     else:
         x = to_dev_bf16(w.x, device)
+    if w.x_fp16:
+        x = x.view(torch.float16)
     slots = torch.from_numpy(w.slots).to(device)
     gamma = None if w.gamma is None else to_dev_bf16(w.gamma, device)
     cos = None if w.cos is None else to_dev_bf16(w.cos, device)
@@ -64,12 +66,13 @@ def run_gpu(w: kvgen.Workload, device="cuda:0", offset: int = 0, aux_offset: int
     aux = aflat = None
     if w.aux is not None:
         aux, aflat = cache_tensor(w.aux, w.aux_init, device, aux_offset)
+    ix = dict(index_mode=w.index_mode, seq_len=w.seq_len)
     ws = kvepi_get_workspace(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos,
-                             sin=sin, cache_aux=aux, eps=w.eps)
+                             sin=sin, cache_aux=aux, eps=w.eps, **ix)
     assert ws == 0
     for _ in range(repeat):
         kvepi_run(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos, sin=sin,
-                  cache_aux=aux, eps=w.eps, stream=stream)
+                  cache_aux=aux, eps=w.eps, stream=stream, **ix)
     torch.cuda.synchronize()
     got = flat[offset:offset + w.cache.alloc_bytes].cpu().numpy()
     # bytes outside the cache view must be untouched as well
@@ -88,13 +91,23 @@ def run_oracle(w: kvgen.Workload):
     aux = None if w.aux_init is None else w.aux_init.copy()
     oracle.epilog(w.mode, w.x, w.slots, cache, w.cache.geom, group_size=w.group_size,
                   gamma=w.gamma, cos=w.cos, sin=w.sin, eps=w.eps, aux_bytes=aux,
-                  aux_geom=None if w.aux is None else w.aux.geom)
+                  aux_geom=None if w.aux is None else w.aux.geom, x_fp16=w.x_fp16,
+                  index_mode=w.index_mode, seq_len=w.seq_len)
     return cache, aux
+
+
+def token_slots(w: kvgen.Workload) -> np.ndarray:
+    """The slot of every token (-1: skipped) under the workload's index mode."""
+    if w.index_mode == 0:
+        return np.where((w.slots >= 0) & (w.slots < w.cache.num_slots), w.slots, -1)
+    return np.array([oracle.token_slot(w.index_mode, w.slots, t, w.seq_len, w.cache.block_num,
+                                       w.cache.block_size) for t in range(w.T)], np.int64)
 
 
 def _code_positions(w: kvgen.Workload):
     """Byte offsets of quantised codes in the main cache, and their count."""
-    hit = w.slots[(w.slots >= 0) & (w.slots < w.cache.num_slots)].astype(np.int64)
+    ts = token_slots(w)
+    hit = ts[ts >= 0].astype(np.int64)
     if w.mode in (kvgen.MODE_FP8_BF16SCALE, kvgen.MODE_FP8_E8M0):
         ncode = w.d - 64
     elif w.mode == kvgen.MODE_MXFP4:

@@ -23,7 +23,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kvepi_row_bytes", "kvepi_get_workspace", "kvepi_run",
-                          "kvepi_status_str", "kvepi_version"}
+                          "kvepi_get_workspace_ex", "kvepi_run_ex", "kvepi_status_str",
+                          "kvepi_version"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -38,7 +39,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.kvepi_version() == 100
+    assert B.kvepi_version() == 110
     for code, name in B.STATUS_NAMES.items():
         assert B.kvepi_status_str(code).startswith(name)
     assert "UNKNOWN" in B.kvepi_status_str(99)
@@ -195,3 +196,73 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+# ---- options: fp16 rows and index modes ----------------------------------------
+
+def call_ex(stage, opt, **kw):
+    """call() through the _ex entry points with a kvepi_options (or None)."""
+    L = B.lib()
+    x = kw.pop("x", P16)
+    T = kw.pop("T", 64)
+    d = kw.pop("d", 256)
+    cache = kw.pop("cache", _cache())
+    aux = kw.pop("aux", None)
+    mode = kw.pop("mode", 0)
+    group = kw.pop("group", 64)
+    slots = kw.pop("slots", P16B)
+    assert not kw
+    ap = ctypes.byref(aux) if aux is not None else None
+    op = ctypes.byref(opt) if opt is not None else None
+    if stage == 1:
+        ws = ctypes.c_uint64(7)
+        st = L.kvepi_get_workspace_ex(x, T, d, d, None, None, None, slots, ctypes.byref(cache),
+                                      ap, mode, group, ctypes.c_float(1e-6), op,
+                                      ctypes.byref(ws))
+        return st, ws.value
+    st = L.kvepi_run_ex(x, T, d, d, None, None, None, slots, ctypes.byref(cache), ap, mode,
+                        group, ctypes.c_float(1e-6), op, None, 0, None)
+    return st, None
+
+
+def O(x_dtype=0, index_mode=0, seq_len=0):
+    return B.kvepi_options(x_dtype, index_mode, seq_len)
+
+
+def test_ex_valid_calls():
+    assert call_ex(1, None) == (0, 0)
+    assert call_ex(1, O()) == (0, 0)
+    ix = dict(d=128, group=32, cache=_cache(hd=128), aux=_cache(data=0x60000, hd=4))
+    for mode, g in ((3, 32), (5, 32)):
+        kw = dict(ix, mode=mode, group=g)
+        if mode == 3:
+            kw["cache"] = _cache(hd=64)
+        assert call_ex(1, O(x_dtype=1), **kw) == (0, 0)
+    assert call_ex(1, O(x_dtype=1), d=128, mode=6, group=0, cache=_cache(hd=128),
+                   aux=_cache(data=0x60000, hd=1)) == (0, 0)
+    # 64 tokens as 8 batches of 8 (cache of 8 blocks of 16 rows)
+    for im in (1, 2, 3):
+        assert call_ex(1, O(index_mode=im, seq_len=8)) == (0, 0)
+    assert call_ex(1, O(index_mode=2, seq_len=64)) == (0, 0)
+    assert call_ex(1, O(index_mode=1, seq_len=1), T=0, x=None, slots=None) == (0, 0)
+
+
+BAD_EX = [
+    ("unknown x dtype", O(x_dtype=2), {}, 4),
+    ("fp16 in mode 0", O(x_dtype=1), {}, 5),
+    ("unknown index mode", O(index_mode=4), {}, 4),
+    ("negative index mode", O(index_mode=-1), {}, 4),
+    ("batch mode without seq_len", O(index_mode=1), {}, 2),
+    ("seq_len not dividing T", O(index_mode=2, seq_len=7), {}, 2),
+    ("more batches than blocks", O(index_mode=1, seq_len=4), {}, 2),
+    ("batch start longer than a block", O(index_mode=3, seq_len=32), dict(T=64), 2),
+    ("more start batches than blocks", O(index_mode=3, seq_len=2), {}, 2),
+]
+
+
+@pytest.mark.parametrize("desc,opt,kw,status", BAD_EX, ids=[b[0] for b in BAD_EX])
+@pytest.mark.parametrize("stage", [1, 2])
+def test_ex_rejects(desc, opt, kw, status, stage):
+    st, _ = call_ex(stage, opt, **kw)
+    assert st == status, (desc, B.kvepi_status_str(st))
+

@@ -15,4 +15,4 @@ def test_fast_divisions_match_ieee(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     print(r.stdout)
     assert r.returncode == 0, r.stdout
-    assert r.stdout.count(" 0 of ") == 3
+    assert r.stdout.count(" 0 of ") == 4
