@@ -94,6 +94,15 @@ def lib() -> ctypes.CDLL:
                                     P, ctypes.c_int, I64, I32, ctypes.POINTER(_Cache),
                                     ctypes.POINTER(_Cache)]
         L.kvo_epilog_ex.restype = ctypes.c_int
+        L.kvo_f32_to_fp16.argtypes = [F]
+        L.kvo_f32_to_fp16.restype = ctypes.c_uint16
+        L.kvo_quant_int8.argtypes = [F, F, P]
+        L.kvo_quant_int8.restype = ctypes.c_int8
+        L.kvo_drq.argtypes = [I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, I64,
+                              P, P, ctypes.c_int, P, P, P, ctypes.c_int, P, P, P, P, P,
+                              ctypes.c_int, I64, ctypes.POINTER(_Cache), ctypes.POINTER(_Cache),
+                              P, P, P]
+        L.kvo_drq.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -239,3 +248,53 @@ def epilog(mode: int, x, slot_mapping, cache_bytes, cache_geom, *, group_size: i
                              ctypes.byref(a) if a is not None else None)
     if rc != 0:
         raise ValueError("oracle epilog rejected its arguments")
+
+
+# ---- dequant -> RoPE -> int8 KV cache ---------------------------------------------
+
+DT_BF16, DT_FP16, DT_INT32, DT_FP32 = 0, 1, 2, 3
+
+
+def f32_to_fp16(f: float) -> int:
+    return int(lib().kvo_f32_to_fp16(ctypes.c_float(f)))
+
+
+def quant_int8(v: float, scale: float, offset=None) -> int:
+    off = None if offset is None else ctypes.byref(ctypes.c_float(offset))
+    return int(lib().kvo_quant_int8(ctypes.c_float(v), ctypes.c_float(scale), off))
+
+
+def drq(x, x_dtype: int, nq: int, nkv: int, D: int, cos, sin, out_dtype: int, *, scale_k,
+        scale_v, k_cache_bytes, v_cache_bytes, cache_geom, index, index_mode: int = INDEX_SLOT,
+        seq_len: int = 0, weight_scale=None, act_scale=None, bias=None, bias_dtype: int = DT_FP32,
+        offset_k=None, offset_v=None, kv_output: bool = True):
+    """Runs the oracle in place on the two int8 caches (uint8 byte buffers of
+    geometry cache_geom = (block_num, block_size, head_dim, block_stride));
+    returns (q_out, k_out, v_out) as uint16 arrays (k_out / v_out None
+    without kv_output).  x is int32 or uint16 [T, H] (16-bit bit patterns)."""
+    x = np.ascontiguousarray(x)
+    T = x.shape[0]
+    H = (nq + 2 * nkv) * D
+    assert x.shape[1] == H
+    q_out = np.zeros((T, nq * D), np.uint16)
+    k_out = np.zeros((T, nkv * D), np.uint16) if kv_output else None
+    v_out = np.zeros((T, nkv * D), np.uint16) if kv_output else None
+    kc = _Cache(k_cache_bytes.ctypes.data, *[int(v) for v in cache_geom])
+    vc = _Cache(v_cache_bytes.ctypes.data, *[int(v) for v in cache_geom])
+    f32 = lambda a: None if a is None else _c(a, np.float32)  # noqa: E731
+    cos = _c(cos, np.uint16)
+    sin = _c(sin, np.uint16)
+    idx = _c(index, np.int32)
+    ws, act, sk, sv, ok, ov = (f32(a) for a in (weight_scale, act_scale, scale_k, scale_v,
+                                                 offset_k, offset_v))
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias)
+    rc = lib().kvo_drq(T, nq, nkv, D, _ptr(x), x_dtype, H, _ptr(cos), _ptr(sin), out_dtype,
+                       _ptr(ws), _ptr(act), _ptr(b), bias_dtype, _ptr(sk), _ptr(sv), _ptr(ok),
+                       _ptr(ov), _ptr(idx), index_mode, seq_len, ctypes.byref(kc),
+                       ctypes.byref(vc), _ptr(q_out), _ptr(k_out), _ptr(v_out))
+    if rc != 0:
+        raise ValueError("oracle drq rejected its arguments")
+    return q_out, k_out, v_out
+

@@ -50,6 +50,41 @@ float kvo_fp16_to_f32(uint16_t h) {
   return sign ? -mag : mag;
 }
 
+/* Round a binary32 value to binary16, to nearest with ties to the even
+ * significand, overflowing to infinity from 65520 (the midpoint between the
+ * largest finite value 65504 and 2^16).  Written from the definition: the
+ * two binary16 neighbours of |f| are built from its binade (or the
+ * subnormal step 2^-24), compared exactly in binary64. */
+uint16_t kvo_f32_to_fp16(float f) {
+  if (isnan(f)) return 0x7E00u;
+  const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+  const double a = fabs((double)f);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+  uint16_t lo;
+  if (a < ldexp(1.0, -14)) {
+    lo = (uint16_t)floor(a / ldexp(1.0, -24)); /* subnormal count */
+  } else {
+    int e;
+    frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+    e -= 1;       /* a in [2^e, 2^(e+1)) */
+    const double step = ldexp(1.0, e - 10);
+    const int k = (int)floor(a / step); /* 1024 .. 2047 */
+    lo = (uint16_t)(((e + 15) << 10) | (k - 1024));
+  }
+  const uint16_t hi = (uint16_t)(lo + 1u); /* next magnitude (0x7C00 = inf) */
+  const double dlo = fabs((double)kvo_fp16_to_f32(lo));
+  const double dhi = hi == 0x7C00u ? 65536.0 : fabs((double)kvo_fp16_to_f32(hi));
+  const double elo = a - dlo, ehi = dhi - a;
+  uint16_t r;
+  if (elo < ehi)
+    r = lo;
+  else if (ehi < elo)
+    r = hi;
+  else
+    r = (lo & 1u) ? hi : lo;
+  return (uint16_t)(sign | r);
+}
+
 static uint32_t f32_bits(float f) {
   uint32_t u;
   memcpy(&u, &f, 4);
@@ -531,3 +566,116 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
   free(srow);
   return 0;
 }
+
+/* ======================================================================== */
+/* Dequant -> RoPE -> static int8 quantisation -> KV cache (the blog on      */
+/* aclnnDequantRopeQuantKvcache: 计算步骤公式 steps 1-5, 约束说明)           */
+/* ======================================================================== */
+
+static float val16(uint16_t h, int dtype) {
+  return dtype == KVO_DT_FP16 ? kvo_fp16_to_f32(h) : kvo_bf16_to_f32(h);
+}
+static uint16_t round16(float f, int dtype) {
+  return dtype == KVO_DT_FP16 ? kvo_f32_to_fp16(f) : kvo_f32_to_bf16(f);
+}
+
+/* Static int8 quantisation of one value (step 4): v / scale, plus the
+ * offset when there is one, rounded half to even, saturated to [-128, 127]. */
+int8_t kvo_quant_int8(float v, float scale, const float *offset) {
+  float q = v / scale;
+  if (offset) q = q + *offset;
+  const double r = nearbyint((double)q); /* exact: q is a binary32 value */
+  if (r > 127.0) return 127;
+  if (r < -128.0) return -128;
+  return (int8_t)r;
+}
+
+int kvo_drq(int64_t T, int nq, int nkv, int D, const void *x, int x_dtype, int64_t x_row_stride,
+            const uint16_t *cos, const uint16_t *sin, int out_dtype, const float *weight_scale,
+            const float *act_scale, const void *bias, int bias_dtype, const float *scale_k,
+            const float *scale_v, const float *offset_k, const float *offset_v,
+            const int32_t *index, int index_mode, int64_t seq_len, const kvo_cache *k_cache,
+            const kvo_cache *v_cache, uint16_t *q_out, uint16_t *k_out, uint16_t *v_out) {
+  if (nq < 1 || nkv < 1 || D < 2 || D % 2) return -1;
+  if (out_dtype != KVO_DT_BF16 && out_dtype != KVO_DT_FP16) return -1;
+  const int dequant = x_dtype == KVO_DT_INT32;
+  if (!dequant && x_dtype != out_dtype) return -1; /* 约束说明 4 */
+  if (dequant && !weight_scale) return -1;         /* 约束说明 5 */
+  if (!dequant && (weight_scale || act_scale || bias)) return -1;
+  if (index_mode != KVO_INDEX_SLOT && index_mode != KVO_INDEX_BATCH_START) return -1;
+  if (index_mode != KVO_INDEX_SLOT && (seq_len <= 0 || T % seq_len != 0)) return -1;
+  const int64_t H = (int64_t)(nq + 2 * nkv) * D, HK = (int64_t)nkv * D;
+  float *dq = (float *)malloc((size_t)H * sizeof(float));
+  float *ko = (float *)malloc((size_t)HK * sizeof(float));
+  for (int64_t t = 0; t < T; ++t) {
+    /* step 1: dequantX (cast, * weight_scale, * activation scale, + bias),
+     * held in the output dtype like every tensor of the chain */
+    for (int64_t h = 0; h < H; ++h) {
+      float v;
+      if (dequant) {
+        v = (float)((const int32_t *)x)[t * x_row_stride + h];
+        v = v * weight_scale[h];
+        if (act_scale) v = v * act_scale[t];
+        if (bias) {
+          float b;
+          if (bias_dtype == KVO_DT_FP32)
+            b = ((const float *)bias)[h];
+          else if (bias_dtype == KVO_DT_INT32)
+            b = (float)((const int32_t *)bias)[h];
+          else
+            b = val16(((const uint16_t *)bias)[h], bias_dtype);
+          v = v + b;
+        }
+        v = val16(round16(v, out_dtype), out_dtype);
+      } else {
+        v = val16(((const uint16_t *)x)[t * x_row_stride + h], x_dtype);
+      }
+      dq[h] = v;
+    }
+    /* steps 2-3: split into q | k | v heads; rotate-half RoPE of q and k
+     * with the token's cos / sin [D] (each product exact in binary32 for
+     * 16-bit operands, one rounding for the sum, then the output dtype) */
+    const uint16_t *c = cos + t * D, *sn = sin + t * D;
+    for (int h = 0; h < nq + nkv; ++h) {
+      const float *in = dq + (int64_t)h * D;
+      for (int j = 0; j < D / 2; ++j) {
+        const float a = in[j], b = in[j + D / 2];
+        const float y1 = a * val16(c[j], out_dtype) - b * val16(sn[j], out_dtype);
+        const float y2 = b * val16(c[j + D / 2], out_dtype) + a * val16(sn[j + D / 2], out_dtype);
+        const uint16_t r1 = round16(y1, out_dtype), r2 = round16(y2, out_dtype);
+        if (h < nq) {
+          q_out[t * nq * D + (int64_t)h * D + j] = r1;
+          q_out[t * nq * D + (int64_t)h * D + j + D / 2] = r2;
+        } else {
+          const int64_t o = (int64_t)(h - nq) * D;
+          if (k_out) {
+            k_out[t * HK + o + j] = r1;
+            k_out[t * HK + o + j + D / 2] = r2;
+          }
+          ko[o + j] = val16(r1, out_dtype);
+          ko[o + j + D / 2] = val16(r2, out_dtype);
+        }
+      }
+    }
+    const float *vv = dq + (int64_t)(nq + nkv) * D;
+    if (v_out)
+      for (int64_t i = 0; i < HK; ++i) v_out[t * HK + i] = round16(vv[i], out_dtype);
+    /* steps 4-5: static int8 quantisation of kOut and vOut, written to the
+     * token's cache row (-1, or a row outside the cache, skips the write) */
+    const int64_t slot = kvo_token_slot(index_mode, index, t, seq_len, k_cache->block_num,
+                                        k_cache->block_size);
+    if (slot < 0) continue;
+    int8_t *kr = (int8_t *)(k_cache->data + (slot / k_cache->block_size) * k_cache->block_stride +
+                            (slot % k_cache->block_size) * k_cache->head_dim);
+    int8_t *vr = (int8_t *)(v_cache->data + (slot / v_cache->block_size) * v_cache->block_stride +
+                            (slot % v_cache->block_size) * v_cache->head_dim);
+    for (int64_t i = 0; i < HK; ++i) {
+      kr[i] = kvo_quant_int8(ko[i], scale_k[i], offset_k ? offset_k + i : NULL);
+      vr[i] = kvo_quant_int8(vv[i], scale_v[i], offset_v ? offset_v + i : NULL);
+    }
+  }
+  free(dq);
+  free(ko);
+  return 0;
+}
+

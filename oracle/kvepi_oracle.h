@@ -50,6 +50,7 @@ extern "C" {
 /* ---- number formats ---------------------------------------------------- */
 float kvo_bf16_to_f32(uint16_t h);
 float kvo_fp16_to_f32(uint16_t h);     /* IEEE binary16, exact           */
+uint16_t kvo_f32_to_fp16(float f);     /* round to nearest, ties to even   */
 uint16_t kvo_f32_to_bf16(float f);     /* round to nearest, ties to even   */
 uint8_t kvo_enc_e4m3(float v);         /* OCP E4M3FN, RNE, saturate to 448 */
 uint8_t kvo_enc_e2m1(float v);         /* OCP E2M1 nibble, RNE, sat. to 6  */
@@ -119,6 +120,27 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
                   int x_fp16, const uint16_t *gamma, const uint16_t *cos, const uint16_t *sin,
                   float eps, const int32_t *index, int index_mode, int64_t seq_len,
                   int32_t group_size, const kvo_cache *cache, const kvo_cache *aux);
+
+/* ---- dequant -> RoPE -> int8 KV cache ----------------------------------- */
+#define KVO_DT_BF16 0
+#define KVO_DT_FP16 1
+#define KVO_DT_INT32 2
+#define KVO_DT_FP32 3
+int8_t kvo_quant_int8(float v, float scale, const float *offset);
+/* x [T, (nq + 2 nkv) * D] (int32, or bf16 / fp16 equal to out_dtype), cos /
+ * sin [T, D] in out_dtype; weight_scale [H] (int32 x only, required),
+ * act_scale [T], bias [H] of bias_dtype (int32 x only, optional);
+ * scale_k / scale_v / offset_k / offset_v [nkv * D]; index: one slot per
+ * token (KVO_INDEX_SLOT, the page mode) or one start row per batch
+ * (KVO_INDEX_BATCH_START, the contiguous mode); caches int8 with head_dim
+ * nkv * D; q_out [T, nq * D], k_out / v_out [T, nkv * D] (may be NULL) in
+ * out_dtype. */
+int kvo_drq(int64_t T, int nq, int nkv, int D, const void *x, int x_dtype, int64_t x_row_stride,
+            const uint16_t *cos, const uint16_t *sin, int out_dtype, const float *weight_scale,
+            const float *act_scale, const void *bias, int bias_dtype, const float *scale_k,
+            const float *scale_v, const float *offset_k, const float *offset_v,
+            const int32_t *index, int index_mode, int64_t seq_len, const kvo_cache *k_cache,
+            const kvo_cache *v_cache, uint16_t *q_out, uint16_t *k_out, uint16_t *v_out);
 
 #ifdef __cplusplus
 }
