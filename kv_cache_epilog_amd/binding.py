@@ -203,3 +203,86 @@ def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
                             ctypes.c_void_p(stream.cuda_stream))
     if st != KVEPI_OK:
         raise KvepiError(st, "kvepi_run")
+
+
+# ---- dequant -> RoPE -> int8 KV cache (include/kvepi_drq.h) -------------------------
+
+KVEPI_DT_BF16 = 0
+KVEPI_DT_FP16 = 1
+KVEPI_DT_INT32 = 2
+KVEPI_DT_FP32 = 3
+KVEPI_DRQ_PAGE = 0
+KVEPI_DRQ_CONTIGUOUS = 1
+
+
+class kvepi_drq_params(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("num_tokens", ctypes.c_int64),
+                ("x_row_stride", ctypes.c_int64), ("nq", ctypes.c_int32),
+                ("nkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
+                ("weight_scale", ctypes.c_void_p), ("act_scale", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int32),
+                ("scale_k", ctypes.c_void_p), ("scale_v", ctypes.c_void_p),
+                ("offset_k", ctypes.c_void_p), ("offset_v", ctypes.c_void_p),
+                ("indices", ctypes.c_void_p), ("cache_mode", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64), ("k_cache", kvepi_cache),
+                ("v_cache", kvepi_cache), ("q_out", ctypes.c_void_p),
+                ("k_out", ctypes.c_void_p), ("v_out", ctypes.c_void_p)]
+
+
+def _drq_lib():
+    L = lib()
+    if not getattr(L, "_drq_typed", False):
+        PP = ctypes.POINTER(kvepi_drq_params)
+        L.kvepi_drq_get_workspace.argtypes = [PP, ctypes.c_void_p]
+        L.kvepi_drq_get_workspace.restype = ctypes.c_int
+        L.kvepi_drq_run.argtypes = [PP, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        L.kvepi_drq_run.restype = ctypes.c_int
+        L._drq_typed = True
+    return L
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.bfloat16: KVEPI_DT_BF16, torch.float16: KVEPI_DT_FP16,
+            torch.int32: KVEPI_DT_INT32, torch.float32: KVEPI_DT_FP32}[t.dtype]
+
+
+def drq_params(x, cos, sin, k_cache, v_cache, indices, *, nq: int, nkv: int, head_dim: int,
+               scale_k, scale_v, q_out, k_out=None, v_out=None, weight_scale=None,
+               act_scale=None, bias=None, offset_k=None, offset_v=None,
+               cache_mode: int = KVEPI_DRQ_PAGE, seq_len: int = 0) -> kvepi_drq_params:
+    """torch tensors -> kvepi_drq_params (pointers, sizes and dtype codes)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [T, H] with contiguous rows")
+    for name, t in (("cos", cos), ("sin", sin), ("q_out", q_out), ("k_out", k_out),
+                    ("v_out", v_out), ("indices", indices)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return kvepi_drq_params(
+        _ptr(x), _dtype_code(x), _dtype_code(cos), x.shape[0], x.stride(0), nq, nkv, head_dim,
+        _ptr(cos), _ptr(sin), _ptr(weight_scale), _ptr(act_scale), _ptr(bias),
+        KVEPI_DT_FP32 if bias is None else _dtype_code(bias), _ptr(scale_k), _ptr(scale_v),
+        _ptr(offset_k), _ptr(offset_v), _ptr(indices), cache_mode, seq_len,
+        cache_desc(k_cache), cache_desc(v_cache), _ptr(q_out), _ptr(k_out), _ptr(v_out))
+
+
+def kvepi_drq_get_workspace(params: kvepi_drq_params) -> int:
+    ws = ctypes.c_uint64()
+    st = _drq_lib().kvepi_drq_get_workspace(ctypes.byref(params), ctypes.byref(ws))
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_drq_get_workspace")
+    return ws.value
+
+
+def kvepi_drq_run(params: kvepi_drq_params, *, stream=None, device=None) -> None:
+    """Enqueue the dequant -> RoPE -> int8 KV cache operator on `stream`
+    (default: torch's current stream)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    st = _drq_lib().kvepi_drq_run(ctypes.byref(params), None, 0,
+                                  ctypes.c_void_p(stream.cuda_stream))
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_drq_run")

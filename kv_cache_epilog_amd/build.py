@@ -9,7 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkvepi.so")
-SOURCES = [os.path.join(CSRC, "kvepi_kernels.hip"), os.path.join(CSRC, "kvepi_host.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("kvepi_kernels.hip", "kvepi_host.cpp",
+                                           "kvepi_drq.hip", "kvepi_drq_host.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
@@ -25,16 +26,30 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    if not force and os.path.exists(LIB_PATH):
-        return LIB_PATH
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}")
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel), then links."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="kvepi_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *compile_flags, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
+                for src, obj in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB_PATH + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -54,6 +54,16 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
 }
 
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32), a in
+// the low half (tests/hw_check.hip compares it with a software rounding for
+// every fp32 value).
+__device__ __forceinline__ uint32_t pack_bf16_rn(float a, float b) {
+  typedef __bf16 rn_bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float rn_f32x2 __attribute__((ext_vector_type(2)));
+  rn_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, rn_bf16x2));
+}
+
 // max(|a|, |b|, |c|) in one instruction (the compiler's fmaxf chain adds
 // canonicalisations for inputs it cannot prove to be canonical).
 __device__ __forceinline__ float max3_abs(float a, float b, float c) {

@@ -1,0 +1,18 @@
+// kvepi_drq_plan.h -- internal description of one validated dequant -> RoPE
+// -> int8 KV cache call, passed from the host validation
+// (kvepi_drq_host.cpp) to the launcher (kvepi_drq.hip).  Not public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "kvepi_drq.h"
+
+struct kvepi_drq_plan {
+  kvepi_drq_params p;       // the caller's parameters (validated)
+  int64_t H;                // (nq + 2 nkv) * head_dim
+  int64_t units;            // T * H / 16 threads, one per 16 values
+  int64_t k_pitch, k_bstride, v_pitch, v_bstride;  // bytes
+};
+
+kvepi_status kvepi_drq_validate(const kvepi_drq_params *p, kvepi_drq_plan *plan);
+kvepi_status kvepi_drq_launch(const kvepi_drq_plan &plan, void *stream);

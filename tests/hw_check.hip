@@ -14,6 +14,9 @@
 //   f16     f16_lo / f16_hi (v_cvt_f32_f16) == a bit-level binary16 decode, every
 //           pattern
 //   fp8s16, fp4s16  the scaled converts as above, every fp16 v
+//   rn16    fp32 -> fp16 ((_Float16), v_cvt_f16_f32) and fp32 -> bf16
+//           (pack_bf16_rn, v_cvt_pk_bf16_f32) == round to nearest even done
+//           on the bits, for every non-NaN fp32 value
 //   div16   div_fast(a, b, rcp_rn(b)) == a / b for every fp16 significand a
 //           against every fp32 significand b (quotient in (1/2, 2); exponents
 //           are a pure scaling while the quotient stays normal)
@@ -79,6 +82,35 @@ __global__ void k_f16(uint32_t n, unsigned *bad) {
   if (!ok_lo || !ok_hi) atomicAdd(bad, 1u);
 }
 
+// round to nearest even on the bits: binary16 (overflow to infinity from
+// 65520; below 2^-14 the subnormal count f * 2^24, exact, rounded) and bfloat16
+__device__ uint32_t f16_rn_ref(uint32_t u) {
+  const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x477FF000u) {
+    code = 0x7C00u;
+  } else if (a >= 0x38800000u) {
+    const uint32_t r = a + 0xFFFu + ((a >> 13) & 1u);
+    code = (r >> 13) - (112u << 10);
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 0x1p24f);
+  }
+  return sign | code;
+}
+
+__global__ void k_rn16(uint32_t base, uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t u = base + i;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return;  // NaN
+  const float f = __uint_as_float(u);
+  const _Float16 h = (_Float16)f;
+  const uint32_t got16 = __builtin_bit_cast(unsigned short, h);
+  const uint32_t gotb = pack_bf16_rn(f, 0.0f) & 0xFFFFu;
+  const uint32_t wantb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  if (got16 != f16_rn_ref(u) || gotb != wantb) atomicAdd(bad, 1u);
+}
+
 // one fp32 divisor significand per thread, every fp16 numerator significand
 __global__ void k_div16(uint32_t n, unsigned *bad) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -141,10 +173,13 @@ int main() {
   hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 0, 1, d + 8, d + 9);
   hipLaunchKernelGGL(k_scaled, dim3((n_sc + 255) / 256), dim3(256), 0, 0, n_sc, 1, 1, d + 10,
                      d + 11);
+  for (uint64_t b = 0; b < (1ull << 32); b += (1ull << 28))
+    hipLaunchKernelGGL(k_rn16, dim3((1u << 28) / 256), dim3(256), 0, 0, (uint32_t)b, 1u << 28,
+                       d + 13);
   const uint32_t n_div = 1u << 23;
   hipLaunchKernelGGL(k_div16, dim3(n_div / 256), dim3(256), 0, 0, n_div, d + 12);
   const hipError_t e = hipDeviceSynchronize();
-  unsigned h[13] = {0};
+  unsigned h[14] = {0};
   (void)hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
   (void)hipFree(d);
   if (e != hipSuccess) {
@@ -160,5 +195,6 @@ int main() {
   printf("fp8s16: %u mismatches of %u\n", h[8], h[9]);
   printf("fp4s16: %u mismatches of %u\n", h[10], h[11]);
   printf("div16: %u mismatches of %llu\n", h[12], 1024ull << 23);
-  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12]) ? 1 : 0;
+  printf("rn16: %u mismatches of %llu\n", h[13], 1ull << 32);
+  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12] | h[13]) ? 1 : 0;
 }

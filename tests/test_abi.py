@@ -11,12 +11,13 @@ import pytest
 from kv_cache_epilog_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvepi.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"KVEPI_API\s+[\w\s\*]*?\b(kvepi_\w+)\s*\(", text)))
 
 
@@ -24,7 +25,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kvepi_row_bytes", "kvepi_get_workspace", "kvepi_run",
                           "kvepi_get_workspace_ex", "kvepi_run_ex", "kvepi_status_str",
-                          "kvepi_version"}
+                          "kvepi_version", "kvepi_drq_get_workspace", "kvepi_drq_run"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n

@@ -1,0 +1,89 @@
+"""GPU parity of the dequant -> RoPE -> static int8 quantisation -> KV cache
+operator (through its C ABI) against the oracle: every output value and
+every cache byte (untouched rows and gaps included) must be equal."""
+import numpy as np
+import pytest
+
+import oracle
+from drq_case import compare, make_case
+
+pytestmark = pytest.mark.gpu
+
+I32, BF, FP, F32 = oracle.DT_INT32, oracle.DT_BF16, oracle.DT_FP16, oracle.DT_FP32
+
+
+@pytest.mark.parametrize("out", [BF, FP])
+@pytest.mark.parametrize("bias", [None, F32, I32, BF, FP])
+def test_int32_dequant(out, bias):
+    c = make_case(100 + out * 10 + (bias or 0), T=300, nq=4, nkv=2, D=64, x_dtype=I32,
+                  out_dtype=out, bias_dtype=bias)
+    compare(c, "int32 dequant")
+
+
+@pytest.mark.parametrize("out", [BF, FP])
+@pytest.mark.parametrize("act,offsets,kv_output", [(False, False, True), (True, False, False),
+                                                    (False, True, False)])
+def test_int32_options(out, act, offsets, kv_output):
+    c = make_case(200 + out, T=257, nq=2, nkv=1, D=128, x_dtype=I32, out_dtype=out,
+                  bias_dtype=F32, act=act, offsets=offsets, kv_output=kv_output)
+    compare(c, "int32 options")
+
+
+@pytest.mark.parametrize("dt", [BF, FP])
+@pytest.mark.parametrize("nq,nkv,D", [(12, 3, 128), (2, 1, 32), (1, 1, 64), (8, 8, 16),
+                                      (30, 1, 128)])
+def test_16bit_activations(dt, nq, nkv, D):
+    c = make_case(300 + D + nq, T=200, nq=nq, nkv=nkv, D=D, x_dtype=dt, out_dtype=dt)
+    compare(c, "16-bit x")
+
+
+def test_atk_shapes():
+    # the operator's two end-to-end cases: fp16 x [1, 2304] (Nq*D 1536, Nkv*D
+    # 384) and int32 x [1, 3584] (splits 1792 / 896 / 896, bf16 bias), page mode
+    compare(make_case(1, T=1, nq=12, nkv=3, D=128, x_dtype=FP, out_dtype=FP, skip=0.0), "atk0")
+    compare(make_case(2, T=1, nq=14, nkv=7, D=128, x_dtype=I32, out_dtype=BF, bias_dtype=BF,
+                      skip=0.0), "atk1")
+
+
+@pytest.mark.parametrize("bs,stride_extra,head", [(16, 0, None), (7, 24, None), (128, 8, 264),
+                                                  (1, 0, None)])
+def test_page_layouts(bs, stride_extra, head):
+    c = make_case(400 + bs, T=500, nq=2, nkv=2, D=64, x_dtype=BF, out_dtype=BF, bs=bs,
+                  stride_extra=stride_extra, head=head, skip=0.1)
+    compare(c, "page layout")
+
+
+@pytest.mark.parametrize("B,S,bs", [(4, 50, 64), (7, 13, 13), (1, 128, 200), (16, 1, 4)])
+def test_contiguous_mode(B, S, bs):
+    c = make_case(500 + B * S, T=B * S, nq=2, nkv=1, D=128, x_dtype=I32, out_dtype=FP,
+                  bias_dtype=FP, cache_mode=1, seq_len=S, bs=bs)
+    compare(c, "contiguous")
+
+
+def test_padded_x_rows():
+    c = make_case(600, T=100, nq=4, nkv=2, D=64, x_dtype=I32, out_dtype=BF, bias_dtype=I32,
+                  x_pad=40)
+    compare(c, "padded x")
+
+
+def test_large_token_count():
+    c = make_case(700, T=20000, nq=4, nkv=1, D=128, x_dtype=FP, out_dtype=FP, bs=128)
+    compare(c, "T=20000")
+
+
+def test_saturation_and_ties():
+    # k / v values far beyond the int8 range and exact .5 quotients
+    c = make_case(800, T=64, nq=1, nkv=1, D=64, x_dtype=BF, out_dtype=BF, skip=0.0)
+    c.scale_k[:] = 0.01
+    c.scale_v[:] = 0.5
+    x = c.x.copy()
+    # v heads: multiples of 0.25 -> quotients at .5 ties for scale 0.5
+    v = np.round(np.random.default_rng(9).standard_normal((64, 64)) * 40) / 4
+    x[:, 2 * 64:] = oracle_bits(v)
+    c.x = x
+    compare(c, "saturation")
+
+
+def oracle_bits(v):
+    import kvgen
+    return kvgen.to_bf16(v)
