@@ -30,6 +30,7 @@ import kvgen  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 METRIC = "tokens/s and effective HBM GB/s (% of peak), d=576 fused epilog"
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_epilog_amd", "csrc", "kvepi_kernels.hip")
+DRQ_SRC = os.path.join(ROOT, "kv_cache_epilog_amd", "csrc", "kvepi_drq.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -53,12 +54,12 @@ def algorithmic_bytes(w: kvgen.Workload) -> int:
     return 4 * w.T + hits * (x_row + rope + written) + gamma
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, src: str = KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on another kernel source."""
     try:
@@ -67,7 +68,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("kernel_sha256_16") != kernel_hash():
+    if not e or e.get("kernel_sha256_16") != kernel_hash(src):
         return None
     return e.get("bytes_per_launch")
 
@@ -93,12 +94,13 @@ def _mean_of(rows, pick):
 
 
 def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
-                  copy_write_csv: str, copy_bytes: int):
+                  copy_write_csv: str, copy_bytes: int, kernel: str = "epilog_kernel",
+                  src: str = KERNEL_SRC):
     """Turn FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the epilog kernel
     into HBM bytes per launch.  Each counter is scaled by the factor that
     makes it read true on a plain device copy of copy_bytes (which reads and
     writes exactly copy_bytes)."""
-    is_epi = lambda k: "epilog_kernel" in k  # noqa: E731
+    is_epi = lambda k: kernel in k  # noqa: E731
     is_copy = lambda k: "copy" in k.lower()  # noqa: E731
     kf = _mean_of(_counter_rows(fetch_csv, "FETCH_SIZE"), is_epi)
     kw = _mean_of(_counter_rows(write_csv, "WRITE_SIZE"), is_epi)
@@ -114,7 +116,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv:
     except (OSError, ValueError):
         table = {}
     table[workload] = {
-        "kernel_sha256_16": kernel_hash(), "bytes_per_launch": read_b + write_b,
+        "kernel_sha256_16": kernel_hash(src), "bytes_per_launch": read_b + write_b,
         "read_bytes": read_b, "write_bytes": write_b,
         "fetch_kib_raw": kf, "write_kib_raw": kw,
         "copy_bytes": copy_bytes, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
@@ -202,6 +204,9 @@ def main():
                     choices=range(len(kvgen.CONFIG_NAMES)),
                     help="workload index (default 4: the d=576 fused epilog; 5 and 6: "
                          "the MX-FP8 and per-row FP8 indexer modes)")
+    ap.add_argument("--drq", choices=kvgen.DRQ_NAMES,
+                    help="time the dequant -> RoPE -> int8 KV cache operator on this "
+                         "workload instead of the epilog")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
@@ -215,8 +220,12 @@ def main():
     if args.write_traffic:
         if not args.copy_probe:
             raise SystemExit("--write-traffic needs --copy-probe MIB (the calibration size)")
-        write_traffic(kvgen.CONFIG_NAMES[args.config], *args.write_traffic,
-                      copy_bytes=args.copy_probe << 20)
+        if args.drq:
+            write_traffic(args.drq, *args.write_traffic, copy_bytes=args.copy_probe << 20,
+                          kernel="drq_kernel", src=DRQ_SRC)
+        else:
+            write_traffic(kvgen.CONFIG_NAMES[args.config], *args.write_traffic,
+                          copy_bytes=args.copy_probe << 20)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -225,6 +234,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
+        return
+    if args.drq:
+        main_drq(args)
         return
 
     import torch
@@ -291,6 +303,117 @@ def main():
         kc = w.cache.head_dim * w.cache.elem_bytes
         idx = (np.asarray(rows)[:, None] + np.arange(kc)[None, :]).reshape(-1)
         result["parity_sample_bytes_equal"] = bool(np.array_equal(got[idx], ocache[idx]))
+    print(json.dumps(result), flush=True)
+
+
+# ---- the dequant -> RoPE -> int8 KV cache operator -------------------------------
+
+def drq_algorithmic_bytes(w) -> int:
+    """Bytes the operator must move: per token the x row, cos and sin, the
+    index (and activation scale), q_out (and k_out, v_out); per token with a
+    cache row the int8 k and v rows; once the weight scales, bias and the
+    per-channel scales and offsets."""
+    H = (w.nq + 2 * w.nkv) * w.D
+    xb = 4 if w.x_dtype == kvgen.DT_INT32 else 2
+    if w.cache_mode == 0:
+        hits = int(np.count_nonzero((w.index >= 0) & (w.index < w.geom[0] * w.geom[1])))
+    else:
+        hits = int(sum(max(0, min(w.seq_len, w.geom[1] - v)) for v in w.index if v >= 0))
+    per_token = H * xb + 2 * 2 * w.D + 4 + (4 if w.act_scale is not None else 0)
+    per_token += 2 * w.nq * w.D + (2 * 2 * w.nkv * w.D if w.kv_output else 0)
+    once = sum(a.nbytes for a in (w.weight_scale, w.bias, w.scale_k, w.scale_v, w.offset_k,
+                                  w.offset_v) if a is not None)
+    return w.T * per_token + hits * 2 * w.nkv * w.D + once
+
+
+def main_drq(args):
+    import torch
+    from kv_cache_epilog_amd import binding as B
+
+    w = kvgen.drq_config(args.drq)
+    dev = torch.device("cuda:0")
+    t16 = torch.bfloat16 if w.out_dtype == kvgen.DT_BF16 else torch.float16
+
+    def up(a, dtype=None):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return t.view(dtype) if dtype is not None else t
+
+    x = up(w.x) if w.x_dtype == kvgen.DT_INT32 else up(w.x.view(np.int16), t16)
+    bias = None
+    if w.bias is not None:
+        bias = up(w.bias) if w.bias_dtype in (kvgen.DT_FP32, kvgen.DT_INT32) else up(
+            w.bias.view(np.int16), torch.bfloat16 if w.bias_dtype == kvgen.DT_BF16 else
+            torch.float16)
+    bn, bs, head, stride = w.geom
+    kflat = torch.full((bn * stride,), 0xAB, dtype=torch.uint8, device=dev)
+    vflat = torch.full((bn * stride,), 0xAB, dtype=torch.uint8, device=dev)
+    kview = kflat.as_strided((bn, bs, 1, head), (stride, head, head, 1))
+    vview = vflat.as_strided((bn, bs, 1, head), (stride, head, head, 1))
+    q = torch.empty((w.T, w.nq * w.D), dtype=t16, device=dev)
+    ko = torch.empty((w.T, w.nkv * w.D), dtype=t16, device=dev) if w.kv_output else None
+    vo = torch.empty((w.T, w.nkv * w.D), dtype=t16, device=dev) if w.kv_output else None
+    p = B.drq_params(x, up(w.cos.view(np.int16), t16), up(w.sin.view(np.int16), t16), kview,
+                     vview, up(w.index), nq=w.nq, nkv=w.nkv, head_dim=w.D,
+                     scale_k=up(w.scale_k), scale_v=up(w.scale_v), q_out=q, k_out=ko, v_out=vo,
+                     weight_scale=up(w.weight_scale), act_scale=up(w.act_scale), bias=bias,
+                     offset_k=up(w.offset_k), offset_v=up(w.offset_v), cache_mode=w.cache_mode,
+                     seq_len=w.seq_len)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        B.kvepi_drq_run(p, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        B.kvepi_drq_run(p, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    abytes = drq_algorithmic_bytes(w)
+    achieved = abytes / (ms * 1e-3) / 1e9
+    H = (w.nq + 2 * w.nkv) * w.D
+    result = {
+        "metric": "tokens/s and effective HBM GB/s (% of peak), dequant-RoPE-int8 KV cache",
+        "value": w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded)",
+        "config": {"workload": args.drq, "tokens": w.T, "hidden": H, "nq": w.nq, "nkv": w.nkv,
+                   "head_dim": w.D, "x_dtype": ["bf16", "fp16", "int32"][w.x_dtype],
+                   "cache_mode": ["page", "contiguous"][w.cache_mode],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(args.drq, DRQ_SRC),
+                     "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms},
+    }
+    if not args.no_cpu:
+        import oracle
+        kc = np.full(bn * stride, 0xAB, np.uint8)
+        vc = np.full(bn * stride, 0xAB, np.uint8)
+
+        def run_prefix(n):
+            t0 = time.perf_counter()
+            oracle.drq(w.x[:n], w.x_dtype, w.nq, w.nkv, w.D, w.cos[:n], w.sin[:n], w.out_dtype,
+                       scale_k=w.scale_k, scale_v=w.scale_v, k_cache_bytes=kc,
+                       v_cache_bytes=vc, cache_geom=w.geom, index=w.index[:n],
+                       weight_scale=w.weight_scale,
+                       act_scale=None if w.act_scale is None else w.act_scale[:n], bias=w.bias,
+                       bias_dtype=w.bias_dtype, offset_k=w.offset_k, offset_v=w.offset_v,
+                       kv_output=w.kv_output)
+            return time.perf_counter() - t0
+
+        # calibrate on a small prefix, then time about cpu_seconds of tokens
+        probe = min(w.T, 1024)
+        dt = run_prefix(probe)
+        n = int(min(w.T, max(probe, probe * args.cpu_seconds / max(dt, 1e-6))))
+        dt = run_prefix(n)
+        result["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"first {n} of {w.T} tokens, single-threaded C "
+                                            f"oracle, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
 
 

@@ -3,11 +3,12 @@
 // aclnnDequantRopeQuantKvcache: 计算步骤公式 steps 1-5).
 //
 // The work is elementwise except for the rotate-half RoPE, which pairs value
-// j of a head with value j + D/2.  One thread owns a "unit" of 16 values of
-// one head: 8 consecutive values of its first half and the 8 values D/2
+// j of a head with value j + D/2.  One thread owns a "unit" of 2V values of
+// one head: V consecutive values of its first half and the V values D/2
 // further on, so the rotation needs no exchange between lanes.  Consecutive
-// threads take consecutive units of a token (and heads follow each other),
-// so every load and store instruction covers contiguous 16-byte pieces.
+// threads take consecutive units of a token (and heads follow each other).
+// V is 8 for 16-bit x and 4 for int32 x, so that every x load is one
+// 16-byte piece per lane and a wave's load covers contiguous bytes.
 // The path is bound by HBM bandwidth: each value is read once (2 or 4 bytes)
 // and written once or twice (the 16-bit outputs and the int8 cache).
 #include <hip/hip_runtime.h>
@@ -30,9 +31,9 @@ struct DArgs {
   uint8_t *kc, *vc;
   int64_t k_pitch, k_bstride, v_pitch, v_bstride;
   uint8_t *q_out, *k_out, *v_out;
-  uint64_t u_magic;  // token = unit / U
+  uint64_t u_magic;  // token = thread / U
   int32_t u_shift, U;
-  uint64_t h_magic;  // head = unit-in-token / (D / 16)
+  uint64_t h_magic;  // head = unit-in-token / (units per head)
   int32_t h_shift, upH;
   uint64_t s_magic;  // batch = token / seq_len (contiguous mode)
   int32_t s_shift, S;
@@ -41,37 +42,54 @@ struct DArgs {
   int32_t num_slots;
   int32_t nq, nkv, D;
   int32_t contiguous;
-  uint32_t total;  // units
+  uint32_t total;  // threads (units)
 };
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
-
-// streamed 16-byte loads (x is read once)
-__device__ __forceinline__ int4 ldnt_i4(const uint8_t *p) {
-  const i32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t *>(p));
-  return make_int4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint4 ldnt_u4(const uint8_t *p) {
-  const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 __device__ __forceinline__ uint32_t mdiv(uint32_t n, uint64_t m, int s) {
   return (uint32_t)(((uint64_t)n * m) >> s);
 }
 
-template <int DT>
-__device__ __forceinline__ void unpack16(const uint4 w, float (&v)[8]) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if constexpr (DT == KVEPI_DT_FP16) {
-      v[2 * k] = kvepi::f16_lo(ws[k]);
-      v[2 * k + 1] = kvepi::f16_hi(ws[k]);
+// NW consecutive 32-bit words (NW = 1, 2 or 4) from p; NT: streamed load
+template <int NW, bool NT = false>
+__device__ __forceinline__ void ldw(const uint8_t *p, uint32_t (&w)[NW]) {
+  if constexpr (NW == 4) {
+    if constexpr (NT) {
+      const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t *>(p));
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     } else {
-      v[2 * k] = __uint_as_float(ws[k] << 16);
-      v[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+      const uint4 v = *reinterpret_cast<const uint4 *>(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+  } else if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t *>(p);
+  }
+}
+template <int NW>
+__device__ __forceinline__ void stw(uint8_t *p, const uint32_t (&w)[NW]) {
+  if constexpr (NW == 4)
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  else if constexpr (NW == 2)
+    *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+  else
+    *reinterpret_cast<uint32_t *>(p) = w[0];
+}
+
+// V 16-bit values of type DT (V / 2 words) as fp32
+template <int DT, int V>
+__device__ __forceinline__ void unpack(const uint32_t (&w)[V / 2], float (&v)[V]) {
+#pragma unroll
+  for (int k = 0; k < V / 2; ++k) {
+    if constexpr (DT == KVEPI_DT_FP16) {
+      v[2 * k] = kvepi::f16_lo(w[k]);
+      v[2 * k + 1] = kvepi::f16_hi(w[k]);
+    } else {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
   }
 }
@@ -89,112 +107,135 @@ __device__ __forceinline__ uint32_t pack16(float a, float b) {
     return kvepi::pack_bf16_rn(a, b);
   }
 }
-template <int DT>
-__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
-  return make_uint4(pack16<DT>(v[0], v[1]), pack16<DT>(v[2], v[3]), pack16<DT>(v[4], v[5]),
-                    pack16<DT>(v[6], v[7]));
+template <int DT, int V>
+__device__ __forceinline__ void pack(const float (&v)[V], uint32_t (&w)[V / 2]) {
+#pragma unroll
+  for (int k = 0; k < V / 2; ++k) w[k] = pack16<DT>(v[2 * k], v[2 * k + 1]);
 }
 
-__device__ __forceinline__ void load8f(const float *p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// bias values h .. h+7 as fp32
-__device__ __forceinline__ void load_bias(const DArgs &a, int64_t h, float (&v)[8]) {
-  if (a.bias_dt == KVEPI_DT_FP32) {
-    load8f(reinterpret_cast<const float *>(a.bias) + h, v);
-  } else if (a.bias_dt == KVEPI_DT_INT32) {
-    const int4 p = *reinterpret_cast<const int4 *>(a.bias + 4 * h);
-    const int4 q = *reinterpret_cast<const int4 *>(a.bias + 4 * h + 16);
-    v[0] = (float)p.x; v[1] = (float)p.y; v[2] = (float)p.z; v[3] = (float)p.w;
-    v[4] = (float)q.x; v[5] = (float)q.y; v[6] = (float)q.z; v[7] = (float)q.w;
+template <int V>
+__device__ __forceinline__ void loadf(const float *p, float (&v)[V]) {
+  uint32_t w[V];
+  if constexpr (V == 8) {
+    uint32_t a[4], b[4];
+    ldw<4>(reinterpret_cast<const uint8_t *>(p), a);
+    ldw<4>(reinterpret_cast<const uint8_t *>(p + 4), b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[k] = a[k];
+      w[k + 4] = b[k];
+    }
   } else {
-    const uint4 w = *reinterpret_cast<const uint4 *>(a.bias + 2 * h);
+    ldw<V>(reinterpret_cast<const uint8_t *>(p), w);
+  }
+#pragma unroll
+  for (int k = 0; k < V; ++k) v[k] = __uint_as_float(w[k]);
+}
+
+// bias values h .. h+V-1 as fp32
+template <int V>
+__device__ __forceinline__ void load_bias(const DArgs &a, int64_t h, float (&v)[V]) {
+  if (a.bias_dt == KVEPI_DT_FP32 || a.bias_dt == KVEPI_DT_INT32) {
+    loadf<V>(reinterpret_cast<const float *>(a.bias) + h, v);
+    if (a.bias_dt == KVEPI_DT_INT32) {
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = (float)(int32_t)__float_as_uint(v[k]);
+    }
+  } else {
+    uint32_t w[V / 2];
+    ldw<V / 2>(a.bias + 2 * h, w);
     if (a.bias_dt == KVEPI_DT_FP16)
-      unpack16<KVEPI_DT_FP16>(w, v);
+      unpack<KVEPI_DT_FP16, V>(w, v);
     else
-      unpack16<KVEPI_DT_BF16>(w, v);
+      unpack<KVEPI_DT_BF16, V>(w, v);
   }
 }
 
-// step 1 for values h .. h+7 of token t: x, or its dequantisation rounded to
-// the output type (then read back as fp32)
-template <int XT, int OT>
-__device__ __forceinline__ void dequant8(const DArgs &a, uint32_t t, int64_t h, float (&v)[8]) {
+// step 1 for values h .. h+V-1 of token t: x, or its dequantisation rounded
+// to the output type (then read back as fp32)
+template <int XT, int OT, int V>
+__device__ __forceinline__ void dequant(const DArgs &a, uint32_t t, int64_t h, float (&v)[V]) {
   const uint8_t *xr = a.x + (int64_t)t * a.x_pitch;
   if constexpr (XT == KVEPI_DT_INT32) {
-    const int4 p = ldnt_i4(xr + 4 * h);
-    const int4 q = ldnt_i4(xr + 4 * h + 16);
-    const int xi[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-    float w[8];
-    load8f(a.w + h, w);
+    static_assert(V == 4, "int32 rows: 4 values (16 bytes) per half");
+    uint32_t xi[4];
+    ldw<4, true>(xr + 4 * h, xi);
+    float w[V];
+    loadf<V>(a.w + h, w);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = (float)xi[k] * w[k];
+    for (int k = 0; k < V; ++k) v[k] = (float)(int32_t)xi[k] * w[k];
     if (a.act != nullptr) {
       const float s = a.act[t];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = v[k] * s;
+      for (int k = 0; k < V; ++k) v[k] = v[k] * s;
     }
     if (a.bias_dt >= 0) {
-      float b[8];
-      load_bias(a, h, b);
+      float b[V];
+      load_bias<V>(a, h, b);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = v[k] + b[k];
+      for (int k = 0; k < V; ++k) v[k] = v[k] + b[k];
     }
-    unpack16<OT>(pack8<OT>(v), v);
+    uint32_t p[V / 2];
+    pack<OT, V>(v, p);
+    unpack<OT, V>(p, v);
   } else {
-    const uint4 w = ldnt_u4(xr + 2 * h);
-    unpack16<XT>(w, v);
+    static_assert(V == 8, "16-bit rows: 8 values (16 bytes) per half");
+    uint32_t w[4];
+    ldw<4, true>(xr + 2 * h, w);
+    unpack<XT, V>(w, v);
   }
 }
 
-// step 4 for 8 channels: rint(v / scale + offset) saturated to int8, packed
-__device__ __forceinline__ uint2 quant8(const float (&v)[8], const float *sc, const float *of) {
-  float s[8], o[8];
-  load8f(sc, s);
-  if (of != nullptr) load8f(of, o);
-  uint32_t b[8];
+// step 4 for V channels: rint(v / scale + offset) saturated to int8, packed
+template <int V>
+__device__ __forceinline__ void quant(const float (&v)[V], const float *sc, const float *of,
+                                      uint32_t (&out)[V / 4]) {
+  float s[V], o[V];
+  loadf<V>(sc, s);
+  if (of != nullptr) loadf<V>(of, o);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < V / 4; ++k) out[k] = 0;
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
     float q = v[k] / s[k];
     if (of != nullptr) q = q + o[k];
     const float r = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(q), -128.0f), 127.0f);
-    b[k] = (uint32_t)(int32_t)r & 0xFFu;
+    out[k / 4] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (k % 4));
   }
-  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
 }
 
-template <int XT, int OT>
+template <int XT, int OT, int V>
 __global__ __launch_bounds__(256) void drq_kernel(const DArgs a) {
   const uint32_t i = blockIdx.x * 256u + threadIdx.x;
   if (i >= a.total) return;
   const uint32_t t = mdiv(i, a.u_magic, a.u_shift);
   const uint32_t u = i - t * (uint32_t)a.U;
   const uint32_t head = mdiv(u, a.h_magic, a.h_shift);
-  const int32_t j0 = 8 * (int32_t)(u - head * (uint32_t)a.upH);
+  const int32_t j0 = V * (int32_t)(u - head * (uint32_t)a.upH);
   const int32_t D = a.D, half = D / 2;
   const int64_t h0 = (int64_t)head * D + j0, h1 = h0 + half;
 
-  float x0[8], x1[8];
-  dequant8<XT, OT>(a, t, h0, x0);
-  dequant8<XT, OT>(a, t, h1, x1);
+  float x0[V], x1[V];
+  dequant<XT, OT, V>(a, t, h0, x0);
+  dequant<XT, OT, V>(a, t, h1, x1);
 
   const int32_t nq = a.nq, nkv = a.nkv;
-  float y0[8], y1[8];
+  float y0[V], y1[V];
   if ((int32_t)head < nq + nkv) {
     // rotate-half RoPE with the token's cos / sin: two products, one sum
-    float c0[8], c1[8], s0[8], s1[8];
+    float c0[V], c1[V], s0[V], s1[V];
+    uint32_t w[V / 2];
     const int64_t cb = 2 * ((int64_t)t * D + j0);
-    unpack16<OT>(*reinterpret_cast<const uint4 *>(a.cos + cb), c0);
-    unpack16<OT>(*reinterpret_cast<const uint4 *>(a.cos + cb + 2 * half), c1);
-    unpack16<OT>(*reinterpret_cast<const uint4 *>(a.sin + cb), s0);
-    unpack16<OT>(*reinterpret_cast<const uint4 *>(a.sin + cb + 2 * half), s1);
+    ldw<V / 2>(a.cos + cb, w);
+    unpack<OT, V>(w, c0);
+    ldw<V / 2>(a.cos + cb + 2 * half, w);
+    unpack<OT, V>(w, c1);
+    ldw<V / 2>(a.sin + cb, w);
+    unpack<OT, V>(w, s0);
+    ldw<V / 2>(a.sin + cb + 2 * half, w);
+    unpack<OT, V>(w, s1);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < V; ++k) {
       const float p0 = x0[k] * c0[k], q0 = x1[k] * s0[k];
       const float p1 = x1[k] * c1[k], q1 = x0[k] * s1[k];
       y0[k] = p0 - q0;
@@ -202,16 +243,18 @@ __global__ __launch_bounds__(256) void drq_kernel(const DArgs a) {
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < V; ++k) {
       y0[k] = x0[k];
       y1[k] = x1[k];
     }
   }
-  const uint4 w0 = pack8<OT>(y0), w1 = pack8<OT>(y1);
+  uint32_t w0[V / 2], w1[V / 2];
+  pack<OT, V>(y0, w0);
+  pack<OT, V>(y1, w1);
   if ((int32_t)head < nq) {
     uint8_t *qo = a.q_out + 2 * ((int64_t)t * nq * D + h0);
-    *reinterpret_cast<uint4 *>(qo) = w0;
-    *reinterpret_cast<uint4 *>(qo + 2 * half) = w1;
+    stw<V / 2>(qo, w0);
+    stw<V / 2>(qo + 2 * half, w1);
     return;
   }
   // k or v head: the 16-bit output, then the int8 codes of the rounded values
@@ -221,8 +264,8 @@ __global__ __launch_bounds__(256) void drq_kernel(const DArgs a) {
   uint8_t *out = is_k ? a.k_out : a.v_out;
   if (out != nullptr) {
     uint8_t *o = out + 2 * ((int64_t)t * nkv * D + c);
-    *reinterpret_cast<uint4 *>(o) = w0;
-    *reinterpret_cast<uint4 *>(o + 2 * half) = w1;
+    stw<V / 2>(o, w0);
+    stw<V / 2>(o + 2 * half, w1);
   }
   // the token's cache row (page: its slot; contiguous: row start[b] + s of
   // block b); -1 or a row outside the cache skips the write
@@ -240,15 +283,17 @@ __global__ __launch_bounds__(256) void drq_kernel(const DArgs a) {
   const uint32_t blk =
       a.bs_log2 >= 0 ? slot >> a.bs_log2 : mdiv(slot, a.bs_magic, a.bs_shift);
   const uint32_t pos = slot - blk * (uint32_t)a.block_size;
-  unpack16<OT>(w0, y0);  // quantise the values as output (rounded)
-  unpack16<OT>(w1, y1);
+  unpack<OT, V>(w0, y0);  // quantise the values as output (rounded)
+  unpack<OT, V>(w1, y1);
   const float *sc = is_k ? a.sk : a.sv;
   const float *of = is_k ? a.ok : a.ov;
   uint8_t *row = is_k ? a.kc + (int64_t)blk * a.k_bstride + (int64_t)pos * a.k_pitch
                       : a.vc + (int64_t)blk * a.v_bstride + (int64_t)pos * a.v_pitch;
-  *reinterpret_cast<uint2 *>(row + c) = quant8(y0, sc + c, of ? of + c : nullptr);
-  *reinterpret_cast<uint2 *>(row + c + half) =
-      quant8(y1, sc + c + half, of ? of + c + half : nullptr);
+  uint32_t q0[V / 4], q1[V / 4];
+  quant<V>(y0, sc + c, of ? of + c : nullptr, q0);
+  quant<V>(y1, sc + c + half, of ? of + c + half : nullptr, q1);
+  stw<V / 4>(row + c, q0);
+  stw<V / 4>(row + c + half, q1);
 }
 
 // n / d == (n * m) >> s for every n < 2^31 (m = ceil(2^(31+l) / d), l =
@@ -269,9 +314,10 @@ kvepi_status kvepi_drq_launch(const kvepi_drq_plan &pl, void *stream) {
   using namespace kvepi_drq;
   const kvepi_drq_params &p = pl.p;
   DArgs a{};
-  const int xb = p.x_dtype == KVEPI_DT_INT32 ? 4 : 2;
+  const bool i32 = p.x_dtype == KVEPI_DT_INT32;
+  const int V = i32 ? 4 : 8;  // values per half-unit
   a.x = static_cast<const uint8_t *>(p.x);
-  a.x_pitch = p.x_row_stride * xb;
+  a.x_pitch = p.x_row_stride * (i32 ? 4 : 2);
   a.cos = static_cast<const uint8_t *>(p.cos);
   a.sin = static_cast<const uint8_t *>(p.sin);
   a.w = p.weight_scale;
@@ -292,9 +338,9 @@ kvepi_status kvepi_drq_launch(const kvepi_drq_plan &pl, void *stream) {
   a.q_out = static_cast<uint8_t *>(p.q_out);
   a.k_out = static_cast<uint8_t *>(p.k_out);
   a.v_out = static_cast<uint8_t *>(p.v_out);
-  a.U = (int32_t)(pl.H / 16);
+  a.U = (int32_t)(pl.H / (2 * V));
   magic((uint32_t)a.U, &a.u_magic, &a.u_shift);
-  a.upH = p.head_dim / 16;
+  a.upH = p.head_dim / (2 * V);
   magic((uint32_t)a.upH, &a.h_magic, &a.h_shift);
   a.contiguous = p.cache_mode == KVEPI_DRQ_CONTIGUOUS;
   a.S = a.contiguous ? (int32_t)p.seq_len : 1;
@@ -308,15 +354,15 @@ kvepi_status kvepi_drq_launch(const kvepi_drq_plan &pl, void *stream) {
   a.nq = p.nq;
   a.nkv = p.nkv;
   a.D = p.head_dim;
-  a.total = (uint32_t)pl.units;
+  a.total = (uint32_t)(p.num_tokens * a.U);
 
   kfn_t fn;
-  if (p.x_dtype == KVEPI_DT_INT32)
-    fn = p.out_dtype == KVEPI_DT_FP16 ? drq_kernel<KVEPI_DT_INT32, KVEPI_DT_FP16>
-                                      : drq_kernel<KVEPI_DT_INT32, KVEPI_DT_BF16>;
+  if (i32)
+    fn = p.out_dtype == KVEPI_DT_FP16 ? drq_kernel<KVEPI_DT_INT32, KVEPI_DT_FP16, 4>
+                                      : drq_kernel<KVEPI_DT_INT32, KVEPI_DT_BF16, 4>;
   else
-    fn = p.out_dtype == KVEPI_DT_FP16 ? drq_kernel<KVEPI_DT_FP16, KVEPI_DT_FP16>
-                                      : drq_kernel<KVEPI_DT_BF16, KVEPI_DT_BF16>;
+    fn = p.out_dtype == KVEPI_DT_FP16 ? drq_kernel<KVEPI_DT_FP16, KVEPI_DT_FP16, 8>
+                                      : drq_kernel<KVEPI_DT_BF16, KVEPI_DT_BF16, 8>;
   const uint32_t blocks = (a.total + 255u) / 256u;
   void *args[] = {&a};
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(blocks),

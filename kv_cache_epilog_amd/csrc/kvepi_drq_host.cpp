@@ -50,7 +50,7 @@ kvepi_status kvepi_drq_validate(const kvepi_drq_params *pp, kvepi_drq_plan *plan
   const int64_t H = (int64_t)(p.nq + 2 * (int64_t)p.nkv) * p.head_dim;
   if (H > 4096 || H % 64 != 0) return KVEPI_ERR_SHAPE;
   if (p.num_tokens < 0 || p.num_tokens > INT32_MAX) return KVEPI_ERR_SHAPE;
-  if (p.num_tokens * (H / 16) > INT32_MAX) return KVEPI_ERR_SHAPE;
+  if (p.num_tokens * (H / 8) > INT32_MAX) return KVEPI_ERR_SHAPE;
   if (p.x_row_stride < H || p.x_row_stride % 8 != 0 || p.x_row_stride > (INT64_C(1) << 28))
     return KVEPI_ERR_LAYOUT;
   // required pointers
@@ -88,7 +88,7 @@ kvepi_status kvepi_drq_validate(const kvepi_drq_params *pp, kvepi_drq_plan *plan
   if (plan) {
     plan->p = p;
     plan->H = H;
-    plan->units = p.num_tokens * (H / 16);
+    plan->units = p.num_tokens * (H / (dequant ? 8 : 16));
     plan->k_pitch = p.k_cache.head_dim;
     plan->k_bstride = p.k_cache.block_stride;
     plan->v_pitch = p.v_cache.head_dim;

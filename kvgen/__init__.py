@@ -255,3 +255,120 @@ def config(i: int) -> Workload:
                     aux=CacheSpec(1024, 128, 1, 128 * 1, 4),
                     row_sigma=1.0, skip_frac=0.01)
     raise IndexError(i)
+
+
+# ---- the dequant -> RoPE -> int8 KV cache operator's inputs ----------------------
+# Inputs follow the operator's own examples: int32 matmul outputs with
+# per-column weight scales, per-token activation scales and a bias, or
+# fp16/bf16 activations; cos/sin of random positions; per-channel static
+# scales sized to the k / v ranges.
+
+DT_BF16, DT_FP16, DT_INT32, DT_FP32 = 0, 1, 2, 3
+
+
+@dataclass
+class DrqWorkload:
+    """Inputs of one dequant -> RoPE -> int8 KV cache call (cache given by its
+    byte geometry; cache_mode 0 = page, 1 = contiguous)."""
+    T: int
+    nq: int
+    nkv: int
+    D: int
+    x: np.ndarray            # int32 or uint16 bits [T, H]
+    x_dtype: int
+    out_dtype: int
+    cos: np.ndarray
+    sin: np.ndarray
+    scale_k: np.ndarray
+    scale_v: np.ndarray
+    index: np.ndarray
+    cache_mode: int          # 0 page, 1 contiguous
+    seq_len: int
+    geom: tuple              # (block_num, block_size, head_dim, block_stride) bytes
+    weight_scale: Optional[np.ndarray] = None
+    act_scale: Optional[np.ndarray] = None
+    bias: Optional[np.ndarray] = None
+    bias_dtype: int = DT_FP32
+    offset_k: Optional[np.ndarray] = None
+    offset_v: Optional[np.ndarray] = None
+    kv_output: bool = True
+    x_pad: int = 0
+    notes: dict = field(default_factory=dict)
+
+
+def to16(a, dt):
+    """bf16 or fp16 bit patterns of float values (round to nearest even)."""
+    return to_bf16(a) if dt == DT_BF16 else to_fp16(a)
+
+
+def drq_make(seed, *, T, nq, nkv, D, x_dtype, out_dtype, cache_mode=0, bias_dtype=None,
+              act=True, offsets=True, kv_output=True, bn=None, bs=16, head=None, stride_extra=0,
+              skip=0.05, seq_len=0, x_pad=0) -> DrqWorkload:
+    rng = np.random.default_rng(seed)
+    H = (nq + 2 * nkv) * D
+    ws = act_s = bias = None
+    if x_dtype == DT_INT32:
+        x = rng.integers(-(1 << 20), 1 << 20, (T, H)).astype(np.int32)
+        ws = (rng.random(H) * 2e-4 + 1e-5).astype(np.float32)
+        if act:
+            act_s = rng.uniform(0.5, 2.0, T).astype(np.float32)
+        if bias_dtype is not None:
+            b = rng.standard_normal(H) * 4
+            if bias_dtype == DT_FP32:
+                bias = b.astype(np.float32)
+            elif bias_dtype == DT_INT32:
+                bias = np.round(b).astype(np.int32)
+            else:
+                bias = to16(b, bias_dtype)
+        mag = 200.0
+    else:
+        x = to16(rng.standard_normal((T, H)) * 3, x_dtype)
+        mag = 12.0
+    pos = rng.integers(0, 32768, T).astype(np.float64)
+    inv = 10000.0 ** (-2.0 * np.arange(D // 2) / D)
+    ang = np.concatenate([pos[:, None] * inv[None, :]] * 2, axis=1)
+    cos, sin = to16(np.cos(ang), out_dtype), to16(np.sin(ang), out_dtype)
+    sk = (mag / 127 * rng.uniform(0.5, 1.5, nkv * D)).astype(np.float32)
+    sv = (mag / 127 * rng.uniform(0.5, 1.5, nkv * D)).astype(np.float32)
+    ok = ov = None
+    if offsets:
+        ok = rng.integers(-8, 8, nkv * D).astype(np.float32)
+        ov = (rng.integers(-16, 16, nkv * D) / 2).astype(np.float32)  # .5 ties
+    row = nkv * D
+    head = head or row
+    if cache_mode == 0:
+        bn = bn or (T + bs - 1) // bs + 2
+        index = rng.permutation(bn * bs)[:T].astype(np.int32)
+        k = int(round(skip * T))
+        if k:
+            index[rng.choice(T, k, replace=False)] = -1
+        if T > 3:
+            index[3] = bn * bs  # outside the cache: skipped
+    else:
+        B = T // seq_len
+        bn = bn or B + 1
+        index = rng.integers(0, bs - seq_len + 1, B).astype(np.int32)
+        if B > 1:
+            index[1] = -1
+    geom = (bn, bs, head, bs * head + stride_extra)
+    return DrqWorkload(T, nq, nkv, D, x, x_dtype, out_dtype, cos, sin, sk, sv, index, cache_mode,
+                   seq_len, geom, ws, act_s, bias, bias_dtype if bias is not None else
+                   DT_FP32, ok, ov, kv_output, x_pad)
+
+
+DRQ_NAMES = ("drq_fp16_h2304", "drq_int32_h3584")
+
+
+def drq_config(name: str) -> DrqWorkload:
+    """Throughput workloads at the operator's two test shapes, with many
+    tokens: fp16 x [65536, 2304] (12 q heads, 3 k / v heads of 128) and
+    int32 x [32768, 3584] (14 / 7 / 7 heads of 128, bf16 bias, activation
+    scales, offsets), page mode with 1 % skipped tokens, k / v outputs on."""
+    if name == DRQ_NAMES[0]:
+        return drq_make(10, T=65536, nq=12, nkv=3, D=128, x_dtype=DT_FP16, out_dtype=DT_FP16,
+                        bs=128, skip=0.01)
+    if name == DRQ_NAMES[1]:
+        return drq_make(11, T=32768, nq=14, nkv=7, D=128, x_dtype=DT_INT32, out_dtype=DT_BF16,
+                        bias_dtype=DT_BF16, bs=128, skip=0.01)
+    raise KeyError(name)
+
