@@ -856,14 +856,24 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       t.own = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((j % L) * R + sub), win);
     t.g = (uint32_t)wave + (uint32_t)j * (uint32_t)a.nwaves;
     const bool in = j < n_it;
+    if constexpr (R > 2) {
+      // many rows per wave: each lane judges its own row (live holds only
+      // the lane's own bit), and the first live row comes from a ballot
+      const uint32_t row = t.g * R + (uint32_t)sub;
+      const bool lv = in && row < (uint32_t)a.T && t.own < ns;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(lv);
+      t.live = lv ? 1u << sub : 0u;
+      t.first = bal != 0 ? t.g * R + (uint32_t)__builtin_ctzll(bal) / L : 0u;
+    } else {
 #pragma unroll
-    for (int r = R - 1; r >= 0; --r) {
-      const uint32_t sl = (uint32_t)__builtin_amdgcn_readlane(win, (j % L) * R + r);
-      const uint32_t row = t.g * R + r;
-      t.sl[r] = sl;
-      if (in && row < (uint32_t)a.T && sl < ns) {
-        t.live |= 1u << r;
-        t.first = row;  // the loop runs downwards: the last assignment is the first row
+      for (int r = R - 1; r >= 0; --r) {
+        const uint32_t sl = (uint32_t)__builtin_amdgcn_readlane(win, (j % L) * R + r);
+        const uint32_t row = t.g * R + r;
+        t.sl[r] = sl;
+        if (in && row < (uint32_t)a.T && sl < ns) {
+          t.live |= 1u << r;
+          t.first = row;  // the loop runs downwards: the last assignment is the first row
+        }
       }
     }
     return t;
