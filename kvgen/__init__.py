@@ -92,6 +92,7 @@ class Workload:
     x_fp16: bool = False   # x holds fp16 bits (indexer modes)
     index_mode: int = 0    # 0: slots holds one slot per token; 1-3: see below
     seq_len: int = 0       # tokens per batch for index modes 1-3
+    rope_dim: int = 64     # rope segment length (any even value in the bf16 split mode)
 
     @property
     def hits(self) -> int:
@@ -181,7 +182,8 @@ def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
          aux: Optional[CacheSpec] = None, norm: bool = False, rope: bool = False,
          row_sigma: float = 0.0, outlier_frac: float = 0.0, skip_frac: float = 0.0,
          n_skip: Optional[int] = None, max_pos: int = 32768, eps: float = 1e-6,
-         group_size: Optional[int] = None, x: Optional[np.ndarray] = None) -> Workload:
+         group_size: Optional[int] = None, x: Optional[np.ndarray] = None,
+         rope_dim: int = 64) -> Workload:
     rng = np.random.default_rng(seed)
     if group_size is None:
         group_size = {MODE_MXFP4: 32, MODE_MXFP8: 32, MODE_FP8_ROW: 0}.get(mode, 64)
@@ -189,14 +191,16 @@ def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
         x = normal_rows(rng, T, d, row_sigma, outlier_frac)
     gamma = cos = sin = None
     if norm:
-        gamma = to_bf16(rng.uniform(0.5, 1.5, size=d - 64))
+        gamma = to_bf16(rng.uniform(0.5, 1.5, size=d - rope_dim))
     if rope:
-        cos, sin, _ = rope_tables(rng, T, max_pos)
+        cos, sin, _ = rope_tables(rng, T, max_pos, dk=rope_dim)
     slots = slot_mapping(rng, T, cache.num_slots, skip_frac, n_skip)
     cache_init = np.full(cache.alloc_bytes, PREFILL, np.uint8)
     aux_init = None if aux is None else np.full(aux.alloc_bytes, PREFILL, np.uint8)
-    return Workload(name, mode, T, d, group_size, x, slots, cache, cache_init,
-                    gamma, cos, sin, eps, aux, aux_init)
+    w = Workload(name, mode, T, d, group_size, x, slots, cache, cache_init,
+                 gamma, cos, sin, eps, aux, aux_init)
+    w.rope_dim = rope_dim
+    return w
 
 
 # ---- the five named workloads ---------------------------------------------

@@ -91,8 +91,10 @@ def lib() -> ctypes.CDLL:
         L.kvo_token_slot.argtypes = [ctypes.c_int, P, I64, I64, I64, I64]
         L.kvo_token_slot.restype = I64
         L.kvo_epilog_ex.argtypes = [ctypes.c_int, I64, I64, P, I64, ctypes.c_int, P, P, P, F,
-                                    P, ctypes.c_int, I64, I32, ctypes.POINTER(_Cache),
-                                    ctypes.POINTER(_Cache)]
+                                    P, ctypes.c_int, I64, ctypes.c_int, I32,
+                                    ctypes.POINTER(_Cache), ctypes.POINTER(_Cache)]
+        L.kvo_rope_row_n.argtypes = [P, P, P, I64, P]
+        L.kvo_rope_row_n.restype = None
         L.kvo_epilog_ex.restype = ctypes.c_int
         L.kvo_f32_to_fp16.argtypes = [F]
         L.kvo_f32_to_fp16.restype = ctypes.c_uint16
@@ -160,6 +162,17 @@ def sumsq_tree(x_bf16) -> float:
     return float(lib().kvo_sumsq_tree(_ptr(x), x.size))
 
 
+def rope_row_n(x_bf16, cos_bf16, sin_bf16) -> np.ndarray:
+    """RoPE of a rope segment of any even length n (cos / sin of length n)."""
+    x = _c(x_bf16, np.uint16)
+    c = _c(cos_bf16, np.uint16)
+    s = _c(sin_bf16, np.uint16)
+    assert x.size % 2 == 0 and c.size == s.size == x.size
+    y = np.empty(x.size, np.uint16)
+    lib().kvo_rope_row_n(_ptr(x), _ptr(c), _ptr(s), x.size, _ptr(y))
+    return y
+
+
 def rope_row(x_bf16, cos_bf16, sin_bf16) -> np.ndarray:
     x, c, s = _c(x_bf16, np.uint16), _c(cos_bf16, np.uint16), _c(sin_bf16, np.uint16)
     assert x.size == 64 and c.size == 64 and s.size == 64
@@ -213,7 +226,7 @@ def token_slot(index_mode: int, index, t: int, seq_len: int, block_num: int,
 def epilog(mode: int, x, slot_mapping, cache_bytes, cache_geom, *, group_size: int,
            gamma=None, cos=None, sin=None, eps: float = 1e-6, aux_bytes=None,
            aux_geom=None, x_fp16: bool = False, index_mode: int = INDEX_SLOT,
-           seq_len: int = 0):
+           seq_len: int = 0, rope_dim: int = 64):
     """Run the oracle in place on host byte buffers.
 
     cache_geom / aux_geom: (block_num, block_size, head_dim, block_stride) in
@@ -244,7 +257,7 @@ def epilog(mode: int, x, slot_mapping, cache_bytes, cache_geom, *, group_size: i
     rc = lib().kvo_epilog_ex(mode, T, d, x.ctypes.data_as(ctypes.c_void_p),
                              x.strides[0] // 2, int(x_fp16), _ptr(gamma), _ptr(cos),
                              _ptr(sin), ctypes.c_float(eps), _ptr(slots), index_mode,
-                             seq_len, group_size, ctypes.byref(c),
+                             seq_len, rope_dim, group_size, ctypes.byref(c),
                              ctypes.byref(a) if a is not None else None)
     if rc != 0:
         raise ValueError("oracle epilog rejected its arguments")

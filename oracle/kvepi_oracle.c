@@ -268,20 +268,26 @@ void kvo_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t n,
  * y = cat(x1, x2) * cos + cat(-x2, x1) * sin.  The output is half-split:
  * y[j] = x1[j]*cos[j] - x2[j]*sin[j], y[32+j] = x2[j]*cos[32+j] +
  * x1[j]*sin[32+j]. */
-void kvo_rope_row(const uint16_t *x, const uint16_t *cos, const uint16_t *sin,
-                  uint16_t *y) {
-  for (int j = 0; j < 32; ++j) {
+void kvo_rope_row_n(const uint16_t *x, const uint16_t *cos, const uint16_t *sin, int64_t n,
+                    uint16_t *y) {
+  const int64_t h = n / 2;
+  for (int64_t j = 0; j < h; ++j) {
     float x1 = kvo_bf16_to_f32(x[2 * j]);
     float x2 = kvo_bf16_to_f32(x[2 * j + 1]);
     float c0 = kvo_bf16_to_f32(cos[j]), s0 = kvo_bf16_to_f32(sin[j]);
-    float c1 = kvo_bf16_to_f32(cos[32 + j]), s1 = kvo_bf16_to_f32(sin[32 + j]);
+    float c1 = kvo_bf16_to_f32(cos[h + j]), s1 = kvo_bf16_to_f32(sin[h + j]);
     float p1 = x1 * c0;
     float p2 = (-x2) * s0;
     y[j] = kvo_f32_to_bf16(p1 + p2);
     float p3 = x2 * c1;
     float p4 = x1 * s1;
-    y[32 + j] = kvo_f32_to_bf16(p3 + p4);
+    y[h + j] = kvo_f32_to_bf16(p3 + p4);
   }
+}
+
+void kvo_rope_row(const uint16_t *x, const uint16_t *cos, const uint16_t *sin,
+                  uint16_t *y) {
+  kvo_rope_row_n(x, cos, sin, 64, y);
 }
 
 /* ======================================================================== */
@@ -508,15 +514,27 @@ int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
                const int32_t *slot_mapping, int32_t group_size,
                const kvo_cache *cache, const kvo_cache *aux) {
   return kvo_epilog_ex(mode, T, d, x, x_row_stride, 0, gamma, cos, sin, eps, slot_mapping,
-                       KVO_INDEX_SLOT, 0, group_size, cache, aux);
+                       KVO_INDEX_SLOT, 0, 64, group_size, cache, aux);
 }
 
 int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_row_stride,
                   int x_fp16, const uint16_t *gamma, const uint16_t *cos, const uint16_t *sin,
                   float eps, const int32_t *index, int index_mode, int64_t seq_len,
-                  int32_t group_size, const kvo_cache *cache, const kvo_cache *aux) {
+                  int rope_dim, int32_t group_size, const kvo_cache *cache,
+                  const kvo_cache *aux) {
   int64_t cc, kc, sc;
-  if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
+  /* the rope segment: the last 64 columns ("aclnnKvCompressEpilog" 接口功能),
+   * or in the bf16 split mode any even Dk with Dk + Dv = d
+   * ("aclnnKvRmsNormRopeCache", shape notes: Dk even) */
+  if (mode == KVO_MODE_BF16_SPLIT) {
+    if (rope_dim < 2 || rope_dim % 2 || d - rope_dim < 8 || (d - rope_dim) % 8 || d > 8192)
+      return -1;
+    cc = kc = d - rope_dim;
+    sc = rope_dim;
+  } else {
+    if (rope_dim != 64) return -1;
+    if (kvo_row_bytes(mode, d, group_size, &cc, &kc, &sc) != 0) return -1;
+  }
   if (index_mode != KVO_INDEX_SLOT && (seq_len <= 0 || T % seq_len != 0)) return -1;
   if ((cos == NULL) != (sin == NULL)) return -1;
   const int indexer = mode == KVO_MODE_MXFP4 || mode == KVO_MODE_MXFP8 ||
@@ -525,7 +543,8 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
   if (mode == KVO_MODE_BF16_SPLIT && (!gamma || !cos)) return -1;
   if ((indexer || mode == KVO_MODE_BF16_SPLIT) && !aux) return -1;
   if (x_fp16 && !indexer) return -1;
-  int64_t nope = d - 64;
+  const int64_t dk = rope_dim;
+  int64_t nope = d - dk;
   uint16_t *v = (uint16_t *)malloc((size_t)d * sizeof(uint16_t));
   uint8_t *row = (uint8_t *)malloc((size_t)kc + 64);
   uint8_t *srow = (uint8_t *)malloc((size_t)sc + 64);
@@ -548,14 +567,14 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
     else
       memcpy(v, xr, (size_t)nope * sizeof(uint16_t));
     if (cos)
-      kvo_rope_row(xr + nope, cos + t * 64, sin + t * 64, v + nope);
+      kvo_rope_row_n(xr + nope, cos + t * dk, sin + t * dk, dk, v + nope);
     else
-      memcpy(v + nope, xr + nope, 64 * sizeof(uint16_t));
+      memcpy(v + nope, xr + nope, (size_t)dk * sizeof(uint16_t));
     if (mode == KVO_MODE_BF16_SPLIT) {
       uint8_t *ckv = row_ptr(cache, s, 2);
       uint8_t *k = row_ptr(aux, s, 2);
       for (int64_t i = 0; i < nope; ++i) put_u16le(ckv + 2 * i, v[i]);
-      for (int64_t j = 0; j < 64; ++j) put_u16le(k + 2 * j, v[nope + j]);
+      for (int64_t j = 0; j < dk; ++j) put_u16le(k + 2 * j, v[nope + j]);
       continue;
     }
     kvo_quant_row(mode, v, d, group_size, row, NULL);

@@ -70,6 +70,9 @@ void kvo_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t n,
 /* Sum of squares as the balanced pairwise tree (exposed for its pin). */
 float kvo_sumsq_tree(const uint16_t *x, int64_t n);
 /* Interleaved RoPE on 64 values -> 64 half-split values. */
+/* the same for a rope segment of n (even) values */
+void kvo_rope_row_n(const uint16_t *x, const uint16_t *cos, const uint16_t *sin, int64_t n,
+                    uint16_t *y);
 void kvo_rope_row(const uint16_t *x, const uint16_t *cos, const uint16_t *sin,
                   uint16_t *y);
 
@@ -114,12 +117,15 @@ int kvo_epilog(int mode, int64_t T, int64_t d, const uint16_t *x,
 int64_t kvo_token_slot(int index_mode, const int32_t *index, int64_t t, int64_t seq_len,
                        int64_t block_num, int64_t block_size);
 
-/* kvo_epilog with fp16 rows (x_fp16, indexer modes only) and the index
- * modes above; T must be a multiple of seq_len outside the SLOT mode. */
+/* kvo_epilog with fp16 rows (x_fp16, indexer modes only), the index modes
+ * above (T must be a multiple of seq_len outside the SLOT mode) and the
+ * rope segment length (64; any even value with d - rope_dim a multiple of
+ * 8 in the bf16 split mode, whose cos / sin are then [T, rope_dim]). */
 int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_row_stride,
                   int x_fp16, const uint16_t *gamma, const uint16_t *cos, const uint16_t *sin,
                   float eps, const int32_t *index, int index_mode, int64_t seq_len,
-                  int32_t group_size, const kvo_cache *cache, const kvo_cache *aux);
+                  int rope_dim, int32_t group_size, const kvo_cache *cache,
+                  const kvo_cache *aux);
 
 /* ---- dequant -> RoPE -> int8 KV cache ----------------------------------- */
 #define KVO_DT_BF16 0

@@ -67,6 +67,8 @@ def run_gpu(w: kvgen.Workload, device="cuda:0", offset: int = 0, aux_offset: int
     if w.aux is not None:
         aux, aflat = cache_tensor(w.aux, w.aux_init, device, aux_offset)
     ix = dict(index_mode=w.index_mode, seq_len=w.seq_len)
+    if w.rope_dim != 64:
+        ix["rope_dim"] = w.rope_dim
     ws = kvepi_get_workspace(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos,
                              sin=sin, cache_aux=aux, eps=w.eps, **ix)
     assert ws == 0
@@ -92,7 +94,7 @@ def run_oracle(w: kvgen.Workload):
     oracle.epilog(w.mode, w.x, w.slots, cache, w.cache.geom, group_size=w.group_size,
                   gamma=w.gamma, cos=w.cos, sin=w.sin, eps=w.eps, aux_bytes=aux,
                   aux_geom=None if w.aux is None else w.aux.geom, x_fp16=w.x_fp16,
-                  index_mode=w.index_mode, seq_len=w.seq_len)
+                  index_mode=w.index_mode, seq_len=w.seq_len, rope_dim=w.rope_dim)
     return cache, aux
 
 
