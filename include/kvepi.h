@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KVEPI_VERSION 110 /* 1.1.0: options (fp16 rows, index modes) */
+#define KVEPI_VERSION 120 /* 1.2.0: options (fp16 rows, index modes, rope length) */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KVEPI_API __attribute__((visibility("default")))
@@ -234,6 +234,16 @@ KVEPI_API kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
  *  seq_len     tokens per batch for the index modes other than SLOT: >= 1,
  *              dividing num_tokens; B must not exceed block_num in the
  *              BATCH and BATCH_START modes (KVEPI_ERR_SHAPE otherwise).
+ *  rope_dim    length Dk of the rope segment, 0 meaning 64.  Modes 0 and 1
+ *              fix it at 64 ("aclnnKvCompressEpilog", 接口功能: the last 64
+ *              columns; anything else is KVEPI_ERR_PARAM).  The bf16 split
+ *              mode 4 takes any even Dk in [2, 128] with Dv = d - Dk a
+ *              multiple of 8 and at least 8 ("aclnnKvRmsNormRopeCache",
+ *              shape notes: Dk + Dv = D, Dk even; KVEPI_ERR_SHAPE
+ *              otherwise): RMSNorm over Dv (gamma [Dv], the ckv cache rows
+ *              Dv elements), RoPE over Dk (cos / sin [T, Dk], the k cache
+ *              rows Dk elements).  x_row_stride stays a multiple of 8, so
+ *              a d that is not (Dk not a multiple of 8) needs padded rows.
  */
 #define KVEPI_X_BF16 0
 #define KVEPI_X_FP16 1
@@ -246,6 +256,8 @@ typedef struct kvepi_options {
   int32_t x_dtype;
   int32_t index_mode;
   int64_t seq_len;
+  int32_t rope_dim;
+  int32_t reserved; /* must be 0 */
 } kvepi_options;
 
 KVEPI_API kvepi_status kvepi_get_workspace_ex(const void *x, int64_t num_tokens, int64_t d,

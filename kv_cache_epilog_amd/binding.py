@@ -51,7 +51,8 @@ class kvepi_cache(ctypes.Structure):
 
 class kvepi_options(ctypes.Structure):
     _fields_ = [("x_dtype", ctypes.c_int32), ("index_mode", ctypes.c_int32),
-                ("seq_len", ctypes.c_int64)]
+                ("seq_len", ctypes.c_int64), ("rope_dim", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -160,22 +161,23 @@ def _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin, cache
             int(quant_mode), int(group_size), ctypes.c_float(eps)), (c, a)
 
 
-def _options(x, index_mode: int, seq_len: int) -> kvepi_options:
-    """x's dtype (fp16 or the bf16 default) and the index mode."""
+def _options(x, index_mode: int, seq_len: int, rope_dim: int = 0) -> kvepi_options:
+    """x's dtype (fp16 or the bf16 default), the index mode and the rope
+    segment length (0: 64)."""
     import torch
     return kvepi_options(KVEPI_X_FP16 if x.dtype == torch.float16 else KVEPI_X_BF16,
-                         int(index_mode), int(seq_len))
+                         int(index_mode), int(seq_len), int(rope_dim), 0)
 
 
 def kvepi_get_workspace(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
                         gamma=None, cos=None, sin=None, cache_aux=None,
                         eps: float = 1e-6, index_mode: int = KVEPI_INDEX_SLOT,
-                        seq_len: int = 0) -> int:
+                        seq_len: int = 0, rope_dim: int = 0) -> int:
     """Stage one.  x may be bf16 or (indexer modes) fp16; index_mode and
     seq_len select how slot_mapping places the tokens (see kvepi_options)."""
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
                         cache_aux, eps, index_mode)
-    opt = _options(x, index_mode, seq_len)
+    opt = _options(x, index_mode, seq_len, rope_dim)
     ws = ctypes.c_uint64()
     st = lib().kvepi_get_workspace_ex(*args, ctypes.byref(opt), ctypes.byref(ws))
     if st != KVEPI_OK:
@@ -185,7 +187,7 @@ def kvepi_get_workspace(x, slot_mapping, cache, quant_mode: int, group_size: int
 
 def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
               gamma=None, cos=None, sin=None, cache_aux=None, eps: float = 1e-6,
-              index_mode: int = KVEPI_INDEX_SLOT, seq_len: int = 0,
+              index_mode: int = KVEPI_INDEX_SLOT, seq_len: int = 0, rope_dim: int = 0,
               workspace=None, stream=None) -> None:
     """Enqueue the epilog on `stream` (a torch.cuda.Stream; default: torch's
     current stream).  Updates cache / cache_aux in place, asynchronously.
@@ -194,7 +196,7 @@ def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
     import torch
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
                         cache_aux, eps, index_mode)
-    opt = _options(x, index_mode, seq_len)
+    opt = _options(x, index_mode, seq_len, rope_dim)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     ws_ptr = None if workspace is None else _ptr(workspace)

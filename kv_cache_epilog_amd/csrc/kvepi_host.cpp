@@ -105,13 +105,26 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
                             int32_t group_size, float eps, const kvepi_options *opt,
                             kvepi_plan *p) {
   if (quant_mode == KVEPI_MODE_HIF8_FP4) return KVEPI_ERR_UNSUPPORTED;
-  const kvepi_options o = opt != nullptr ? *opt : kvepi_options{0, 0, 0};
+  const kvepi_options o = opt != nullptr ? *opt : kvepi_options{0, 0, 0, 0, 0};
   if (o.x_dtype != KVEPI_X_BF16 && o.x_dtype != KVEPI_X_FP16) return KVEPI_ERR_PARAM;
   if (o.index_mode < KVEPI_INDEX_SLOT || o.index_mode > KVEPI_INDEX_BATCH_START)
     return KVEPI_ERR_PARAM;
+  if (o.reserved != 0) return KVEPI_ERR_PARAM;
+  const int32_t rope_dim = o.rope_dim == 0 ? 64 : o.rope_dim;
   int64_t cc = 0, kc = 0, sc = 0;
-  kvepi_status st = row_geometry(quant_mode, d, group_size, &cc, &kc, &sc);
-  if (st != KVEPI_OK) return st;
+  kvepi_status st;
+  if (quant_mode == KVEPI_MODE_BF16_SPLIT && rope_dim != 64) {
+    // "aclnnKvRmsNormRopeCache", shape notes: Dk + Dv = D, Dk even
+    if (rope_dim < 2 || rope_dim % 2 != 0 || rope_dim > 128) return KVEPI_ERR_PARAM;
+    const int64_t dv = d - rope_dim;
+    if (dv < 8 || dv % 8 != 0 || d > 8192) return KVEPI_ERR_SHAPE;
+    cc = kc = dv;
+    sc = rope_dim;
+  } else {
+    if (rope_dim != 64) return KVEPI_ERR_PARAM;
+    st = row_geometry(quant_mode, d, group_size, &cc, &kc, &sc);
+    if (st != KVEPI_OK) return st;
+  }
 
   if (num_tokens < 0 || num_tokens > INT32_MAX) return KVEPI_ERR_SHAPE;
   if (num_tokens > 0 && (x == nullptr || slot_mapping == nullptr))
@@ -175,7 +188,8 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
     q.seq_len = o.index_mode == KVEPI_INDEX_SLOT ? 0 : o.seq_len;
     q.T = num_tokens;
     q.d = d;
-    q.nope = indexer ? d : d - 64;
+    q.nope = indexer ? d : d - rope_dim;
+    q.rope_dim = rope_dim;
     q.x_stride = x_row_stride;
     q.x = static_cast<const uint16_t *>(x);
     q.gamma = static_cast<const uint16_t *>(gamma);

@@ -77,6 +77,8 @@ struct KArgs {
   uint64_t sq_magic;   // row / seq_len == (row * sq_magic) >> sq_shift
   int32_t sq_shift;
   int32_t n_chunk_b;   // index entries per batch in the block-index mode
+  int32_t rope_half;   // M_SPLIT_G: rope_dim / 2 output pairs per row
+  int32_t rope_pitch;  // M_SPLIT_G: bytes per cos / sin row (2 * rope_dim)
   int32_t nwaves;      // waves in the grid
   int32_t n_groups;    // row groups (wave-iterations) = ceil(T / rows per wave)
   int32_t xcd_blocks;  // blocks per XCD for the XCD-major remap, 0 = off
@@ -215,6 +217,9 @@ __device__ __forceinline__ uint2 ld8(const uint8_t *p) {
 __device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
+__device__ __forceinline__ uint32_t ld2(const uint8_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+}
 // gamma is shared by every row: a plain (cached) load.
 __device__ __forceinline__ uint4 ld16_cached(const uint16_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
@@ -265,11 +270,15 @@ __device__ __forceinline__ void unpack8x(const uint4 w, float (&v)[8]) {
 // bytes per lane for lanes with nothing to store.
 constexpr int kSinkHalf = 16384;
 __device__ __attribute__((aligned(256))) uint8_t g_sink[2 * kSinkHalf + 64 * 16];
-enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4, M_MXFP8 = 5, M_FP8_ROW = 6 };
+enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4, M_MXFP8 = 5, M_FP8_ROW = 6,
+       M_SPLIT_G = 7 /* the bf16 split with a rope segment of another length */ };
 // the indexer modes quantise the whole row (no rope segment)
 constexpr bool whole_row(int m) { return m == M_MXFP4 || m == M_MXFP8 || m == M_FP8_ROW; }
 // modes writing a second cache (scales or the k rows)
 constexpr bool has_aux(int m) { return m != M_FP8_BF16 && m != M_FP8_E8M0; }
+// the rope segment: the last 64 columns, or (M_SPLIT_G) rope_dim columns
+constexpr bool fixed_rope(int m) { return !whole_row(m) && m != M_SPLIT_G; }
+constexpr bool gen_rope(int m) { return m == M_SPLIT_G; }
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
 // y[32h + 2p] and y[32h + 2p + 1] from the interleaved pairs 2p and 2p+1
@@ -278,6 +287,9 @@ constexpr bool has_aux(int m) { return m != M_FP8_BF16 && m != M_FP8_E8M0; }
 template <int L>
 struct RopeShape {
   static constexpr int TPL = L >= 32 ? 1 : 32 / L;  // tasks per lane
+  // rope segments of another length (M_SPLIT_G): one task per output pair
+  // (y[p], y[p + Dk/2]), up to 64 pairs (Dk <= 128)
+  static constexpr int TPG = (64 + L - 1) / L;
 };
 
 // Chunk layout: lane li of a row owns C chunks of 16 bytes (8 values),
@@ -292,12 +304,16 @@ __device__ __forceinline__ int chunk_of(int li, int j) {
 
 template <int MODE, bool ROPE, int L, int C>
 struct RowBuf {
-  static constexpr bool HAS_ROPE_SEG = !whole_row(MODE);
+  static constexpr bool HAS_ROPE_SEG = fixed_rope(MODE);
   static constexpr int TPL = RopeShape<L>::TPL;
+  static constexpr int TPG = gen_rope(MODE) ? RopeShape<L>::TPG : 1;
   uint4 xw[C];
   uint2 rx[HAS_ROPE_SEG ? TPL : 1];             // x[4p .. 4p+3] (or 2 copied values)
   uint32_t rc[HAS_ROPE_SEG && ROPE ? TPL : 1];  // cos pair
   uint32_t rs[HAS_ROPE_SEG && ROPE ? TPL : 1];  // sin pair
+  uint32_t gx[TPG];  // M_SPLIT_G: x[2p], x[2p+1]
+  uint32_t gc[TPG];  // cos[p] | cos[p + Dk/2] << 16
+  uint32_t gs[TPG];  // sin[p] | sin[p + Dk/2] << 16
 };
 
 // Loads one row into registers.  xr, cr and sr are the wave-uniform bases of
@@ -337,6 +353,20 @@ __device__ __forceinline__ void load_row(const KArgs &a, const uint8_t *xr, cons
       }
     }
   }
+  if constexpr (gen_rope(MODE)) {
+    // task p (lanes past the last pair read pair 0 again)
+    const uint32_t ro = xo + 2u * (uint32_t)a.nseg;
+    const uint32_t half = (uint32_t)a.rope_half;
+    const uint32_t cb = (uint32_t)a.rope_pitch * dr;
+#pragma unroll
+    for (int k = 0; k < RowBuf<MODE, ROPE, L, C>::TPG; ++k) {
+      const uint32_t p0 = (uint32_t)(li + L * k);
+      const uint32_t p = p0 < half ? p0 : 0u;
+      b.gx[k] = ld4(xr + (ro + 4u * p));
+      b.gc[k] = ld2(cr + (cb + 2u * p)) | (ld2(cr + (cb + 2u * (p + half))) << 16);
+      b.gs[k] = ld2(sr + (cb + 2u * p)) | (ld2(sr + (cb + 2u * (p + half))) << 16);
+    }
+  }
 }
 
 // A computed row waiting to be stored: destination pointers, code words
@@ -346,7 +376,7 @@ struct RowOut {
   uint8_t *p0, *p1;
   uint4 w[C];
   uint32_t sb[C];
-  uint32_t ry[whole_row(MODE) ? 1 : RopeShape<L>::TPL];
+  uint32_t ry[whole_row(MODE) ? 1 : (gen_rope(MODE) ? RopeShape<L>::TPG : RopeShape<L>::TPL)];
 };
 
 // E4M3 codes of v / 2^E (E the group's e8m0 exponent, -127..127) as two
@@ -507,6 +537,18 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int j = 0; j < C; ++j) o.w[j] = yw[j];
 #pragma unroll
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
+  } else if constexpr (MODE == M_SPLIT_G) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) o.w[j] = yw[j];
+    // y[p] = a c[p] - b s[p], y[p + Dk/2] = b c[p + Dk/2] + a s[p + Dk/2]
+    // (both products exact)
+#pragma unroll
+    for (int k = 0; k < RowBuf<MODE, ROPE, L, C>::TPG; ++k) {
+      const float xa = lo_f(b.gx[k]), xb = hi_f(b.gx[k]);
+      const float c0 = lo_f(b.gc[k]), c1 = hi_f(b.gc[k]);
+      const float s0 = lo_f(b.gs[k]), s1 = hi_f(b.gs[k]);
+      o.ry[k] = pack_bf16(__builtin_fmaf(xa, c0, -xb * s0), __builtin_fmaf(xb, c1, xa * s1));
+    }
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
@@ -706,7 +748,21 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
   const int c_al = FAST ? 16 : a.c_align;
   const int a_al = FAST ? 4 : a.a_align;
   uint8_t *lsink = g_sink + 2 * kSinkHalf + 16 * lane;
-  if constexpr (MODE == M_SPLIT) {
+  if constexpr (MODE == M_SPLIT_G) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = chunk_of<L>(li, j);
+      st_u128((FAST || c < a.nchunk) ? o.p0 + 16 * c : lsink, o.w[j], c_al);
+    }
+    const int half = a.rope_half;
+#pragma unroll
+    for (int k = 0; k < RowBuf<MODE, ROPE, L, C>::TPG; ++k) {
+      const int p = li + L * k;
+      const bool in = p < half;
+      st_u16(in ? o.p1 + 2 * p : lsink + 4, o.ry[k], 2);
+      st_u16(in ? o.p1 + 2 * (p + half) : lsink + 6, o.ry[k] >> 16, 2);
+    }
+  } else if constexpr (MODE == M_SPLIT) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int c = chunk_of<L>(li, j);
@@ -884,8 +940,9 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   auto issue = [&](const IterInfo<R> &t, RowBuf<MODE, ROPE, L, C> &b) {
     const uint32_t dr = lane_live(t) ? t.g * R + sub - t.first : 0u;
     const uint8_t *xr = reinterpret_cast<const uint8_t *>(a.x) + (uint64_t)t.first * a.x_pitch;
-    const uint8_t *cr = reinterpret_cast<const uint8_t *>(a.cos) + (uint64_t)t.first * 128;
-    const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)t.first * 128;
+    const uint64_t rp = gen_rope(MODE) ? (uint64_t)a.rope_pitch : 128u;  // cos / sin row bytes
+    const uint8_t *cr = reinterpret_cast<const uint8_t *>(a.cos) + (uint64_t)t.first * rp;
+    const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)t.first * rp;
     load_row<MODE, NORM, ROPE, L, C, FAST>(a, xr, cr, sr, dr, li, b);
   };
   // issues the loads of iteration j's own rows, whatever their slots (rows
@@ -894,8 +951,9 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
     const uint32_t base = j < n_it ? ((uint32_t)wave + (uint32_t)j * (uint32_t)a.nwaves) * R : 0u;
     const uint32_t dr = min((uint32_t)sub, (uint32_t)a.T - 1u - base);
     const uint8_t *xr = reinterpret_cast<const uint8_t *>(a.x) + (uint64_t)base * a.x_pitch;
-    const uint8_t *cr = reinterpret_cast<const uint8_t *>(a.cos) + (uint64_t)base * 128;
-    const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)base * 128;
+    const uint64_t rp = gen_rope(MODE) ? (uint64_t)a.rope_pitch : 128u;
+    const uint8_t *cr = reinterpret_cast<const uint8_t *>(a.cos) + (uint64_t)base * rp;
+    const uint8_t *sr = reinterpret_cast<const uint8_t *>(a.sin) + (uint64_t)base * rp;
     load_row<MODE, NORM, ROPE, L, C, FAST>(a, xr, cr, sr, dr, li, b);
   };
   // computes iteration j's rows and stores them (after the caller has issued
@@ -1067,6 +1125,8 @@ kfn_t pick(int mode, bool norm, bool rope, bool xf16, int L, int C, int fast) {
       return pick_indexer<M_MXFP8>(L, C, fast, xf16);
     case M_FP8_ROW:
       return pick_indexer<M_FP8_ROW>(L, C, fast, xf16);
+    case M_SPLIT_G:
+      return pick_layout<M_SPLIT_G, true, true>(L, C, fast);
     default:
       return pick_layout<M_SPLIT, true, true>(L, C, fast);
   }
@@ -1162,6 +1222,8 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   a.c_align = p.c_align;
   a.a_align = p.aux != nullptr ? p.a_align : 16;
   a.eps = p.eps;
+  a.rope_half = (int32_t)(p.rope_dim / 2);
+  a.rope_pitch = (int32_t)(2 * p.rope_dim);
   a.nseg_f = (float)p.nope;
   a.inv_nseg = (p.nope & (p.nope - 1)) == 0 ? 1.0f / (float)p.nope : 0.0f;
 
@@ -1181,7 +1243,9 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   const bool aligned = L * C == a.nchunk && a.c_align >= 16 &&
                        (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
   const int fast = !aligned ? 0 : (p.mode == KVEPI_MODE_FP8_BF16SCALE && L == 32) ? 2 : 1;
-  kfn_t fn = pick(p.mode, p.norm, p.rope, p.x_fp16, L, C, fast);
+  // the bf16 split with a rope segment of another length than 64
+  const int kmode = p.mode == KVEPI_MODE_BF16_SPLIT && p.rope_dim != 64 ? (int)M_SPLIT_G : p.mode;
+  kfn_t fn = pick(kmode, p.norm, p.rope, p.x_fp16, L, C, fast);
   size_t lds = p.norm ? (size_t)L * C * 32 : 0;  // gamma as fp32, 32 KB at most
   if (fast == 2) lds += (size_t)4 * (64 / L) * p.kv_cache_col;  // staging, 4 waves
 

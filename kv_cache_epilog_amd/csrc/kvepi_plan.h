@@ -14,6 +14,7 @@ struct kvepi_plan {
   bool x_fp16;   // x holds fp16 values (indexer modes)
   int32_t index_mode;  // KVEPI_INDEX_*
   int64_t seq_len;     // tokens per batch (index modes other than SLOT)
+  int32_t rope_dim;    // rope segment length (64 except in the bf16 split mode)
   int64_t T, d, nope, x_stride;
   const uint16_t *x, *gamma, *cos, *sin;
   const int32_t *slots;

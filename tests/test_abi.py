@@ -40,7 +40,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.kvepi_version() == 110
+    assert B.kvepi_version() == 120
     for code, name in B.STATUS_NAMES.items():
         assert B.kvepi_status_str(code).startswith(name)
     assert "UNKNOWN" in B.kvepi_status_str(99)
@@ -212,22 +212,23 @@ def call_ex(stage, opt, **kw):
     mode = kw.pop("mode", 0)
     group = kw.pop("group", 64)
     slots = kw.pop("slots", P16B)
+    gamma, cos, sin = kw.pop("gamma", None), kw.pop("cos", None), kw.pop("sin", None)
     assert not kw
     ap = ctypes.byref(aux) if aux is not None else None
     op = ctypes.byref(opt) if opt is not None else None
     if stage == 1:
         ws = ctypes.c_uint64(7)
-        st = L.kvepi_get_workspace_ex(x, T, d, d, None, None, None, slots, ctypes.byref(cache),
+        st = L.kvepi_get_workspace_ex(x, T, d, d, gamma, cos, sin, slots, ctypes.byref(cache),
                                       ap, mode, group, ctypes.c_float(1e-6), op,
                                       ctypes.byref(ws))
         return st, ws.value
-    st = L.kvepi_run_ex(x, T, d, d, None, None, None, slots, ctypes.byref(cache), ap, mode,
+    st = L.kvepi_run_ex(x, T, d, d, gamma, cos, sin, slots, ctypes.byref(cache), ap, mode,
                         group, ctypes.c_float(1e-6), op, None, 0, None)
     return st, None
 
 
-def O(x_dtype=0, index_mode=0, seq_len=0):
-    return B.kvepi_options(x_dtype, index_mode, seq_len)
+def O(x_dtype=0, index_mode=0, seq_len=0, rope_dim=0, reserved=0):
+    return B.kvepi_options(x_dtype, index_mode, seq_len, rope_dim, reserved)
 
 
 def test_ex_valid_calls():
@@ -246,6 +247,13 @@ def test_ex_valid_calls():
         assert call_ex(1, O(index_mode=im, seq_len=8)) == (0, 0)
     assert call_ex(1, O(index_mode=2, seq_len=64)) == (0, 0)
     assert call_ex(1, O(index_mode=1, seq_len=1), T=0, x=None, slots=None) == (0, 0)
+    # the split mode with a 32-column rope segment: ckv rows 544, k rows 32
+    assert call_ex(1, O(rope_dim=32), d=576, mode=4, gamma=P16C, cos=P16D,
+                   sin=P16D + 0x1000, cache=_cache(hd=544),
+                   aux=_cache(data=0x70000, hd=32)) == (0, 0)
+    assert call_ex(1, O(rope_dim=64), d=576, mode=4, gamma=P16C, cos=P16D,
+                   sin=P16D + 0x1000, cache=_cache(hd=512),
+                   aux=_cache(data=0x70000, hd=64)) == (0, 0)
 
 
 BAD_EX = [
@@ -258,6 +266,11 @@ BAD_EX = [
     ("more batches than blocks", O(index_mode=1, seq_len=4), {}, 2),
     ("batch start longer than a block", O(index_mode=3, seq_len=32), dict(T=64), 2),
     ("more start batches than blocks", O(index_mode=3, seq_len=2), {}, 2),
+    ("reserved field set", O(reserved=1), {}, 4),
+    ("rope length in mode 0", O(rope_dim=32), {}, 4),
+    ("odd rope length in the split mode", O(rope_dim=33), dict(d=576, mode=4), 4),
+    ("rope length above 128", O(rope_dim=130), dict(d=578, mode=4), 4),
+    ("Dv not a multiple of 8", O(rope_dim=36), dict(d=576, mode=4), 2),
 ]
 
 

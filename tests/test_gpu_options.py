@@ -147,3 +147,44 @@ def test_index_modes_many_iterations_per_wave(index_mode, waves, monkeypatch):
 def test_fp16_with_block_index():
     w = _indexed(5, 256, 2, 6, 45, 8, 6 * 6 + 2, seed=70, x16=True)
     assert check(w) == 0
+
+
+# ---- rope segments of other lengths in the bf16 split mode ------------------------------
+
+@pytest.mark.parametrize("dk,dv", [(2, 64), (6, 64), (32, 544), (128, 512), (96, 512),
+                                   (10, 1024), (64, 512), (40, 8), (126, 200)])
+def test_split_rope_lengths(dk, dv):
+    d = dv + dk
+    T, bs = 300, 7
+    nblk = (T + bs - 1) // bs + 2
+    cache = CacheSpec(nblk, bs, dv, bs * dv + 8, 2)
+    aux = CacheSpec(nblk, bs, dk, bs * dk + 2, 2)
+    w = kvgen.make(f"split_dk{dk}", 4, T, d, seed=dk + dv, cache=cache, aux=aux, norm=True,
+                   rope=True, row_sigma=1.0, skip_frac=0.1, rope_dim=dk)
+    # rows of x start 16-byte aligned: a d that is not a multiple of 8 takes
+    # padded rows (a row stride above d)
+    check(w, x_pad=(-d) % 8)
+
+
+@pytest.mark.parametrize("waves", [4, 64])
+def test_split_rope_length_many_iterations(waves, monkeypatch):
+    monkeypatch.setenv("KVEPI_MAX_WAVES", str(waves))
+    dk, dv, T, bs = 32, 512, 2001, 16
+    nblk = (T + bs - 1) // bs + 2
+    w = kvgen.make("split_dk32_it", 4, T, dv + dk, seed=77, cache=CacheSpec(nblk, bs, dv, bs * dv, 2),
+                   aux=CacheSpec(nblk, bs, dk, bs * dk, 2), norm=True, rope=True, rope_dim=dk)
+    check(w)
+
+
+def test_split_rope_length_with_block_index():
+    dk, dv = 48, 256
+    B, S, bs = 4, 37, 8
+    nc = -(-S // bs)
+    bn = B * nc + 2
+    w = kvgen.make("split_dk48_blk", 4, B * S, dv + dk, seed=78,
+                   cache=CacheSpec(bn, bs, dv, bs * dv, 2), aux=CacheSpec(bn, bs, dk, bs * dk, 2),
+                   norm=True, rope=True, rope_dim=dk)
+    w.slots = kvgen.index_array(np.random.default_rng(79), 2, B, S, bn, bs, 0.1)
+    w.index_mode = 2
+    w.seq_len = S
+    check(w)
