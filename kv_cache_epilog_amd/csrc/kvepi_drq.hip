@@ -97,12 +97,14 @@ __device__ __forceinline__ void unpack(const uint32_t (&w)[V / 2], float (&v)[V]
 // fp32 -> the 16-bit output type, round to nearest even (v_cvt_pk_bf16_f32 /
 // v_cvt_f16_f32; tests/hw_check.hip compares both with a software rounding
 // for every fp32 value)
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 template <int DT>
 __device__ __forceinline__ uint32_t pack16(float a, float b) {
   if constexpr (DT == KVEPI_DT_FP16) {
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(unsigned short, ha) |
-           ((uint32_t)__builtin_bit_cast(unsigned short, hb) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
   } else {
     return kvepi::pack_bf16_rn(a, b);
   }
@@ -187,6 +189,8 @@ __device__ __forceinline__ void dequant(const DArgs &a, uint32_t t, int64_t h, f
 }
 
 // step 4 for V channels: rint(v / scale + offset) saturated to int8, packed
+// (IEEE division: a reciprocal with one correction, guarded to the range
+// where it is exact, measured no faster here)
 template <int V>
 __device__ __forceinline__ void quant(const float (&v)[V], const float *sc, const float *of,
                                       uint32_t (&out)[V / 4]) {
@@ -236,10 +240,18 @@ __global__ __launch_bounds__(256) void drq_kernel(const DArgs a) {
     unpack<OT, V>(w, s1);
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      const float p0 = x0[k] * c0[k], q0 = x1[k] * s0[k];
-      const float p1 = x1[k] * c1[k], q1 = x0[k] * s1[k];
-      y0[k] = p0 - q0;
-      y1[k] = p1 + q1;
+      if constexpr (OT == KVEPI_DT_FP16) {
+        // fp16 products are exact in fp32 (22 significant bits, never
+        // below 2^-48), so one FMA gives the rounded sum of the two
+        y0[k] = __builtin_fmaf(x0[k], c0[k], -(x1[k] * s0[k]));
+        y1[k] = __builtin_fmaf(x1[k], c1[k], x0[k] * s1[k]);
+      } else {
+        // bf16 products can fall below the fp32 normal range: round each
+        const float p0 = x0[k] * c0[k], q0 = x1[k] * s0[k];
+        const float p1 = x1[k] * c1[k], q1 = x0[k] * s1[k];
+        y0[k] = p0 - q0;
+        y1[k] = p1 + q1;
+      }
     }
   } else {
 #pragma unroll

@@ -87,3 +87,26 @@ def test_saturation_and_ties():
 def oracle_bits(v):
     import kvgen
     return kvgen.to_bf16(v)
+
+
+@pytest.mark.parametrize("case", ["tiny_values", "tiny_scales", "huge_values", "huge_scales"])
+def test_division_paths(case):
+    # waves whose values or scales leave the range of the fast division take
+    # IEEE division; both must give the oracle's codes
+    c = make_case(900, T=256, nq=1, nkv=1, D=64, x_dtype=BF, out_dtype=BF, skip=0.0)
+    rng = np.random.default_rng(10)
+    x = c.x.copy()
+    if case == "tiny_values":
+        x[::3, 64:] = oracle_bits(rng.standard_normal((len(x[::3]), 128)) * 1e-12)
+        c.scale_k[:] = 1e-13
+        c.scale_v[:] = 1e-13
+    elif case == "tiny_scales":
+        c.scale_k[::5] = 1e-32
+        c.scale_v[::7] = 3e-33
+    elif case == "huge_values":
+        x[::4, 64:] = oracle_bits(rng.standard_normal((len(x[::4]), 128)) * 1e25)
+    else:
+        c.scale_k[::3] = 1e31
+        c.scale_v[::2] = 5e30
+    c.x = x
+    compare(c, case)
