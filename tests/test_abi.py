@@ -280,3 +280,13 @@ def test_ex_rejects(desc, opt, kw, status, stage):
     st, _ = call_ex(stage, opt, **kw)
     assert st == status, (desc, B.kvepi_status_str(st))
 
+
+
+def test_valid_run_without_a_device_reports_runtime_error():
+    # on a host without a GPU a valid call reaches the launch, which the HIP
+    # runtime refuses: KVEPI_ERR_RUNTIME, not a crash
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call(2) == (7, None)
+    assert call_ex(2, O(index_mode=2, seq_len=8)) == (7, None)

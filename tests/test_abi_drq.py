@@ -92,3 +92,10 @@ def test_null_params_and_workspace_pointer():
     ws = ctypes.c_uint64()
     assert L.kvepi_drq_get_workspace(None, ctypes.byref(ws)) == 1
     assert L.kvepi_drq_get_workspace(ctypes.byref(params()), None) == 1
+
+
+def test_valid_run_without_a_device_reports_runtime_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call(2, params()) == (7, None)
