@@ -3,25 +3,29 @@
 // One kernel template covers every mode.  A token row is handled by a group
 // of L lanes of one 64-lane wavefront (64/L rows per wave-iteration: L = 32,
 // two rows per wave, for the d = 576 rows; L = 16, four rows, for the d = 128
-// indexer rows).  Each lane owns C 16-byte chunks of 8 bf16 values, chunk
+// indexer rows).  Each lane owns C 16-byte chunks of 8 16-bit values, chunk
 // li + L*j, so every load instruction reads L*16 contiguous bytes of a row.
 // The path is bound by HBM bandwidth; the design keeps the VALU work and the
 // number of memory instructions per row small:
 //  - waves are persistent (one block per resident slot of the device); each
 //    wave loads its slots ahead and issues the loads of the row two steps
 //    ahead before storing the current one (two register sets);
-//  - the rope segment is spread over 32 lanes (one output pair each);
+//  - the 64-column rope segment is spread over 32 tasks of two outputs each
+//    (a rope segment of another length, in the bf16 split mode, over one
+//    task per output pair);
 //  - codes come from the gfx950 converts v_cvt_pk_fp8_f32 /
 //    v_cvt_scalef32_pk_fp8_f32 / v_cvt_scalef32_pk_fp4_f32, which round to
 //    nearest even exactly like the reference encoders over the value ranges
-//    used here (|q| <= 448 for FP8, |q| <= 6 for FP4, power-of-two scales in
-//    [2^-100, 2^100]); outside those ranges a group falls back to software
-//    encoding.
+//    used here (|q| <= 456 for FP8 -- the unscaled convert stops saturating
+//    at 464 --, |q| <= 6 for FP4, power-of-two scales in [2^-100, 2^100]);
+//    outside those ranges a group falls back to software encoding.
 //
 // Steps per row (sources cited by page title and section):
-//  1. slot = slot_mapping[t]; -1 (or any value outside [0, num_slots)) skips
-//     the token: nothing is read or written for it
-//     ("aclnnKvCompressEpilog", 约束说明).
+//  1. The token's slot: slot_mapping[t], or from the index modes (a row of
+//     the token's batch, one block per chunk of block_size tokens, a start
+//     row per batch; "aclnnKvRmsNormRopeCache", index constraints); -1, or
+//     any value that would leave the cache, skips the token: nothing is
+//     written for it ("aclnnKvCompressEpilog", 约束说明).
 //  2. RMSNorm of the nope segment ("aclnnKvRmsNormRopeCache", 计算公式 (2)):
 //     squares summed as a balanced pairwise tree -- within a lane over its 8
 //     values, then across lanes by a DPP / ds_swizzle butterfly whose pairing
@@ -32,15 +36,22 @@
 //     (Markstein), which returns the correctly rounded quotient for a bf16
 //     numerator and a normal result -- a row falls back to full division when
 //     that cannot be guaranteed.
-//  3. Interleaved RoPE of the last 64 columns, half-split output
+//  3. Interleaved RoPE of the rope segment (the last 64 columns, or Dk
+//     columns in the bf16 split mode), half-split output
 //     ("aclnnKvRmsNormRopeCache", 计算公式 (1)).
-//  4. Per-group amax (DPP max over the 8 or 4 lanes of a group), the scale
-//     ("aclnnKvCompressEpilog", 计算公式: amax / 448 as bf16, or the e8m0
-//     power of two rounded up; "indexer_quant_cache": e8m0 over groups of 32
-//     with FP4 max 6) and the codes, round-to-nearest-even with saturation.
-//  5. Stores of exactly kvCacheCol bytes at the slot's row; the widest store
-//     the row alignment allows is used (16/8/4/2/1 bytes), so odd headDim
-//     such as 323 works.
+//  4. Per-group amax (DPP max over the lanes of a group, or of the whole row
+//     for the per-row FP8 mode), the scale ("aclnnKvCompressEpilog",
+//     计算公式: amax / 448 as bf16, or the e8m0 power of two rounded up;
+//     "indexer_quant_cache": e8m0 over groups of 32 with FP4 max 6 or FP8
+//     max 448, or amax / 448 in fp32 for the whole row) and the codes,
+//     round-to-nearest-even with saturation.  The indexer modes also read
+//     fp16 rows ("indexer_quant_cache", 接口功能).
+//  5. Stores of exactly kvCacheCol bytes at the slot's row (plus the scale
+//     row or the k row in the second cache).  Mode 0 rows laid out as one or
+//     two chunks on each of 32 lanes (d = 320 and d = 576, 16-byte aligned
+//     rows) are assembled in LDS and leave as one 16-byte store per lane;
+//     otherwise the widest store the row alignment allows is used
+//     (16/8/4/2/1 bytes), so odd headDim such as 323 works.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -401,8 +412,9 @@ __device__ __forceinline__ void codes_e8m0_fp8(const float (&v)[8], int E, uint3
   }
 }
 
-// E4M3 codes of eight quotients, each in [-512, 512] or NaN (hardware
-// convert: round to nearest even, saturating at 448).
+// E4M3 codes of eight quotients, each of magnitude at most 456 or NaN (the
+// hardware convert rounds to nearest even and, below 464, saturates to 448;
+// tests/hw_check.hip).
 __device__ __forceinline__ void codes_fp8(const float (&q)[8], uint32_t (&cw)[2]) {
   int w0 = 0, w1 = 0;
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], w0, false);
@@ -822,9 +834,10 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
   }
 }
 
-// Wave-uniform description of one wave-iteration (R rows): which rows are
-// live, the first live row (the one skipped tokens read instead of their
-// own) and every row's slot.
+// Description of one wave-iteration (R rows): which rows are live, the first
+// live row (the one skipped tokens read instead of their own) and every
+// row's slot, all wave-uniform for R <= 2.  For R > 2 each lane keeps its own
+// row's slot (own) and only its own row's bit in live; sl is unused.
 template <int R>
 struct IterInfo {
   uint32_t live;   // bit r: row r is live
@@ -1239,7 +1252,8 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   const int64_t n_groups = (p.T + rows_per_wave - 1) / rows_per_wave;
   // FAST: whole chunks per lane and 16-byte aligned rows (4-byte aligned k
   // rows in the bf16 split mode); stores then need no alignment dispatch
-  // 2: mode 0 rows of at most 64 chunks also assemble their rows in LDS
+  // 2: mode 0 rows laid out on 32 lanes (one or two chunks each) also
+  // assemble their rows in LDS
   const bool aligned = L * C == a.nchunk && a.c_align >= 16 &&
                        (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
   const int fast = !aligned ? 0 : (p.mode == KVEPI_MODE_FP8_BF16SCALE && L == 32) ? 2 : 1;
