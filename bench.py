@@ -34,10 +34,11 @@ DRQ_SRC = os.path.join(ROOT, "kv_cache_epilog_amd", "csrc", "kvepi_drq.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def algorithmic_bytes(w: kvgen.Workload) -> int:
+def algorithmic_bytes(w: kvgen.Workload, dense: bool = False) -> int:
     """Bytes the method must move: 4 B slot per token; for every hit row the
     x row (plus its cos and sin rows with RoPE) and the bytes written; gamma
-    once."""
+    once.  dense: the x (and cos / sin) rows of skipped tokens counted as
+    read too."""
     from kv_cache_epilog_amd import kvepi_row_bytes
     hits = w.hits
     x_row = 2 * w.d
@@ -51,7 +52,8 @@ def algorithmic_bytes(w: kvgen.Workload) -> int:
         _, kc, _ = kvepi_row_bytes(w.mode, w.d, w.group_size)
         written = kc
     gamma = 2 * (w.d - 64) if w.gamma is not None else 0
-    return 4 * w.T + hits * (x_row + rope + written) + gamma
+    read_rows = w.T if dense else hits
+    return 4 * w.T + read_rows * (x_row + rope) + hits * written + gamma
 
 
 def kernel_hash(src: str = KERNEL_SRC) -> str:
@@ -140,6 +142,30 @@ def copy_probe(mib: int, steps: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "launches": steps}), flush=True)
+
+
+def copy_ceiling(dev, stream, mib: int = 512, warmup: int = 20, steps: int = 50):
+    """Achieved bandwidth of a plain device-to-device copy (torch's copy_,
+    the runtime's copy kernel) of mib MiB, timed in the same run with HIP
+    events on the launch stream: the practical ceiling that the kernel's
+    effective bandwidth is also compared with.  Bytes = read + written."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            dst.copy_(src)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def upload(w: kvgen.Workload, dev):
@@ -288,8 +314,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name),
-                     "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms_kernel},
+                     "algorithmic_bytes_per_launch": abytes,
+                     "dense_bytes_per_launch": algorithmic_bytes(w, dense=True),
+                     "kernel_ms_mean": ms_kernel},
     }
+    cc = copy_ceiling(dev, stream)
+    result["copy_ceiling"] = {"achieved": cc, "unit": "GB/s", "kernel": "device copy, 512 MiB",
+                              "frac": achieved / cc}
     if not args.no_cpu:
         n, dt, ocache, oaux = cpu_baseline(w, args.cpu_seconds)
         result["cpu_baseline"] = {
@@ -389,6 +420,9 @@ def main_drq(args):
                      "traffic": measured_traffic(args.drq, DRQ_SRC),
                      "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms},
     }
+    cc = copy_ceiling(dev, stream)
+    result["copy_ceiling"] = {"achieved": cc, "unit": "GB/s", "kernel": "device copy, 512 MiB",
+                              "frac": achieved / cc}
     if not args.no_cpu:
         import oracle
         kc = np.full(bn * stride, 0xAB, np.uint8)

@@ -1,0 +1,64 @@
+"""Host-side checks of bench.py (no GPU): the algorithmic byte counts that
+the effective bandwidth is computed from, and the one-GPU guard.
+
+The byte counts follow the row sizes of "aclnnKvCompressEpilog" (约束说明:
+kvCacheCol = (d - 64) + 128 + scale bytes, padded to 32 in mode 0) and of
+indexer_quant_cache (MX-FP4 rows of d/2 bytes plus d/32 scale bytes): per
+hit row the x row (and cos / sin rows when RoPE is on) is read and the
+cache row written; every token reads its 4-byte slot; gamma is read once.
+The expected totals below are that sum written out by hand for each
+workload, not a call of the function under test."""
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+sys.path.insert(0, str(ROOT))
+
+import bench  # noqa: E402
+import kvgen  # noqa: E402
+
+
+def _hand_count(T, hits, read_row, write_row, gamma_bytes=0):
+    return 4 * T + hits * (read_row + write_row) + gamma_bytes
+
+
+@pytest.mark.parametrize("cfg, expected", [
+    # mode-1 prefill d = 576: x row 1152 B, cache row (576-64)+128+8 = 648 B
+    (2, _hand_count(16384, 16056, 1152, 648)),
+    # MX-FP4 indexer d = 128: x row 256 B, 64 code bytes + 4 e8m0 scale bytes
+    (3, _hand_count(131072, 129761, 256, 64 + 4)),
+    # fused d = 576: x 1152 B + cos 128 B + sin 128 B, 672-byte cache row,
+    # gamma of 512 bf16 values
+    (4, _hand_count(262144, 254280, 1152 + 256, 672, 2 * 512)),
+])
+def test_algorithmic_bytes(cfg, expected):
+    w = kvgen.config(cfg)
+    assert bench.algorithmic_bytes(w) == expected
+
+
+def test_published_totals():
+    # the same totals as plain numbers (bytes per launch)
+    assert _hand_count(16384, 16056, 1152, 648) == 28_966_336
+    assert _hand_count(131072, 129761, 256, 68) == 42_566_852
+    assert _hand_count(262144, 254280, 1408, 672, 1024) == 529_952_000
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "1 GPU" in r.stderr or "--gpus 1" in r.stderr
+
+
+def test_traffic_needs_matching_source():
+    # measured traffic is reported only for the kernel source it was taken on
+    assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_dense_count_adds_skipped_rows():
+    w = kvgen.config(3)
+    skipped = w.T - w.hits
+    assert bench.algorithmic_bytes(w, dense=True) - bench.algorithmic_bytes(w) == skipped * 256
