@@ -114,6 +114,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// y rounded to bf16 (nearest even) and read back as fp32: a zero low half
+// next to the bf16 code makes the word that value's fp32 bits.
+__device__ __forceinline__ float round_bf16(float y) {
+  return __uint_as_float(pack_bf16(0.0f, y));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
@@ -416,7 +422,8 @@ __device__ __forceinline__ void codes_e8m0_fp8(const float (&v)[8], int E, uint3
 // hardware convert rounds to nearest even and, below 464, saturates to 448;
 // tests/hw_check.hip).
 __device__ __forceinline__ void codes_fp8(const float (&q)[8], uint32_t (&cw)[2]) {
-  int w0 = 0, w1 = 0;
+  // (any initial words: the two converts of each fill both halves)
+  int w0 = __builtin_bit_cast(int, q[0]), w1 = __builtin_bit_cast(int, q[4]);
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], w0, false);
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], w1, false);
@@ -432,6 +439,40 @@ __device__ __forceinline__ float div448_fast(float m) {
   constexpr float H448 = 1.0f / 448.0f;
   constexpr float L448 = (float)(1.0 / 448.0 - (double)H448);
   return __builtin_fmaf(m, H448, m * L448);
+}
+
+// Mode 0 codes of one group of 8 values per lane (v, group maximum m);
+// returns the stored bf16 scale bits.  The scale is amax / 448 (IEEE),
+// stored as bf16, and the codes divide by the stored value.
+// fast (callers pass m in [2^-71, 2^100], which keeps m / 448 and the
+// stored scale inside the range of the fast division and reciprocal):
+// m / 448 = fma(m, H, m * Lo) with H + Lo a double-length 1/448, and v / su =
+// fma(v, rs, v * rl) with rs + rl a double-length 1/su: both are exactly the
+// IEEE quotient for bf16 operands (their distance to a rounding boundary is
+// far above the error), except that v / su below 2^-100 may differ -- where
+// every code is +-0.  rs is rounded downwards so that rl >= 0 and a zero v
+// keeps its sign.  Otherwise the group divides exactly (an infinite scale,
+// from an infinite RMSNorm output, gives +-0 for finite values and the NaN
+// code for inf / inf).
+__device__ __forceinline__ uint32_t codes_fp8_bf16scale(const float (&v)[8], float m, bool fast,
+                                                        uint32_t (&cw)[2]) {
+  const float su = round_bf16(fast ? div448_fast(m) : m / 448.0f);
+  if (fast) {
+    float rs = rcp_rn(su);
+    if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
+    const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
+    float qv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[t], rs, v[t] * rl);
+    codes_fp8(qv, cw);
+  } else {
+    uint32_t q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = su > 0.0f ? enc_e4m3_sw(v[t] / su) : 0u;
+    cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+    cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+  }
+  return __float_as_uint(su) >> 16;
 }
 
 template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST, bool XF16>
@@ -635,55 +676,52 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
     }
     o.sb[0] = __float_as_uint(s);
-  } else {  // FP8 modes
+  } else if constexpr (MODE == M_FP8_E8M0) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
       unpack8(yw[j], v);
-      float m = amax8(v);
-      m = grp_max<8>(m);  // 64 values = 8 lanes
+      const float m = grp_max<8>(amax8(v));  // 64 values = 8 lanes
+      const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
       uint32_t cw[2];
-      uint32_t sbits;
-      if constexpr (MODE == M_FP8_E8M0) {
-        const int E = e8m0_exp<8, 0x600000u>(m);  // FP8 max 448 = 1.75 * 2^8
-        sbits = (uint32_t)(E + 127);
-        codes_e8m0_fp8(v, E, cw);
-      } else {
-        // scale = amax / 448 (IEEE), stored as bf16; codes divide by the
-        // stored value.  Far from 1 a residual or the reciprocal of the fast
-        // division could leave the normal range; such groups divide exactly
-        // (an infinite scale, from an infinite RMSNorm output, gives +-0 for
-        // finite values and the NaN code for inf / inf).
-        // m in [2^-71, 2^100] keeps m / 448 and the stored scale inside the
-        // range of the fast division and reciprocal
-        // Fast path: m / 448 = fma(m, H, m * Lo) with H + Lo a double-length
-        // 1/448, and v / su = fma(v, rs, v * rl) with rs + rl a double-length
-        // 1/su: both are exactly the IEEE quotient for bf16 operands (their
-        // distance to a rounding boundary is far above the error), except
-        // that v / su below 2^-100 may differ -- where every code is +-0.
-        // rs is rounded downwards so that rl >= 0 and a zero v keeps its sign.
-        const bool fastq = m >= 0x1p-71f && m <= 0x1p+100f;
-        const float s32 = fastq ? div448_fast(m) : m / 448.0f;
-        sbits = pack_bf16(s32, 0.0f) & 0xFFFFu;
-        const float su = __uint_as_float(sbits << 16);
-        if (fastq) {
-          float rs = rcp_rn(su);
-          if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
-          const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
-          float qv[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[t], rs, v[t] * rl);
-          codes_fp8(qv, cw);
-        } else {
-          uint32_t q[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) q[t] = su > 0.0f ? enc_e4m3_sw(v[t] / su) : 0u;
-          cw[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-          cw[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-        }
-      }
+      codes_e8m0_fp8(v, E, cw);
       o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
-      o.sb[j] = sbits;
+      o.sb[j] = (uint32_t)(E + 127);
+    }
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
+  } else {  // M_FP8_BF16
+    // After an RMSNorm the chunks go in pairs: the two group maxima reduce
+    // together and the fast-path choice is made once for the wave, so the
+    // common case runs as one straight block (measured faster; without
+    // RMSNorm the same form costs registers, and each lane chooses alone).
+    constexpr int NB = (NORM && C >= 2) ? 2 : 1;
+#pragma unroll
+    for (int j0 = 0; j0 < C; j0 += NB) {
+      float vv[NB][8], mm[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        unpack8(yw[j0 + i], vv[i]);
+        mm[i] = amax8(vv[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) mm[i] = grp_max<8>(mm[i]);  // 64 values = 8 lanes
+      bool inr[NB], all = true;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        inr[i] = mm[i] >= 0x1p-71f && mm[i] <= 0x1p+100f;
+        all = all && inr[i];
+      }
+      uint32_t cw[NB][2];
+      if (NORM && __builtin_amdgcn_ballot_w64(!all) == 0) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], true, cw[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], inr[i], cw[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) o.w[j0 + i] = make_uint4(cw[i][0], cw[i][1], 0u, 0u);
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
