@@ -144,6 +144,33 @@ def copy_probe(mib: int, steps: int):
     print(json.dumps({"copy_bytes": n, "launches": steps}), flush=True)
 
 
+def cold_launches(step, dev, stream, launches: int = 20, scrub_mib: int = 512,
+                  scrub: bool = True):
+    """Mean kernel time with the device caches cold: before each launch a
+    read-only reduction over scrub_mib MiB (twice the 256 MB Infinity Cache
+    and far beyond L2) evicts the inputs and leaves clean lines, so no
+    write-back of the scrub lands inside the timed launch; HIP events on the
+    launch stream time each launch alone (its dispatch included)."""
+    import torch
+    n = scrub_mib << 20
+    a = torch.zeros(n // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    evs = []
+    with torch.cuda.stream(stream):
+        for _ in range(launches):
+            if scrub:
+                torch.amax(a, out=sink)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del a, sink
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / launches
+
+
 def copy_ceiling(dev, stream, mib: int = 512, warmup: int = 20, steps: int = 50):
     """Achieved bandwidth of a plain device-to-device copy (torch's copy_,
     the runtime's copy kernel) of mib MiB, timed in the same run with HIP
@@ -194,9 +221,43 @@ def upload(w: kvgen.Workload, dev):
     return t
 
 
+def host_info():
+    """Host core count and CPU model (for the CPU baseline's record)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+class _pinned:
+    """Runs the enclosed block on one host core (restores the mask after)."""
+
+    def __enter__(self):
+        self.prev = os.sched_getaffinity(0)
+        self.core = min(self.prev)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.prev)
+        return False
+
+
 def cpu_baseline(w: kvgen.Workload, max_seconds: float):
     """The oracle as it stands (single-threaded C) on the same workload, on
-    leading tokens until about max_seconds of CPU time."""
+    leading tokens until about max_seconds of CPU time, pinned to one host
+    core."""
+    with _pinned():
+        return _cpu_baseline(w, max_seconds)
+
+
+def _cpu_baseline(w: kvgen.Workload, max_seconds: float):
     import oracle
     cache = w.cache_init.copy()
     aux = None if w.aux_init is None else w.aux_init.copy()
@@ -321,12 +382,20 @@ def main():
     cc = copy_ceiling(dev, stream)
     result["copy_ceiling"] = {"achieved": cc, "unit": "GB/s", "kernel": "device copy, 512 MiB",
                               "frac": achieved / cc}
+    ms_cold = cold_launches(step, dev, stream)
+    ms_single = cold_launches(step, dev, stream, scrub=False)
+    result["cold"] = {"ms_per_launch": ms_cold, "tokens_per_s": w.T / (ms_cold * 1e-3),
+                      "achieved": abytes / (ms_cold * 1e-3) / 1e9, "unit": "GB/s",
+                      "frac": abytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      "launches": 20, "scrub": "512 MiB read-only reduction before each launch",
+                      "ms_per_launch_unscrubbed": ms_single}
     if not args.no_cpu:
         n, dt, ocache, oaux = cpu_baseline(w, args.cpu_seconds)
+        ncpu, model = host_info()
         result["cpu_baseline"] = {
             "value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {w.T} tokens of {w.name}, single-threaded C oracle, "
-                      f"{dt:.1f} s"}
+            "sample": f"first {n} of {w.T} tokens of {w.name}, single-threaded C oracle "
+                      f"pinned to one of {ncpu} host cores ({model}), {dt:.1f} s"}
         # the timed GPU path wrote the same rows: compare the tokens the
         # oracle covered
         got = t["cache_flat"].view(torch.uint8).cpu().numpy()
@@ -423,6 +492,14 @@ def main_drq(args):
     cc = copy_ceiling(dev, stream)
     result["copy_ceiling"] = {"achieved": cc, "unit": "GB/s", "kernel": "device copy, 512 MiB",
                               "frac": achieved / cc}
+    ms_cold = cold_launches(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream)
+    ms_single = cold_launches(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream,
+                              scrub=False)
+    result["cold"] = {"ms_per_launch": ms_cold, "tokens_per_s": w.T / (ms_cold * 1e-3),
+                      "achieved": abytes / (ms_cold * 1e-3) / 1e9, "unit": "GB/s",
+                      "frac": abytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      "launches": 20, "scrub": "512 MiB read-only reduction before each launch",
+                      "ms_per_launch_unscrubbed": ms_single}
     if not args.no_cpu:
         import oracle
         kc = np.full(bn * stride, 0xAB, np.uint8)
@@ -440,14 +517,17 @@ def main_drq(args):
             return time.perf_counter() - t0
 
         # calibrate on a small prefix, then time about cpu_seconds of tokens
-        probe = min(w.T, 1024)
-        dt = run_prefix(probe)
-        n = int(min(w.T, max(probe, probe * args.cpu_seconds / max(dt, 1e-6))))
-        dt = run_prefix(n)
+        with _pinned():
+            probe = min(w.T, 1024)
+            dt = run_prefix(probe)
+            n = int(min(w.T, max(probe, probe * args.cpu_seconds / max(dt, 1e-6))))
+            dt = run_prefix(n)
+        ncpu, model = host_info()
         result["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1,
                                   "kind": "oracle",
                                   "sample": f"first {n} of {w.T} tokens, single-threaded C "
-                                            f"oracle, {dt:.1f} s"}
+                                            f"oracle pinned to one of {ncpu} host cores "
+                                            f"({model}), {dt:.1f} s"}
     print(json.dumps(result), flush=True)
 
 

@@ -8,6 +8,7 @@ hit row the x row (and cos / sin rows when RoPE is on) is read and the
 cache row written; every token reads its 4-byte slot; gamma is read once.
 The expected totals below are that sum written out by hand for each
 workload, not a call of the function under test."""
+import os
 import subprocess
 import sys
 from pathlib import Path
@@ -62,3 +63,15 @@ def test_dense_count_adds_skipped_rows():
     w = kvgen.config(3)
     skipped = w.T - w.hits
     assert bench.algorithmic_bytes(w, dense=True) - bench.algorithmic_bytes(w) == skipped * 256
+
+
+def test_pinned_restores_affinity():
+    before = os.sched_getaffinity(0)
+    with bench._pinned() as p:
+        assert os.sched_getaffinity(0) == {p.core}
+    assert os.sched_getaffinity(0) == before
+
+
+def test_host_info():
+    n, model = bench.host_info()
+    assert n >= 1 and isinstance(model, str) and model
