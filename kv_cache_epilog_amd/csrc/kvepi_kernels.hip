@@ -488,8 +488,8 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int j = 0; j < C; ++j) {
       float v[8];
       unpack8(b.xw[j], v);
-      // squares of bf16 values are exact, so fma(b, b, a*a) is the
-      // rounded sum of the two squares
+      // the square of a bf16 value with |v| >= 2^-67 is exact, so then
+      // fma(b, b, a*a) is the rounded sum of the two rounded squares
       const float s01 = __builtin_fmaf(v[1], v[1], v[0] * v[0]);
       const float s23 = __builtin_fmaf(v[3], v[3], v[2] * v[2]);
       const float s45 = __builtin_fmaf(v[5], v[5], v[4] * v[4]);
@@ -510,7 +510,28 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     for (int w = 1; w < C; w *= 2)
 #pragma unroll
       for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
-    const float ss = part[0];
+    float ss = part[0];
+    // A smaller magnitude (zeros included, which costs nothing) can have a
+    // square that underflows and rounds, and the fused sum above would then
+    // round once where the definition rounds the square first: such waves,
+    // rare, sum the separately rounded squares.
+    if (__builtin_amdgcn_ballot_w64(mn < 0x1p-67f) != 0) {
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        float v[8], q[8];
+        unpack8(b.xw[j], v);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) q[t] = v[t] * v[t];
+        s8[j] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+      }
+#pragma unroll
+      for (int j = 0; j < C; ++j) part[j] = grp_sum<L>(s8[j]);
+#pragma unroll
+      for (int w = 1; w < C; w *= 2)
+#pragma unroll
+        for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
+      ss = part[0];
+    }
     const float mean = a.inv_nseg != 0.0f ? ss * a.inv_nseg : ss / a.nseg_f;
     const float xs = mean + a.eps;
     // (a wave-uniform choice, so only one of the two square roots runs)

@@ -298,3 +298,60 @@ def test_many_iterations_per_wave(case, waves, monkeypatch):
     else:
         w = _small(0, T, 256, seed=36, bs=16)
     check(w)
+
+
+def _tree_f32(a):
+    s = np.asarray(a, np.float32)
+    while s.size > 1:
+        s = (s[0::2] + s[1::2]).astype(np.float32)
+    return s[0]
+
+
+def _rmsnorm_out(v, g, fused_pairs):
+    """bf16 RMSNorm outputs of one row with eps = 0 (numpy fp32): the squares
+    rounded one by one, or (fused_pairs) each pair summed with one rounding
+    as an fma of the second square onto the first rounded square would."""
+    if fused_pairs:
+        p = (v[0::2] * v[0::2]).astype(np.float32)
+        pairs = (v[1::2].astype(np.float64) ** 2 + p.astype(np.float64)).astype(np.float32)
+        ss = _tree_f32(pairs)
+    else:
+        ss = _tree_f32((v * v).astype(np.float32))
+    rms = np.sqrt(np.float32(ss / np.float32(v.size)))
+    return kvgen.to_bf16(((v / rms).astype(np.float32) * g).astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", [4, 0])
+def test_underflowing_squares(mode):
+    # Rows of pairs (a, b) with a = M0 2^-70 (a^2 exact, in [2^-125, 2^-124))
+    # and b = M1 2^-82 (b^2 between 0.5 and 0.75 of that binade's last
+    # place, below the normal range): the definition rounds b^2 first (to a
+    # half place, a tie when added to a^2), a fused pair sum rounds once, and
+    # with eps = 0 the last place of the sum can reach rms.  Rows are kept
+    # only where the two readings give different bf16 outputs with this
+    # workload's gamma, so the comparison with the oracle exercises the case.
+    rng = np.random.default_rng(23)
+    T, d = 32, 576
+    x = kvgen.to_bf16(rng.standard_normal((T, d)))
+    # (the bf16 split writes the RoPE output to its second cache, so it
+    # takes cos and sin; the rope columns do not enter the RMSNorm)
+    w = _small(mode, T, d, seed=29, skip=0.0, norm=True, rope=mode == 4, x=x, eps=0.0)
+    g = kvgen.bf16_to_f32(w.gamma).astype(np.float32)
+    # (a one-place change of rms reaches a bf16 output only when an output
+    # lies that close to a bf16 rounding boundary: about 1 row in 260 here)
+    rows = []
+    for _ in range(20000):
+        sgn = np.where(rng.random(512) < 0.5, -1.0, 1.0)
+        row = np.empty(512)
+        row[0::2] = sgn[0::2] * rng.integers(182, 256, 256) * 2.0 ** -70
+        row[1::2] = sgn[1::2] * rng.integers(182, 222, 256) * 2.0 ** -82
+        bits = kvgen.to_bf16(row)
+        v = kvgen.bf16_to_f32(bits).astype(np.float32)
+        if not np.array_equal(_rmsnorm_out(v, g, True), _rmsnorm_out(v, g, False)):
+            rows.append(bits)
+            if len(rows) == T // 2:
+                break
+    assert len(rows) == T // 2
+    for r, bits in enumerate(rows):
+        w.x[r, :512] = bits
+    check(w)
