@@ -241,7 +241,7 @@ float kvo_sumsq_tree(const uint16_t *x, int64_t n) {
   float *sq = (float *)calloc((size_t)p, sizeof(float));
   for (int64_t i = 0; i < n; ++i) {
     float xi = kvo_bf16_to_f32(x[i]);
-    sq[i] = xi * xi; /* square_x = x * x (exact for a bf16 x) */
+    sq[i] = xi * xi; /* square_x = x * x, one fp32 rounding (exact when |x| >= 2^-67) */
   }
   float ss = tree_sum(sq, p);
   free(sq);
