@@ -595,10 +595,13 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         const float a1 = lo_f(b.rx[k].y), b1 = hi_f(b.rx[k].y);
         const float c0 = lo_f(b.rc[k]), c1 = hi_f(b.rc[k]);
         const float s0 = lo_f(b.rs[k]), s1 = hi_f(b.rs[k]);
-        // first half: a*c - b*s; second half: b*c + a*s (both products exact)
+        // first half: a*c - b*s; second half: b*c + a*s.  Each product is
+        // rounded on its own, as the definition has it: a product of two
+        // bf16 values is exact unless it underflows, and there a fused
+        // multiply-add would round once where the definition rounds twice.
         const float p0 = hi ? b0 : a0, q0 = hi ? a0 : -b0;
         const float p1 = hi ? b1 : a1, q1 = hi ? a1 : -b1;
-        ry[k] = pack_bf16(__builtin_fmaf(p0, c0, q0 * s0), __builtin_fmaf(p1, c1, q1 * s1));
+        ry[k] = pack_bf16(p0 * c0 + q0 * s0, p1 * c1 + q1 * s1);
       } else {
         ry[k] = b.rx[k].x;
       }
@@ -614,14 +617,14 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
   } else if constexpr (MODE == M_SPLIT_G) {
 #pragma unroll
     for (int j = 0; j < C; ++j) o.w[j] = yw[j];
-    // y[p] = a c[p] - b s[p], y[p + Dk/2] = b c[p + Dk/2] + a s[p + Dk/2]
-    // (both products exact)
+    // y[p] = a c[p] - b s[p], y[p + Dk/2] = b c[p + Dk/2] + a s[p + Dk/2],
+    // each product rounded on its own (as above)
 #pragma unroll
     for (int k = 0; k < RowBuf<MODE, ROPE, L, C>::TPG; ++k) {
       const float xa = lo_f(b.gx[k]), xb = hi_f(b.gx[k]);
       const float c0 = lo_f(b.gc[k]), c1 = hi_f(b.gc[k]);
       const float s0 = lo_f(b.gs[k]), s1 = hi_f(b.gs[k]);
-      o.ry[k] = pack_bf16(__builtin_fmaf(xa, c0, -xb * s0), __builtin_fmaf(xb, c1, xa * s1));
+      o.ry[k] = pack_bf16(xa * c0 + -xb * s0, xb * c1 + xa * s1);
     }
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll

@@ -164,3 +164,51 @@ def check(w: kvgen.Workload, label="", **kw):
     got, agot = run_gpu(w, **kw)
     want, awant = run_oracle(w)
     return compare(w, got, want, agot, awant, label or w.name)
+
+
+def _bf16_values(rng, n, emin, emax):
+    e = rng.integers(emin, emax + 1, n).astype(np.float64)
+    m = rng.integers(128, 256, n) / 128.0
+    sg = np.where(rng.random(n) < 0.5, -1.0, 1.0)
+    return kvgen.to_bf16(sg * m * 2.0 ** e)
+
+
+def rope_product_cases(rng, n):
+    """n quadruples (p, q, c, s) of bf16 bit patterns for which p*c + q*s
+    rounded to bf16 differs between rounding each product on its own (the
+    definition) and rounding p*c + RN(q*s) once (a fused multiply-add):
+    tiny p, q and small c, s, so that the products underflow and round."""
+    out = []
+    while sum(len(o[0]) for o in out) < n:
+        N = 1 << 20
+        p, q = _bf16_values(rng, N, -126, -112), _bf16_values(rng, N, -126, -112)
+        c, s = _bf16_values(rng, N, -30, -8), _bf16_values(rng, N, -30, -8)
+        pf, qf, cf, sf = (kvgen.bf16_to_f32(v).astype(np.float32) for v in (p, q, c, s))
+        sep = kvgen.to_bf16((pf * cf).astype(np.float32) + (qf * sf).astype(np.float32))
+        qs = (qf * sf).astype(np.float32).astype(np.float64)
+        fused = kvgen.to_bf16((pf.astype(np.float64) * cf.astype(np.float64) + qs)
+                              .astype(np.float32))
+        k = np.nonzero(sep != fused)[0]
+        out.append((p[k], q[k], c[k], s[k]))
+    return tuple(np.concatenate([o[i] for o in out])[:n] for i in range(4))
+
+
+def plant_rope_cases(w, rng, dk):
+    """Fills every rope pair of w with such cases: even tokens exercise the
+    first half (y[j] = a c[j] - b s[j]), odd tokens the second half
+    (y[j + dk/2] = b c[j + dk/2] + a s[j + dk/2])."""
+    h = dk // 2
+    p, q, c, s = rope_product_cases(rng, w.T * h)
+    neg = lambda v: v ^ np.uint16(0x8000)  # noqa: E731  (bf16 negation)
+    base = w.d - dk
+    i = 0
+    for t in range(w.T):
+        for j in range(h):
+            if t % 2 == 0:   # a = p, -b = q, c[j], s[j]
+                w.x[t, base + 2 * j], w.x[t, base + 2 * j + 1] = p[i], neg(q[i])
+                w.cos[t, j], w.sin[t, j] = c[i], s[i]
+            else:            # b = p, a = q, c[j + h], s[j + h]
+                w.x[t, base + 2 * j + 1], w.x[t, base + 2 * j] = p[i], q[i]
+                w.cos[t, j + h], w.sin[t, j + h] = c[i], s[i]
+            i += 1
+    return i

@@ -188,3 +188,19 @@ def test_split_rope_length_with_block_index():
     w.index_mode = 2
     w.seq_len = S
     check(w)
+
+
+@pytest.mark.parametrize("dk", [32, 10])
+def test_split_rope_length_underflowing_products(dk):
+    # the general rope length with every pair a case where rounding each
+    # product on its own (the definition) and a fused multiply-add give
+    # different bf16 outputs (tiny values times small cos / sin)
+    from parity import plant_rope_cases
+    dv, T, bs = 512, 32, 8
+    d = dv + dk
+    nblk = (T + bs - 1) // bs + 2
+    w = kvgen.make(f"split_dk{dk}_uf", 4, T, d, seed=91 + dk,
+                   cache=CacheSpec(nblk, bs, dv, bs * dv, 2),
+                   aux=CacheSpec(nblk, bs, dk, bs * dk, 2), norm=True, rope=True, rope_dim=dk)
+    assert plant_rope_cases(w, np.random.default_rng(dk), dk) == T * dk // 2
+    check(w, x_pad=(-d) % 8)

@@ -355,3 +355,16 @@ def test_underflowing_squares(mode):
     for r, bits in enumerate(rows):
         w.x[r, :512] = bits
     check(w)
+
+
+@pytest.mark.parametrize("mode", [0, 4])
+def test_rope_underflowing_products(mode):
+    # tiny rope values times small cos / sin: a product of two bf16 values
+    # that underflows rounds, and a fused multiply-add would round the pair
+    # once; every rope pair here is a case where that changes the bf16
+    # output (found and checked on the CPU by plant_rope_cases)
+    from parity import plant_rope_cases
+    rng = np.random.default_rng(31)
+    w = _small(mode, 32, 576, seed=37, skip=0.0, norm=True, rope=True)
+    assert plant_rope_cases(w, rng, 64) == 32 * 32
+    check(w)
