@@ -368,3 +368,48 @@ def test_rope_underflowing_products(mode):
     w = _small(mode, 32, 576, seed=37, skip=0.0, norm=True, rope=True)
     assert plant_rope_cases(w, rng, 64) == 32 * 32
     check(w)
+
+
+def test_offsets_beyond_4gib():
+    # A cache of about 4.7 GB written at slots whose byte offsets all lie
+    # past 2^32, and x rows 128 MB apart (an 8 GB row stride span), so that
+    # both the row addresses and the x addresses need 64-bit arithmetic.
+    # The expected rows come from the oracle on a small cache of the same
+    # row layout; only the touched rows and their neighbours are read back.
+    import torch
+    from kv_cache_epilog_amd import kvepi_run
+    from parity import to_dev_bf16
+    T, d, bs, kc = 64, 576, 128, 672
+    small = _small(0, T, d, seed=41, skip=0.1, norm=True, rope=True)
+    ocache, _ = run_oracle(small)
+    dev = torch.device("cuda:0")
+    bn, stride = 54000, bs * kc + 256          # a gap after every block
+    flat = torch.full((bn * stride,), kvgen.PREFILL, dtype=torch.uint8, device=dev)
+    view = flat.as_strided((bn, bs, 1, kc), (stride, kc, kc, 1))
+    first = (2 ** 32 // stride + 1) * bs      # first slot of a block past 2^32
+    rng = np.random.default_rng(41)
+    big = rng.choice(np.arange(first, bn * bs - 1, 2), T, replace=False).astype(np.int32)
+    big[small.slots < 0] = -1
+    xs = 1 << 26                               # elements between rows of x
+    xbuf = torch.empty((T, xs), dtype=torch.bfloat16, device=dev)
+    x = xbuf[:, :d]
+    x.copy_(to_dev_bf16(small.x, dev))
+    kvepi_run(x, torch.from_numpy(big).to(dev), view, 0, 64,
+              gamma=to_dev_bf16(small.gamma, dev), cos=to_dev_bf16(small.cos, dev),
+              sin=to_dev_bf16(small.sin, dev), eps=small.eps)
+    torch.cuda.synchronize()
+    hit = np.nonzero(big >= 0)[0]
+    off = np.array([(int(s) // bs) * stride + (int(s) % bs) * kc for s in big[hit]], np.int64)
+    assert off.min() >= 2 ** 32
+    idx = torch.from_numpy(off[:, None] + np.arange(kc)[None, :]).to(dev)
+    got = flat[idx].cpu().numpy()
+    want = np.stack([ocache[small.cache.row_offset(int(s)):][:kc] for s in small.slots[hit]])
+    assert np.array_equal(got, want)
+    # the next row (the slots are even, so never written) and the block gaps
+    nxt = flat[idx + kc].cpu().numpy()
+    assert np.all(nxt == kvgen.PREFILL)
+    gaps = torch.from_numpy(((big[hit] // bs) * stride + bs * kc).astype(np.int64)[:, None]
+                            + np.arange(256)[None, :]).to(dev)
+    assert np.all(flat[gaps].cpu().numpy() == kvgen.PREFILL)
+    del flat, view, xbuf
+    torch.cuda.empty_cache()
