@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,9 +57,21 @@ def algorithmic_bytes(w: kvgen.Workload, dense: bool = False) -> int:
     return 4 * w.T + read_rows * (x_row + rope) + hits * written + gamma
 
 
+def code_text(text: str) -> str:
+    """C++ source with its comments removed and every run of blank space
+    made one space: what the compiler sees of it (no string literal of the
+    kernel sources holds a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash(src: str = KERNEL_SRC) -> str:
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of a kernel source's code: measured traffic belongs to
+    the code, so a change to it invalidates the figure and an edit of a
+    comment does not."""
+    with open(src, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload: str, src: str = KERNEL_SRC):

@@ -988,7 +988,7 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
     t.g = (uint32_t)wave + (uint32_t)j * (uint32_t)a.nwaves;
     const bool in = j < n_it;
     if constexpr (R > 2) {
-      // many rows per wave: each lane judges its own row (live holds only
+      // many rows per wave: each lane decides for its own row (live holds only
       // the lane's own bit), and the first live row comes from a ballot
       const uint32_t row = t.g * R + (uint32_t)sub;
       const bool lv = in && row < (uint32_t)a.T && t.own < ns;

@@ -75,3 +75,11 @@ def test_pinned_restores_affinity():
 def test_host_info():
     n, model = bench.host_info()
     assert n >= 1 and isinstance(model, str) and model
+
+
+def test_code_hash_ignores_comments_only():
+    a = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    b = "/* a function */\nint f(int x) {\n  // the next value\n  return x   +   1;\n}\n"
+    c = "int f(int x) {\n  return x + 2;  // one more\n}\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
