@@ -88,7 +88,7 @@ kvepi_status kvepi_drq_validate(const kvepi_drq_params *pp, kvepi_drq_plan *plan
   if (plan) {
     plan->p = p;
     plan->H = H;
-    plan->units = p.num_tokens * (H / (dequant ? 8 : 16));
+    plan->units = p.num_tokens * (H / 16);
     plan->k_pitch = p.k_cache.head_dim;
     plan->k_bstride = p.k_cache.block_stride;
     plan->v_pitch = p.v_cache.head_dim;

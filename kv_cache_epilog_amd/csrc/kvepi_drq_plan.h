@@ -10,7 +10,7 @@
 struct kvepi_drq_plan {
   kvepi_drq_params p;       // the caller's parameters (validated)
   int64_t H;                // (nq + 2 nkv) * head_dim
-  int64_t units;            // threads: T * H / 16 (int32 x: T * H / 8)
+  int64_t units;            // threads: T * H / 16
   int64_t k_pitch, k_bstride, v_pitch, v_bstride;  // bytes
 };
 
