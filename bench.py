@@ -407,6 +407,8 @@ def main():
         ncpu, model = host_info()
         result["cpu_baseline"] = {
             "value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            # the same algorithmic bytes, prorated to the tokens of the sample
+            "gbps": abytes * n / w.T / dt / 1e9,
             "sample": f"first {n} of {w.T} tokens of {w.name}, single-threaded C oracle "
                       f"pinned to one of {ncpu} host cores ({model}), {dt:.1f} s"}
         # the timed GPU path wrote the same rows: compare the tokens the
@@ -538,6 +540,7 @@ def main_drq(args):
         ncpu, model = host_info()
         result["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1,
                                   "kind": "oracle",
+                                  "gbps": abytes * n / w.T / dt / 1e9,
                                   "sample": f"first {n} of {w.T} tokens, single-threaded C "
                                             f"oracle pinned to one of {ncpu} host cores "
                                             f"({model}), {dt:.1f} s"}
