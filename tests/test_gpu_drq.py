@@ -29,6 +29,17 @@ def test_int32_options(out, act, offsets, kv_output):
     compare(c, "int32 options")
 
 
+@pytest.mark.parametrize("out", [BF, FP])
+@pytest.mark.parametrize("nq,nkv,D", [(8, 8, 16), (2, 1, 32), (30, 1, 128), (2, 1, 16)])
+def test_int32_head_shapes(out, nq, nkv, D):
+    # int32 rows at the smallest head (D = 16: a unit is the whole head, and
+    # heads of 16 make H = 64 with three or 24 heads), a small one, and the
+    # largest row (H = 4096)
+    c = make_case(250 + D + nq, T=150, nq=nq, nkv=nkv, D=D, x_dtype=I32, out_dtype=out,
+                  bias_dtype=BF, act=True, offsets=True)
+    compare(c, "int32 head shapes")
+
+
 @pytest.mark.parametrize("dt", [BF, FP])
 @pytest.mark.parametrize("nq,nkv,D", [(12, 3, 128), (2, 1, 32), (1, 1, 64), (8, 8, 16),
                                       (30, 1, 128)])
