@@ -7,9 +7,13 @@ into a paged cache [2048, 128, 1, 672] whose block stride is 1.25x the dense
 one, 3% of the tokens skipped.  Inputs are seeded synthetic data resident in
 HBM before timing starts.
 
-Prints one JSON line: tokens/s (T / kernel time), plus the roofline of the
+Prints one JSON line: tokens/s (T / kernel time); the roofline of the
 epilog kernel (algorithmic bytes per launch / mean launch time, against the
-8 TB/s HBM peak) and the CPU oracle timed on the host as a reported baseline.
+8 TB/s HBM peak, with the measured HBM bytes when they were taken on the
+current kernel code); a plain device copy timed in the same run; single
+launches after a cache scrub ("cold"); and the CPU oracle timed on one host
+core as a reported baseline.  --config N selects the other epilog workloads
+and --drq NAME the dequant -> RoPE -> int8 operator's.
 """
 from __future__ import annotations
 
