@@ -33,7 +33,8 @@
  *    allocates nothing and keeps no pointer after a call returns.
  *  - kvepi_run is asynchronous: buffers must stay alive and unmodified until
  *    the stream has passed the launched kernel.  The library never
- *    synchronises the stream.
+ *    synchronises the stream (except under the KVEPI_CHECK_SLOTS debug check
+ *    described at kvepi_run).
  *  - Every check runs before any launch, so a call that returns an error
  *    writes nothing.
  *  - Results are deterministic: the same inputs give the same bytes
@@ -190,7 +191,13 @@ KVEPI_API kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, in
  * The launch uses one persistent workgroup per resident slot of the device.
  * The environment variable KVEPI_MAX_WAVES (a multiple of 4, read at every
  * call) caps the number of wavefronts; it exists for tests of the kernel's
- * multi-iteration paths and never changes the result. */
+ * multi-iteration paths and never changes the result.
+ * Debug aid: with the environment variable KVEPI_CHECK_SLOTS set (to anything
+ * but "0"; read at every call), kvepi_run and kvepi_run_ex copy slot_mapping
+ * to the host, synchronously on `stream`, and return KVEPI_ERR_PARAM before
+ * any launch if two tokens name the same row (index mode KVEPI_INDEX_SLOT
+ * only; a failed copy returns KVEPI_ERR_RUNTIME).  Repeated slots are
+ * otherwise not detected: their rows are unspecified. */
 KVEPI_API kvepi_status kvepi_run(const void *x, int64_t num_tokens, int64_t d,
                        int64_t x_row_stride, const void *gamma,
                        const void *cos, const void *sin,

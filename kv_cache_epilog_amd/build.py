@@ -10,7 +10,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkvepi.so")
 SOURCES = [os.path.join(CSRC, n) for n in ("kvepi_kernels.hip", "kvepi_host.cpp",
-                                           "kvepi_drq.hip", "kvepi_drq_host.cpp")]
+                                           "kvepi_debug.cpp", "kvepi_drq.hip",
+                                           "kvepi_drq_host.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

@@ -1,6 +1,8 @@
 // kvepi_host.cpp -- argument validation, row geometry and the two-stage C ABI
 // of the fused KV-cache write epilog.  Pure host code: no call in this file
-// touches the GPU, so every check can run (and be tested) without one.
+// touches the GPU, so every check can run (and be tested) without one (the
+// optional duplicate-slot check that kvepi_run calls lives in
+// kvepi_debug.cpp).
 #include <math.h>
 #include <stdint.h>
 
@@ -259,6 +261,8 @@ kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d,
                      eps, options, &plan);
   if (st != KVEPI_OK) return st;
   if (plan.T == 0) return KVEPI_OK;
+  st = kvepi_debug_check_slots(plan, slot_mapping, stream);
+  if (st != KVEPI_OK) return st;
   return kvepi_launch(plan, stream);
 }
 

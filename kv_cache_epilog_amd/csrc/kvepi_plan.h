@@ -43,3 +43,7 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
 
 // Enqueue the kernel for a validated plan (T > 0).
 kvepi_status kvepi_launch(const kvepi_plan &plan, void *stream);
+// The optional duplicate-slot check (KVEPI_CHECK_SLOTS; kvepi_debug.cpp):
+// KVEPI_OK unless it is enabled and two tokens name the same row.
+kvepi_status kvepi_debug_check_slots(const kvepi_plan &plan, const int32_t *slot_mapping,
+                                     void *stream);

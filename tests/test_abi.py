@@ -290,3 +290,13 @@ def test_valid_run_without_a_device_reports_runtime_error():
         pytest.skip("a GPU is present")
     assert call(2) == (7, None)
     assert call_ex(2, O(index_mode=2, seq_len=8)) == (7, None)
+
+
+def test_slot_check_without_a_device_reports_runtime_error(monkeypatch):
+    # the debug check copies the slots to the host before the launch: on a
+    # host without a GPU that copy fails, KVEPI_ERR_RUNTIME, not a crash
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    monkeypatch.setenv("KVEPI_CHECK_SLOTS", "1")
+    assert call(2) == (7, None)

@@ -413,3 +413,28 @@ def test_offsets_beyond_4gib():
     assert np.all(flat[gaps].cpu().numpy() == kvgen.PREFILL)
     del flat, view, xbuf
     torch.cuda.empty_cache()
+
+
+def test_duplicate_slot_check(monkeypatch):
+    # KVEPI_CHECK_SLOTS: two tokens naming one row are rejected with
+    # KVEPI_ERR_PARAM before any launch (the cache keeps every byte); distinct
+    # slots pass the check and give the oracle's bytes
+    import torch
+    from kv_cache_epilog_amd import kvepi_run
+    from kv_cache_epilog_amd.binding import KvepiError
+    from parity import cache_tensor, to_dev_bf16
+    monkeypatch.setenv("KVEPI_CHECK_SLOTS", "1")
+    w = _small(0, 64, 576, seed=43, skip=0.1, norm=True, rope=True)
+    check(w)
+    dev = torch.device("cuda:0")
+    slots = w.slots.copy()
+    hit = np.nonzero(slots >= 0)[0]
+    slots[hit[-1]] = slots[hit[0]]
+    cache, flat = cache_tensor(w.cache, w.cache_init, dev)
+    with pytest.raises(KvepiError) as e:
+        kvepi_run(to_dev_bf16(w.x, dev), torch.from_numpy(slots).to(dev), cache, 0, 64,
+                  gamma=to_dev_bf16(w.gamma, dev), cos=to_dev_bf16(w.cos, dev),
+                  sin=to_dev_bf16(w.sin, dev), eps=w.eps)
+    assert e.value.status == 4  # KVEPI_ERR_PARAM
+    torch.cuda.synchronize()
+    assert np.all(flat.cpu().numpy() == kvgen.PREFILL)
