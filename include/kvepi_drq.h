@@ -83,6 +83,12 @@ typedef struct kvepi_drq_params {
  * blocks, or seq_len above the block size); LAYOUT for alignment. */
 KVEPI_API kvepi_status kvepi_drq_get_workspace(const kvepi_drq_params *params,
                                                uint64_t *workspace_bytes);
+/* Debug aid: with the environment variable KVEPI_CHECK_SLOTS set (to
+ * anything but "0"; read at every call), kvepi_drq_run in page mode copies
+ * indices to the host, synchronously on `stream`, and returns
+ * KVEPI_ERR_PARAM before any launch if two tokens name the same row (a
+ * failed copy returns KVEPI_ERR_RUNTIME); otherwise repeated slots are not
+ * detected and their rows are unspecified. */
 KVEPI_API kvepi_status kvepi_drq_run(const kvepi_drq_params *params, void *workspace,
                                      uint64_t workspace_bytes, void *stream);
 

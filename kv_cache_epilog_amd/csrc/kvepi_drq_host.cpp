@@ -115,6 +115,8 @@ kvepi_status kvepi_drq_run(const kvepi_drq_params *params, void *workspace,
   const kvepi_status st = kvepi_drq_validate(params, &plan);
   if (st != KVEPI_OK) return st;
   if (plan.units == 0) return KVEPI_OK;
+  const kvepi_status cs = kvepi_drq_debug_check_slots(plan, stream);
+  if (cs != KVEPI_OK) return cs;
   return kvepi_drq_launch(plan, stream);
 }
 

@@ -16,3 +16,7 @@ struct kvepi_drq_plan {
 
 kvepi_status kvepi_drq_validate(const kvepi_drq_params *p, kvepi_drq_plan *plan);
 kvepi_status kvepi_drq_launch(const kvepi_drq_plan &plan, void *stream);
+// The optional duplicate-slot check of page mode (KVEPI_CHECK_SLOTS;
+// kvepi_debug.cpp): KVEPI_OK unless it is enabled and two tokens name the
+// same row.
+kvepi_status kvepi_drq_debug_check_slots(const kvepi_drq_plan &plan, void *stream);

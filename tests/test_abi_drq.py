@@ -99,3 +99,11 @@ def test_valid_run_without_a_device_reports_runtime_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call(2, params()) == (7, None)
+
+
+def test_slot_check_without_a_device_reports_runtime_error(monkeypatch):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    monkeypatch.setenv("KVEPI_CHECK_SLOTS", "1")
+    assert call(2, params()) == (7, None)

@@ -121,3 +121,18 @@ def test_division_paths(case):
         c.scale_v[::2] = 5e30
     c.x = x
     compare(c, case)
+
+
+def test_duplicate_slot_check(monkeypatch):
+    # KVEPI_CHECK_SLOTS in page mode: distinct slots pass the check and match
+    # the oracle; a repeated slot is rejected with KVEPI_ERR_PARAM
+    from kv_cache_epilog_amd.binding import KvepiError
+    from drq_case import run_gpu
+    monkeypatch.setenv("KVEPI_CHECK_SLOTS", "1")
+    c = make_case(1000, T=64, nq=2, nkv=1, D=64, x_dtype=BF, out_dtype=BF, skip=0.1)
+    compare(c, "distinct slots under the check")
+    hit = np.nonzero(c.index >= 0)[0]
+    c.index[hit[-1]] = c.index[hit[0]]
+    with pytest.raises(KvepiError) as e:
+        run_gpu(c)
+    assert e.value.status == 4  # KVEPI_ERR_PARAM
