@@ -192,7 +192,10 @@ def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
     """Enqueue the epilog on `stream` (a torch.cuda.Stream; default: torch's
     current stream).  Updates cache / cache_aux in place, asynchronously.
     x may be bf16 or (indexer modes) fp16; index_mode and seq_len select how
-    slot_mapping places the tokens (see kvepi_options)."""
+    slot_mapping places the tokens (see kvepi_options).  Raises KvepiError
+    with the library's status on a rejected call (nothing is written then);
+    with KVEPI_CHECK_SLOTS=1 in the environment, repeated slots are such an
+    error (the check synchronises the stream)."""
     import torch
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
                         cache_aux, eps, index_mode)
@@ -280,7 +283,9 @@ def kvepi_drq_get_workspace(params: kvepi_drq_params) -> int:
 
 def kvepi_drq_run(params: kvepi_drq_params, *, stream=None, device=None) -> None:
     """Enqueue the dequant -> RoPE -> int8 KV cache operator on `stream`
-    (default: torch's current stream)."""
+    (default: torch's current stream).  Raises KvepiError on a rejected call
+    (nothing is written then); with KVEPI_CHECK_SLOTS=1 in the environment,
+    repeated page-mode slots are such an error."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream(device)
