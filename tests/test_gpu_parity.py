@@ -438,3 +438,48 @@ def test_duplicate_slot_check(monkeypatch):
     assert e.value.status == 4  # KVEPI_ERR_PARAM
     torch.cuda.synchronize()
     assert np.all(flat.cpu().numpy() == kvgen.PREFILL)
+
+
+def _fuzz_case(k):
+    """A seeded random workload: mode, row width, RMSNorm / RoPE, token
+    count, block size, head padding, block stride, skip density, row sigma,
+    fp16 rows (indexer modes), buffer offsets and padded x rows."""
+    rng = np.random.default_rng(7000 + k)
+    mode = int(rng.choice([0, 1, 3, 4, 5, 6]))
+    if mode in (0, 1, 4):
+        d = 64 * int(rng.integers(2, 129))          # 128 .. 8192
+    else:
+        d = 32 * int(rng.integers(1, 257))          # 32 .. 8192
+    norm = mode == 4 or (mode in (0, 1) and bool(rng.random() < 0.5))
+    rope = mode == 4 or (mode in (0, 1) and bool(rng.random() < 0.5))
+    T = int(rng.choice([1, 2, 63, 64, 65, 129, int(rng.integers(1, 1500))]))
+    if d >= 4096:
+        T = min(T, 300)
+    bs = int(rng.choice([1, 3, 16, 128, int(rng.integers(1, 200))]))
+    skip = float(rng.choice([0.0, 0.05, 0.3, 1.0]))
+    sigma = float(rng.choice([0.0, 1.0, 3.0]))
+    group = {3: 32, 5: 32, 6: 0}.get(mode, 64)
+    import oracle
+    kc = d - 64 if mode == 4 else oracle.row_bytes(mode, d, group)[1]
+    head = kc + int(rng.choice([0, 0, 1, 3, 16]))
+    stride_extra = int(rng.choice([0, 0, 5, 64]))
+    x = None
+    fp16 = mode in (3, 5, 6) and bool(rng.random() < 0.3)
+    if fp16:
+        x = kvgen.fp16_rows(rng, T, d, row_sigma=sigma)
+    w = _small(mode, T, d, seed=7000 + k, bs=bs, head=head, stride_extra=stride_extra,
+               norm=norm, rope=rope, skip=skip, row_sigma=sigma,
+               **({} if x is None else {"x": x}))
+    if fp16:
+        w.x_fp16 = True
+    kw = dict(offset=int(rng.choice([0, 0, 1, 7, 32])) * w.cache.elem_bytes,
+              x_pad=int(rng.choice([0, 0, 8, 24])))
+    if mode in (3, 5, 6):
+        kw["aux_offset"] = int(rng.choice([0, 4]))
+    return w, kw
+
+
+@pytest.mark.parametrize("k", range(160))
+def test_fuzz(k):
+    w, kw = _fuzz_case(k)
+    assert check(w, f"fuzz {k}: {w.name}", **kw) == 0
