@@ -136,3 +136,39 @@ def test_duplicate_slot_check(monkeypatch):
     with pytest.raises(KvepiError) as e:
         run_gpu(c)
     assert e.value.status == 4  # KVEPI_ERR_PARAM
+
+
+def _drq_fuzz_case(k):
+    """A seeded random case: x / output dtypes, head dim and head counts
+    (H <= 4096, H % 64 == 0), bias dtype, activation scales, offsets, k / v
+    outputs, page or contiguous mode, block size, head padding, block stride,
+    skipped tokens and padded x rows."""
+    rng = np.random.default_rng(9000 + k)
+    xt = int(rng.choice([I32, BF, FP]))
+    out = int(rng.choice([BF, FP])) if xt == I32 else xt
+    while True:
+        D = 16 * int(rng.integers(1, 17))
+        nkv, nq = int(rng.integers(1, 9)), int(rng.integers(1, 33))
+        H = (nq + 2 * nkv) * D
+        if H % 64 == 0 and H <= 4096:
+            break
+    kw = dict(kv_output=bool(rng.random() < 0.5), x_pad=int(rng.choice([0, 0, 8, 32])),
+              offsets=bool(rng.random() < 0.7), head=nkv * D + int(rng.choice([0, 0, 16, 32])),
+              stride_extra=int(rng.choice([0, 0, 8, 64])))
+    if xt == I32:
+        kw["bias_dtype"] = [None, F32, I32, BF, FP][int(rng.integers(0, 5))]
+        kw["act"] = bool(rng.random() < 0.7)
+    if rng.random() < 0.3:
+        S, B = int(rng.integers(1, 65)), int(rng.integers(1, 9))
+        kw.update(cache_mode=1, seq_len=S, bs=S + int(rng.integers(0, 20)))
+        T = B * S
+    else:
+        T = int(rng.choice([1, 2, 17, 64, int(rng.integers(1, 800))]))
+        kw.update(bs=int(rng.choice([1, 3, 16, 128, int(rng.integers(1, 100))])),
+                  skip=float(rng.choice([0.0, 0.05, 0.5])))
+    return make_case(9000 + k, T=T, nq=nq, nkv=nkv, D=D, x_dtype=xt, out_dtype=out, **kw)
+
+
+@pytest.mark.parametrize("k", range(80))
+def test_fuzz(k):
+    compare(_drq_fuzz_case(k), f"fuzz {k}")
