@@ -204,3 +204,31 @@ def test_split_rope_length_underflowing_products(dk):
                    aux=CacheSpec(nblk, bs, dk, bs * dk, 2), norm=True, rope=True, rope_dim=dk)
     assert plant_rope_cases(w, np.random.default_rng(dk), dk) == T * dk // 2
     check(w, x_pad=(-d) % 8)
+
+
+def _index_fuzz_case(k):
+    """A seeded random workload in one of the batch-major index modes: mode,
+    row width, RMSNorm / RoPE, index mode, batches, sequence length, block
+    size and count, skip density, fp16 rows (indexer modes)."""
+    rng = np.random.default_rng(11000 + k)
+    mode = int(rng.choice([0, 1, 3, 4, 5, 6]))
+    d = 64 * int(rng.integers(2, 41)) if mode in (0, 1, 4) else 32 * int(rng.integers(1, 81))
+    norm = mode == 4 or (mode in (0, 1) and bool(rng.random() < 0.5))
+    rope = mode == 4 or (mode in (0, 1) and bool(rng.random() < 0.5))
+    index_mode = int(rng.integers(1, 4))
+    B, S = int(rng.integers(1, 13)), int(rng.integers(1, 160))
+    if index_mode == 2:
+        bs = int(rng.integers(1, 64))
+        bn = B * (-(-S // bs)) + int(rng.integers(0, 4))
+    else:
+        bs = S + int(rng.integers(0, 40))
+        bn = B + int(rng.integers(0, 4))
+    x16 = mode in (3, 5, 6) and bool(rng.random() < 0.3)
+    return _indexed(mode, d, index_mode, B, S, bs, bn, seed=11000 + k, norm=norm, rope=rope,
+                    skip=float(rng.choice([0.0, 0.1, 0.5])),
+                    stride_extra=int(rng.choice([0, 16, 40])), x16=x16)
+
+
+@pytest.mark.parametrize("k", range(60))
+def test_index_fuzz(k):
+    check(_index_fuzz_case(k), f"index fuzz {k}")
