@@ -232,3 +232,29 @@ def _index_fuzz_case(k):
 @pytest.mark.parametrize("k", range(60))
 def test_index_fuzz(k):
     check(_index_fuzz_case(k), f"index fuzz {k}")
+
+
+def _rope_length_fuzz_case(k):
+    """A seeded random bf16-split workload with a rope segment of random even
+    length Dk (2..128) and a nope width Dv (a multiple of 8), random block
+    layout, skips and RMSNorm spread."""
+    rng = np.random.default_rng(13000 + k)
+    dk = 2 * int(rng.integers(1, 65))
+    dv = 8 * int(rng.integers(1, 200))
+    if dk == 64:  # the 64-column segment takes the standard layout: d % 64 == 0
+        dv = 64 * int(rng.integers(1, 25))
+    d = dv + dk
+    T, bs = int(rng.choice([1, 7, 64, int(rng.integers(1, 600))])), int(rng.integers(1, 40))
+    nblk = (T + bs - 1) // bs + 2
+    w = kvgen.make(f"rl{k}_dk{dk}_dv{dv}", 4, T, d, seed=13000 + k,
+                   cache=CacheSpec(nblk, bs, dv, bs * dv + 8 * int(rng.integers(0, 3)), 2),
+                   aux=CacheSpec(nblk, bs, dk, bs * dk + 2 * int(rng.integers(0, 5)), 2),
+                   norm=True, rope=True, row_sigma=float(rng.choice([0.0, 2.0])),
+                   skip_frac=float(rng.choice([0.0, 0.1])), rope_dim=dk)
+    return w, (-d) % 8 + 8 * int(rng.integers(0, 3))
+
+
+@pytest.mark.parametrize("k", range(30))
+def test_rope_length_fuzz(k):
+    w, x_pad = _rope_length_fuzz_case(k)
+    check(w, f"rope length fuzz {k}", x_pad=x_pad)
