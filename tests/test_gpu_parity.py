@@ -483,3 +483,13 @@ def _fuzz_case(k):
 def test_fuzz(k):
     w, kw = _fuzz_case(k)
     assert check(w, f"fuzz {k}: {w.name}", **kw) == 0
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_fuzz_few_waves(k, monkeypatch):
+    # the same random workloads on a grid capped at 8 waves, so that every
+    # wave runs many iterations (slot windows, the two-deep pipeline's
+    # hand-offs, the last partial window)
+    monkeypatch.setenv("KVEPI_MAX_WAVES", "8")
+    w, kw = _fuzz_case(k)
+    assert check(w, f"fuzz few waves {k}: {w.name}", **kw) == 0
