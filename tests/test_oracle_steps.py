@@ -115,7 +115,7 @@ def test_rmsnorm_eps_matters():
     assert bf16_to_f32(y)[0] < 0.8  # eps (1e-6) dominates x^2 (1e-6 too)
 
 
-def test_sumsq_tree_error_bound_and_order():
+def test_sumsq_tree_error_bound():
     rng = np.random.default_rng(11)
     for n in (64, 192, 512, 1000, 8128):
         x = to_bf16(rng.standard_normal(n) * 3)
@@ -124,13 +124,99 @@ def test_sumsq_tree_error_bound_and_order():
         got = oracle.sumsq_tree(x)
         depth = int(np.ceil(np.log2(n)))
         assert abs(got - exact) <= depth * 2.0 ** -24 * exact * 1.01
-    # the tree is balanced: a row whose halves are each exact sums but whose
-    # sequential sum would round differently.
-    x = np.zeros(4, np.float32)
-    x[:] = [2.0 ** 12, 1.0, 2.0 ** 12, 1.0]  # squares 2^24, 1, 2^24, 1
-    xb = to_bf16(x)
-    # ((2^24 + 1) + (2^24 + 1)) rounds each half to 2^24 -> 2^25
-    assert oracle.sumsq_tree(xb) == 2.0 ** 25
+
+
+# The summation order of the sum of squares.  The reading is a balanced
+# pairwise tree over the index order, zero-padded at the end to the next power
+# of two.  The sums below are written here from that description, independently
+# of the oracle's code, together with the orders a plausible slip would give:
+# a running sum, first-level pairs taken a half apart (i with i + p/2), and the
+# zero padding placed in front.  The rows are chosen so that each of those
+# orders gives a different fp32 sum from the reading's tree, so the oracle
+# matches the tree and none of the others.
+
+def _squares32(x_bf16):
+    v = bf16_to_f32(x_bf16)
+    return (v * v).astype(np.float32)  # one fp32 rounding (exact for normal bf16)
+
+
+def _pad(sq, front=False):
+    p = 1
+    while p < sq.size:
+        p *= 2
+    z = np.zeros(p - sq.size, np.float32)
+    return np.concatenate([z, sq] if front else [sq, z]).astype(np.float32)
+
+
+def _tree_recursive(a):
+    """Sum of a (a power-of-two length) as left half + right half, recursively,
+    every addition in fp32."""
+    if a.size == 1:
+        return np.float32(a[0])
+    h = a.size // 2
+    return np.float32(_tree_recursive(a[:h]) + _tree_recursive(a[h:]))
+
+
+def _tree_adjacent(a):
+    while a.size > 1:
+        a = (a[0::2] + a[1::2]).astype(np.float32)
+    return np.float32(a[0])
+
+
+def _tree_strided(a):
+    while a.size > 1:
+        h = a.size // 2
+        a = (a[:h] + a[h:]).astype(np.float32)
+    return np.float32(a[0])
+
+
+def _running(sq):
+    s = np.float32(0.0)
+    for v in sq:
+        s = np.float32(s + v)
+    return s
+
+
+def _order_rows(n, seed):
+    """Seeded bf16 rows of length n with squares spread over many binades (so
+    that the order of the additions shows), each of which separates the tree
+    from every wrong order that differs from it at this length."""
+    rng = np.random.default_rng(seed)
+    found = []
+    for _ in range(400):
+        mag = np.exp(rng.normal(0.0, 2.5, n))
+        x = to_bf16(rng.choice([-1.0, 1.0], n) * mag)
+        sq = _squares32(x)
+        tree = _tree_adjacent(_pad(sq))
+        wrong = [_running(sq), _tree_strided(_pad(sq))]
+        if n & (n - 1):
+            wrong.append(_tree_adjacent(_pad(sq, front=True)))
+        if all(w != tree for w in wrong):
+            found.append((x, tree))
+            if len(found) == 3:
+                return found
+    raise AssertionError(f"no separating row found for n = {n}")
+
+
+def test_sumsq_tree_written_two_ways_agree():
+    rng = np.random.default_rng(5)
+    for n in (8, 448, 512, 576):
+        a = _pad(_squares32(to_bf16(np.exp(rng.normal(0, 2.5, n)))))
+        assert _tree_recursive(a) == _tree_adjacent(a)
+
+
+@pytest.mark.parametrize("n,seed", [(448, 21), (512, 22)])
+def test_sumsq_tree_order_is_pinned(n, seed):
+    # 448 and 512 are nope lengths of the epilog's rows (d = 512 and 576)
+    for x, tree in _order_rows(n, seed):
+        got = np.float32(oracle.sumsq_tree(x))
+        assert got == tree
+        assert got == _tree_recursive(_pad(_squares32(x)))
+        sq = _squares32(x)
+        assert got != _running(sq)
+        assert got != _tree_strided(_pad(sq))
+        if n & (n - 1):
+            assert got != _tree_adjacent(_pad(sq, front=True))
 
 
 # ---- RoPE -------------------------------------------------------------------
