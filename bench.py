@@ -61,6 +61,20 @@ def algorithmic_bytes(w: kvgen.Workload, dense: bool = False) -> int:
     return 4 * w.T + read_rows * (x_row + rope) + hits * written + gamma
 
 
+def algorithmic_split(w: kvgen.Workload):
+    """(read, written) parts of algorithmic_bytes."""
+    total = algorithmic_bytes(w)
+    from kv_cache_epilog_amd import kvepi_row_bytes
+    if w.mode == kvgen.MODE_BF16_SPLIT:
+        written = 2 * (w.d - 64) + 2 * 64
+    elif w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
+        _, kc, sc = kvepi_row_bytes(w.mode, w.d, w.group_size)
+        written = kc + sc * w.aux.elem_bytes
+    else:
+        written = kvepi_row_bytes(w.mode, w.d, w.group_size)[1]
+    return total - w.hits * written, w.hits * written
+
+
 def code_text(text: str) -> str:
     """C++ source with its comments removed and every run of blank space
     made one space: what the compiler sees of it (no string literal of the
@@ -188,28 +202,227 @@ def cold_launches(step, dev, stream, launches: int = 20, scrub_mib: int = 512,
     return sum(e0.elapsed_time(e1) for e0, e1 in evs) / launches
 
 
-def copy_ceiling(dev, stream, mib: int = 512, warmup: int = 20, steps: int = 50):
-    """Achieved bandwidth of a plain device-to-device copy (torch's copy_,
-    the runtime's copy kernel) of mib MiB, timed in the same run with HIP
-    events on the launch stream: the practical ceiling that the kernel's
-    effective bandwidth is also compared with.  Bytes = read + written."""
+CEILING_LIB = os.path.join(ROOT, "kv_cache_epilog_amd", "libkvepi_ceiling.so")
+_ceil = None
+
+
+def ceiling_lib():
+    """The reference memory kernels (kv_cache_epilog_amd/csrc/kvepi_ceiling.hip)."""
+    global _ceil
+    if _ceil is None:
+        import ctypes
+        if not os.path.exists(CEILING_LIB):
+            raise RuntimeError(f"{CEILING_LIB} is missing: build it with "
+                               "`python -m kv_cache_epilog_amd.build`")
+        L = ctypes.CDLL(CEILING_LIB)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.kvc_stream.argtypes = [P, P, P, ctypes.c_uint64, I32, I32, I32, P]
+        L.kvc_stream.restype = ctypes.c_int
+        L.kvc_scatter_rows.argtypes = [P, I64, I32, P, I32, P, I32, I32, I64, I64, I32, I32, P]
+        L.kvc_scatter_rows.restype = ctypes.c_int
+        L.kvc_empty.argtypes = [I32, P]
+        L.kvc_empty.restype = ctypes.c_int
+        L.kvc_clock.argtypes = [P, I32, P]
+        L.kvc_clock.restype = ctypes.c_int
+        _ceil = L
+    return _ceil
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what}: hip error {rc}")
+
+
+def time_back_to_back(launch, stream, launches: int, warmup: int = 5) -> float:
+    """ms per launch of `launches` back-to-back launches, HIP events on the
+    launch stream around them (after `warmup` untimed launches)."""
     import torch
-    n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
     with torch.cuda.stream(stream):
         for _ in range(warmup):
-            dst.copy_(src)
+            launch()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(steps):
-            dst.copy_(src)
+        for _ in range(launches):
+            launch()
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    del src, dst
-    return 2 * n / (ms * 1e-3) / 1e9
+    return e0.elapsed_time(e1) / launches
+
+
+def shader_clock_mhz(dev, stream) -> float:
+    """The shader clock now, from kvc_clock (core clock counter over the
+    100 MHz reference counter across a ~15 us FMA chain of one wave)."""
+    import torch
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    _check(ceiling_lib().kvc_clock(out.data_ptr(), 4000, stream.cuda_stream), "kvc_clock")
+    torch.cuda.synchronize()
+    t0, t1, r0, r1 = (int(v) for v in out.cpu())
+    return 100.0 * (t1 - t0) / max(r1 - r0, 1)
+
+
+SETTLE_MS = 60.0
+
+
+def settle(step, dev, stream, ms: float = SETTLE_MS, group: int = 10):
+    """Runs the timed step back to back for about `ms` of device time before
+    the warm-up.  When the epilog starts, the device lowers its shader clock
+    (from about 2.4 GHz to about 1.7 GHz, measured with kvc_clock between
+    groups of launches) and brings it back within about 15-20 ms of
+    sustained load; copies do not trigger this.  Settling first makes the
+    timed region see the steady clock whatever --warmup is.  Returns the
+    launches run and the shader clock after them."""
+    import torch
+    n, spent = 0, 0.0
+    while spent < ms and n < 200000:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(group):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+        n += group
+    return {"launches": n, "ms": spent, "sclk_mhz_after": shader_clock_mhz(dev, stream)}
+
+
+def device_cus() -> int:
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+class StreamCeiling:
+    """The streaming kernel kvc_stream over buffers of `total_bytes` (read +
+    written) in the read:write mix r:w, with `per_cu` blocks of 256 threads
+    per CU."""
+
+    def __init__(self, dev, stream, total_bytes: int, r: int, w: int, per_cu: int = 4):
+        import torch
+        self.r, self.w = r, w
+        self.steps = max(1, int(total_bytes // (1024 * (r + w))))
+        self.bytes = self.steps * 1024 * (r + w)
+        self.src = torch.zeros(max(1, self.steps * r * 1024), dtype=torch.uint8, device=dev)
+        self.dst = torch.empty(max(1, self.steps * w * 1024), dtype=torch.uint8, device=dev)
+        self.sink = torch.empty(8 * device_cus() * 256 * 16, dtype=torch.uint8, device=dev)
+        self.stream = stream
+        self.per_cu = per_cu
+
+    def launch(self):
+        _check(ceiling_lib().kvc_stream(self.src.data_ptr(), self.dst.data_ptr(),
+                                        self.sink.data_ptr(), self.steps, self.r, self.w,
+                                        self.per_cu * device_cus(), self.stream.cuda_stream),
+               "kvc_stream")
+
+    def gbps(self, ms: float) -> float:
+        return self.bytes / (ms * 1e-3) / 1e9
+
+    def best(self, launches: int):
+        """Times the grids of 2, 4 and 8 blocks per CU (the rate of a
+        streaming kernel depends on how many waves share the memory
+        system); keeps the fastest.  Returns its ms per launch."""
+        times = {}
+        for per_cu in (2, 4, 8):
+            self.per_cu = per_cu
+            times[per_cu] = time_back_to_back(self.launch, self.stream, launches)
+        self.per_cu = min(times, key=times.get)
+        return times[self.per_cu]
+
+
+def mix_of(read_bytes: float, write_bytes: float):
+    """The streaming kernel's read:write mix closest to a workload's."""
+    ratio = read_bytes / max(write_bytes, 1.0)
+    return min(((1, 1), (2, 1), (4, 1)), key=lambda m: abs(np.log(ratio / (m[0] / m[1]))))
+
+
+def ceilings(dev, stream, abytes: int, read_bytes: int, write_bytes: int, launches: int = 50):
+    """Reference kernels timed in the same run: plain streaming at 512 MiB
+    (copy, read-only, the workload's read:write mix) and at the workload's own
+    byte count and mix (back to back), and an empty launch of the streaming
+    grid.  Returns the dict of the JSON line's copy_ceiling (without the
+    epilog's fractions, filled in by the caller)."""
+    out = {"unit": "GB/s", "kernel": "kvc_stream (kv_cache_epilog_amd/csrc/kvepi_ceiling.hip): "
+                                     "16-byte nontemporal loads, 16-byte stores, the fastest "
+                                     "of 2, 4 and 8 blocks per CU"}
+    r, w = mix_of(read_bytes, write_bytes)
+    for name, tb, rr, ww in (("copy_512MiB", 1 << 30, 1, 1), ("read_512MiB", 1 << 29, 1, 0),
+                             ("mix_512MiB", (1 << 29) * (r + w) // r, r, w)):
+        c = StreamCeiling(dev, stream, tb, rr, ww)
+        out[name] = c.gbps(c.best(20))
+        del c
+    c = StreamCeiling(dev, stream, abytes, r, w)
+    ms = c.best(launches)
+    out.update({"mix": f"{r}:{w}", "bytes": c.bytes, "achieved": c.gbps(ms),
+                "ms_per_launch": ms, "blocks_per_cu": c.per_cu})
+    out["_same_size"] = c
+    lib = ceiling_lib()
+    blocks = 8 * device_cus()
+    out["empty_launch_us"] = 1e3 * time_back_to_back(
+        lambda: _check(lib.kvc_empty(blocks, stream.cuda_stream), "kvc_empty"), stream, launches)
+    return out
+
+
+def finish_ceiling(cc: dict, achieved: float, stream, dev) -> dict:
+    """Completes ceilings()'s dict once the epilog has been timed: the
+    epilog's effective bandwidth over the same-size streaming rate (frac) and
+    over the 512 MiB ones, and the same-size kernel timed cold (after the
+    same scrub as the epilog's cold launches)."""
+    c = cc.pop("_same_size")
+    cc["frac"] = achieved / cc["achieved"]
+    for k in ("copy_512MiB", "read_512MiB", "mix_512MiB"):
+        cc["frac_of_" + k] = achieved / cc[k]
+    ms_cold = cold_launches(c.launch, dev, stream)
+    cc["cold_achieved"] = c.gbps(ms_cold)
+    cc["cold_ms_per_launch"] = ms_cold
+    del c
+    return cc
+
+
+def metric_name(w: kvgen.Workload) -> str:
+    """The headline metric for the fused d = 576 workload, else the same
+    metric named for the workload timed."""
+    if w.name == kvgen.CONFIG_NAMES[4]:
+        return METRIC
+    return f"tokens/s and effective HBM GB/s (% of peak), {w.name}"
+
+
+def pattern_ceiling(w: kvgen.Workload, dev, stream, launches: int = 50):
+    """The epilog's own memory pattern with no arithmetic (kvc_scatter_rows):
+    every hit row reads its input bytes (x, plus cos and sin with RoPE, as one
+    row rounded up to 16 bytes) and writes its row (kvCacheCol rounded up to
+    16 bytes; the aux row left out) to its slot's row of a buffer with the
+    cache's geometry.  Returns ms per launch back to back, and the kernel's
+    bytes per launch."""
+    import torch
+    src_row = 2 * w.d + (256 if w.cos is not None else 0)
+    src_row = (src_row + 15) // 16 * 16
+    from kv_cache_epilog_amd import kvepi_row_bytes
+    if w.mode == kvgen.MODE_BF16_SPLIT:
+        row = 2 * (w.d - 64)
+    else:
+        row = kvepi_row_bytes(w.mode, w.d, w.group_size)[1]
+    row = (row + 15) // 16 * 16
+    pitch = w.cache.head_dim * w.cache.elem_bytes
+    bstride = w.cache.block_stride * w.cache.elem_bytes
+    if row > 2048 or src_row > 2048 or pitch % 16 or bstride % 16 or row > pitch:
+        return None
+    src = torch.zeros(w.T * src_row, dtype=torch.uint8, device=dev)
+    dst = torch.empty(w.cache.block_num * bstride, dtype=torch.uint8, device=dev)
+    slots = torch.from_numpy(w.slots).to(dev)
+    lib = ceiling_lib()
+    blocks = 8 * device_cus()
+
+    def launch():
+        _check(lib.kvc_scatter_rows(src.data_ptr(), src_row, src_row, slots.data_ptr(), w.T,
+                                    dst.data_ptr(), row, w.cache.block_size, pitch, bstride,
+                                    w.cache.num_slots, blocks, stream.cuda_stream),
+               "kvc_scatter_rows")
+
+    ms = time_back_to_back(launch, stream, launches)
+    nbytes = 4 * w.T + w.hits * (src_row + row)
+    del src, dst, slots
+    return {"ms_per_launch": ms, "bytes": nbytes, "achieved": nbytes / (ms * 1e-3) / 1e9,
+            "src_row_bytes": src_row, "row_bytes": row}
 
 
 def upload(w: kvgen.Workload, dev):
@@ -312,6 +525,10 @@ def main():
                     help="time the dequant -> RoPE -> int8 KV cache operator on this "
                          "workload instead of the epilog")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="device time of back-to-back steps run before the warm-up so that "
+                         "the shader clock has recovered from the drop the start of the "
+                         "load causes (0: none)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times "
@@ -355,6 +572,14 @@ def main():
         kvepi_run(t["x"], t["slots"], t["cache"], w.mode, w.group_size, gamma=t["gamma"],
                   cos=t["cos"], sin=t["sin"], cache_aux=t["aux"], eps=w.eps, stream=stream)
 
+    abytes = algorithmic_bytes(w)
+    rbytes, wbytes = algorithmic_split(w)
+    # Reference kernels first: they also bring the device out of idle before
+    # the epilog's own warm-up (see the copy_ceiling entry of the line).
+    cc = ceilings(dev, stream, abytes, rbytes, wbytes)
+    pat = pattern_ceiling(w, dev, stream)
+    st = settle(step, dev, stream, args.settle_ms) if args.settle_ms > 0 else None
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -373,13 +598,13 @@ def main():
     ms_total = total0.elapsed_time(total1)
     ms_per_step = ms_total / args.steps
     ms_kernel = ms_per_step
+    sclk_after = shader_clock_mhz(dev, stream)
 
-    abytes = algorithmic_bytes(w)
     achieved = abytes / (ms_kernel * 1e-3) / 1e9
     tokens_per_s = w.T / (ms_per_step * 1e-3)
 
     result = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric_name(w), "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded)",
@@ -393,19 +618,25 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name),
                      "algorithmic_bytes_per_launch": abytes,
+                     "algorithmic_read_bytes": rbytes, "algorithmic_write_bytes": wbytes,
                      "dense_bytes_per_launch": algorithmic_bytes(w, dense=True),
                      "kernel_ms_mean": ms_kernel},
     }
-    cc = copy_ceiling(dev, stream)
-    result["copy_ceiling"] = {"achieved": cc, "unit": "GB/s", "kernel": "device copy, 512 MiB",
-                              "frac": achieved / cc}
+    result["settle"] = dict(st or {"launches": 0, "ms": 0.0}, sclk_mhz_after_timed=sclk_after)
+    result["copy_ceiling"] = finish_ceiling(cc, achieved, stream, dev)
+    if pat is not None:
+        result["copy_ceiling"]["pattern"] = dict(
+            pat, frac=pat["ms_per_launch"] / ms_kernel,
+            kernel="kvc_scatter_rows: the epilog's reads and row writes, no arithmetic")
     ms_cold = cold_launches(step, dev, stream)
     ms_single = cold_launches(step, dev, stream, scrub=False)
     result["cold"] = {"ms_per_launch": ms_cold, "tokens_per_s": w.T / (ms_cold * 1e-3),
                       "achieved": abytes / (ms_cold * 1e-3) / 1e9, "unit": "GB/s",
                       "frac": abytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                       "launches": 20, "scrub": "512 MiB read-only reduction before each launch",
-                      "ms_per_launch_unscrubbed": ms_single}
+                      "ms_per_launch_unscrubbed": ms_single,
+                      "frac_of_ceiling_cold": abytes / (ms_cold * 1e-3) / 1e9 /
+                      result["copy_ceiling"]["cold_achieved"]}
     if not args.no_cpu:
         n, dt, ocache, oaux = cpu_baseline(w, args.cpu_seconds)
         ncpu, model = host_info()
@@ -432,17 +663,22 @@ def drq_algorithmic_bytes(w) -> int:
     index (and activation scale), q_out (and k_out, v_out); per token with a
     cache row the int8 k and v rows; once the weight scales, bias and the
     per-channel scales and offsets."""
+    return sum(drq_algorithmic_split(w))
+
+
+def drq_algorithmic_split(w):
+    """(read, written) parts of drq_algorithmic_bytes."""
     H = (w.nq + 2 * w.nkv) * w.D
     xb = 4 if w.x_dtype == kvgen.DT_INT32 else 2
     if w.cache_mode == 0:
         hits = int(np.count_nonzero((w.index >= 0) & (w.index < w.geom[0] * w.geom[1])))
     else:
         hits = int(sum(max(0, min(w.seq_len, w.geom[1] - v)) for v in w.index if v >= 0))
-    per_token = H * xb + 2 * 2 * w.D + 4 + (4 if w.act_scale is not None else 0)
-    per_token += 2 * w.nq * w.D + (2 * 2 * w.nkv * w.D if w.kv_output else 0)
+    read_token = H * xb + 2 * 2 * w.D + 4 + (4 if w.act_scale is not None else 0)
+    write_token = 2 * w.nq * w.D + (2 * 2 * w.nkv * w.D if w.kv_output else 0)
     once = sum(a.nbytes for a in (w.weight_scale, w.bias, w.scale_k, w.scale_v, w.offset_k,
                                   w.offset_v) if a is not None)
-    return w.T * per_token + hits * 2 * w.nkv * w.D + once
+    return w.T * read_token + once, w.T * write_token + hits * 2 * w.nkv * w.D
 
 
 def main_drq(args):
@@ -480,6 +716,12 @@ def main_drq(args):
                      offset_k=up(w.offset_k), offset_v=up(w.offset_v), cache_mode=w.cache_mode,
                      seq_len=w.seq_len)
     stream = torch.cuda.current_stream(dev)
+    abytes = drq_algorithmic_bytes(w)
+    rbytes, wbytes = drq_algorithmic_split(w)
+    # reference kernels first (they also bring the device out of idle)
+    cc = ceilings(dev, stream, abytes, rbytes, wbytes)
+    st = (settle(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream, args.settle_ms)
+          if args.settle_ms > 0 else None)
     for _ in range(args.warmup):
         B.kvepi_drq_run(p, stream=stream)
     torch.cuda.synchronize()
@@ -491,7 +733,7 @@ def main_drq(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    abytes = drq_algorithmic_bytes(w)
+    sclk_after = shader_clock_mhz(dev, stream)
     achieved = abytes / (ms * 1e-3) / 1e9
     H = (w.nq + 2 * w.nkv) * w.D
     result = {
@@ -506,11 +748,12 @@ def main_drq(args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(args.drq, DRQ_SRC),
-                     "algorithmic_bytes_per_launch": abytes, "kernel_ms_mean": ms},
+                     "algorithmic_bytes_per_launch": abytes,
+                     "algorithmic_read_bytes": rbytes, "algorithmic_write_bytes": wbytes,
+                     "kernel_ms_mean": ms},
     }
-    cc = copy_ceiling(dev, stream)
-    result["copy_ceiling"] = {"achieved": cc, "unit": "GB/s", "kernel": "device copy, 512 MiB",
-                              "frac": achieved / cc}
+    result["settle"] = dict(st or {"launches": 0, "ms": 0.0}, sclk_mhz_after_timed=sclk_after)
+    result["copy_ceiling"] = finish_ceiling(cc, achieved, stream, dev)
     ms_cold = cold_launches(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream)
     ms_single = cold_launches(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream,
                               scrub=False)
@@ -518,7 +761,9 @@ def main_drq(args):
                       "achieved": abytes / (ms_cold * 1e-3) / 1e9, "unit": "GB/s",
                       "frac": abytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                       "launches": 20, "scrub": "512 MiB read-only reduction before each launch",
-                      "ms_per_launch_unscrubbed": ms_single}
+                      "ms_per_launch_unscrubbed": ms_single,
+                      "frac_of_ceiling_cold": abytes / (ms_cold * 1e-3) / 1e9 /
+                      result["copy_ceiling"]["cold_achieved"]}
     if not args.no_cpu:
         import oracle
         kc = np.full(bn * stride, 0xAB, np.uint8)

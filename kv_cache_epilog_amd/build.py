@@ -55,6 +55,19 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+CEILING_SRC = os.path.join(CSRC, "kvepi_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libkvepi_ceiling.so")
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """Builds libkvepi_ceiling.so, the reference memory kernels bench.py
+    times beside the epilog (a separate library: not part of the C ABI)."""
+    tmp = CEILING_LIB + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, "-o", tmp, CEILING_SRC], verbose)
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
 HW_CHECK_SRC = os.path.join(ROOT, "tests", "hw_check.hip")
 HW_CHECK_BIN = os.path.join(ROOT, "tests", "hw_check")
 
@@ -77,4 +90,5 @@ def build_hw_check(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ceiling(verbose=True))
     print(build_hw_check(verbose=True))

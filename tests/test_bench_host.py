@@ -83,3 +83,29 @@ def test_code_hash_ignores_comments_only():
     c = "int f(int x) {\n  return x + 2;  // one more\n}\n"
     assert bench.code_text(a) == bench.code_text(b)
     assert bench.code_text(a) != bench.code_text(c)
+
+
+def test_algorithmic_split_by_hand():
+    # fused d = 576: reads are the slots, x + cos + sin of every hit row and
+    # gamma; writes are the 672-byte rows
+    w = kvgen.config(4)
+    r, wr = bench.algorithmic_split(w)
+    assert r == 4 * 262144 + 254280 * 1408 + 1024
+    assert wr == 254280 * 672
+    assert r + wr == bench.algorithmic_bytes(w)
+    # MX-FP4 indexer: 64 code bytes and a 4-byte scale row written per hit
+    w = kvgen.config(3)
+    assert bench.algorithmic_split(w) == (4 * 131072 + 129761 * 256, 129761 * 68)
+
+
+def test_ceiling_mix_follows_the_workload():
+    # the streaming mix closest (in log ratio) to the workload's read:write
+    assert bench.mix_of(1408, 672) == (2, 1)
+    assert bench.mix_of(1152, 648) == (2, 1)
+    assert bench.mix_of(256, 68) == (4, 1)
+    assert bench.mix_of(100, 100) == (1, 1)
+
+
+def test_metric_is_named_for_the_workload():
+    assert bench.metric_name(kvgen.config(4)) == bench.METRIC
+    assert bench.metric_name(kvgen.config(3)).endswith("mxfp4_indexer_d128")

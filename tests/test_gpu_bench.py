@@ -38,13 +38,23 @@ def _check(d, steps, warmup):
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
     assert r["traffic"] is None or r["traffic"] > 0
-    assert d["copy_ceiling"]["achieved"] > 0 and d["cold"]["ms_per_launch"] > 0
+    c = d["copy_ceiling"]
+    assert c["achieved"] > 0 and c["cold_achieved"] > 0 and d["cold"]["ms_per_launch"] > 0
+    assert abs(c["frac"] - r["achieved"] / c["achieved"]) < 1e-9
+    for k in ("copy_512MiB", "read_512MiB", "mix_512MiB"):
+        assert c[k] > 0 and abs(c["frac_of_" + k] - r["achieved"] / c[k]) < 1e-9
+    assert c["mix"] in ("1:1", "2:1", "4:1") and c["empty_launch_us"] > 0
+    assert r["algorithmic_read_bytes"] + r["algorithmic_write_bytes"] == \
+        r["algorithmic_bytes_per_launch"]
 
 
 def test_epilog_bench_line():
     d = _run("--config", "0", "--steps", "3", "--warmup", "2")
     _check(d, 3, 2)
     assert d["config"]["workload"] == "mode0_tiny_d256"
+    assert d["metric"].endswith("mode0_tiny_d256")
+    pat = d["copy_ceiling"]["pattern"]
+    assert pat["ms_per_launch"] > 0 and pat["row_bytes"] == 352 and pat["src_row_bytes"] == 512
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0 and cb["gbps"] > 0
     assert d["parity_sample_bytes_equal"] is True
