@@ -101,6 +101,7 @@ typedef enum kvepi_status {
 #define KVEPI_MODE_BF16_SPLIT 4
 #define KVEPI_MODE_MXFP8 5
 #define KVEPI_MODE_FP8_ROW 6
+#define KVEPI_MODE_FP4_NOPE 7
 
 /* A paged cache [block_num, block_size, 1, head_dim] ("aclnnKvCompressEpilog",
  * 约束说明: four dimensions, dimension -2 fixed at 1, only the block

@@ -63,6 +63,17 @@ kvepi_status row_geometry(int32_t mode, int64_t d, int32_t group_size,
       *kc = d;
       *sc = 1;
       return KVEPI_OK;
+    case KVEPI_MODE_FP4_NOPE: {
+      // quantMode=2: concatCol = 64 + (d-64)/2 + ((d-64)/G)*2, padded to 32
+      // bytes; G in {16, 32, 64} dividing d-64
+      if (d % 64 != 0 || d <= 64 || d > 8192) return KVEPI_ERR_SHAPE;
+      if (group_size != 16 && group_size != 32 && group_size != 64) return KVEPI_ERR_PARAM;
+      if ((d - 64) % group_size != 0) return KVEPI_ERR_SHAPE;
+      *cc = 64 + (d - 64) / 2 + ((d - 64) / group_size) * 2;
+      *kc = (*cc + 31) / 32 * 32;
+      *sc = (d - 64) / group_size;
+      return KVEPI_OK;
+    }
     case KVEPI_MODE_BF16_SPLIT:
       if (d % 64 != 0 || d <= 64 || d > 8192) return KVEPI_ERR_SHAPE;
       *cc = d - 64;
@@ -107,6 +118,7 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
                             int32_t group_size, float eps, const kvepi_options *opt,
                             kvepi_plan *p) {
   if (quant_mode == KVEPI_MODE_HIF8_FP4) return KVEPI_ERR_UNSUPPORTED;
+  if (quant_mode == KVEPI_MODE_FP4_NOPE) return KVEPI_ERR_UNSUPPORTED;  // no kernel yet
   const kvepi_options o = opt != nullptr ? *opt : kvepi_options{0, 0, 0, 0, 0};
   if (o.x_dtype != KVEPI_X_BF16 && o.x_dtype != KVEPI_X_FP16) return KVEPI_ERR_PARAM;
   if (o.index_mode < KVEPI_INDEX_SLOT || o.index_mode > KVEPI_INDEX_BATCH_START)

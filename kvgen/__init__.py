@@ -26,6 +26,7 @@ MODE_MXFP4 = 3
 MODE_BF16_SPLIT = 4
 MODE_MXFP8 = 5
 MODE_FP8_ROW = 6
+MODE_FP4_NOPE = 7
 
 PREFILL = 0xAB
 
@@ -186,7 +187,8 @@ def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
          rope_dim: int = 64) -> Workload:
     rng = np.random.default_rng(seed)
     if group_size is None:
-        group_size = {MODE_MXFP4: 32, MODE_MXFP8: 32, MODE_FP8_ROW: 0}.get(mode, 64)
+        group_size = {MODE_MXFP4: 32, MODE_MXFP8: 32, MODE_FP8_ROW: 0,
+                      MODE_FP4_NOPE: 32}.get(mode, 64)
     if x is None:
         x = normal_rows(rng, T, d, row_sigma, outlier_frac)
     gamma = cos = sin = None
@@ -208,7 +210,9 @@ def make(name: str, mode: int, T: int, d: int, *, seed: int, cache: CacheSpec,
 CONFIG_NAMES = ("mode0_tiny_d256", "rmsnorm_rope_bf16_d576", "mode1_prefill_d576",
                 "mxfp4_indexer_d128", "fused_epilog_d576",
                 # the other indexer modes at the MX-FP4 indexer's shape
-                "mxfp8_indexer_d128", "fp8row_indexer_d128")
+                "mxfp8_indexer_d128", "fp8row_indexer_d128",
+                # quantMode 2's FP4 nope segment at the fused workload's shape
+                "fp4_nope_d576")
 
 
 def config(i: int) -> Workload:
@@ -258,6 +262,14 @@ def config(i: int) -> Workload:
                     cache=CacheSpec(1024, 128, 128, 128 * 128),
                     aux=CacheSpec(1024, 128, 1, 128 * 1, 4),
                     row_sigma=1.0, skip_frac=0.01)
+    if i == 7:
+        # quantMode 2's nope segment after RMSNorm at the shape of 4:
+        # [262144,576], RMSNorm(512), group-32 E2M1 codes with bf16 scales;
+        # 352-byte rows (64 rope bytes left untouched) in a cache
+        # [2048,128,1,352] whose block stride is 1.25x the dense one; 3% skipped.
+        return make(CONFIG_NAMES[7], MODE_FP4_NOPE, 262144, 576, seed=7,
+                    cache=CacheSpec(2048, 128, 352, 128 * 352 * 5 // 4),
+                    norm=True, skip_frac=0.03, group_size=32)
     raise IndexError(i)
 
 

@@ -27,6 +27,7 @@ MODE_MXFP4 = 3
 MODE_BF16_SPLIT = 4
 MODE_MXFP8 = 5
 MODE_FP8_ROW = 6
+MODE_FP4_NOPE = 7
 
 _lib = None
 
@@ -209,6 +210,8 @@ def quant_row(mode: int, v_bf16, group_size: int, *, x_fp16: bool = False):
         return out, sout[:sc]
     if mode == MODE_FP8_ROW:
         return out, sout[:4].view(np.float32)  # the fp32 scale
+    if mode == MODE_FP4_NOPE:
+        return out[64:].copy(), None  # the bytes written: the row from byte 64 on
     return out, None
 
 

@@ -11,11 +11,12 @@
  * no excess precision, no contraction); binary64 is used only where a value
  * is exact in it (comparisons against fmax*2^E, scaled code search).
  *
- * Parity unpinned: the codes of quantMode 0 and of the indexer fp8 mode
- * divide each value by the scale as it is stored (bf16 in quantMode 0, fp32
- * in the fp8 mode), not by the unrounded amax / 448.  The pages print no
- * example that tells the two apart; the tests pin this choice only where the
- * two agree (power-of-two scales).
+ * Parity unpinned: the codes of quantMode 0, of quantMode 2's FP4 nope
+ * segment and of the indexer fp8 mode divide each value by the scale as it
+ * is stored (bf16 in quantMode 0 and 2, fp32 in the fp8 mode), not by the
+ * unrounded amax / FP_MAX.  The pages print no example that tells the two
+ * apart; the tests pin this choice only where the two agree (power-of-two
+ * scales) and otherwise check the reading's own hand-worked codes.
  */
 #include "kvepi_oracle.h"
 
@@ -321,6 +322,15 @@ int kvo_row_bytes(int mode, int64_t d, int32_t group_size, int64_t *concat_col,
     cc = d;
     kc = d;
     sc = 1; /* one FLOAT per row */
+  } else if (mode == KVO_MODE_FP4_NOPE) {
+    /* quantMode=2: concatCol = 64 + (d-64)/2 + ((d-64)/G)*2, aligned to
+     * 32 bytes; G in {16, 32, 64} dividing d-64 */
+    if (d % 64 != 0 || d <= 64 || d > 8192) return -1;
+    if (group_size != 16 && group_size != 32 && group_size != 64) return -1;
+    if ((d - 64) % group_size != 0) return -1;
+    cc = 64 + (d - 64) / 2 + ((d - 64) / group_size) * 2;
+    kc = (cc + 31) / 32 * 32;
+    sc = (d - 64) / group_size;
   } else if (mode == KVO_MODE_BF16_SPLIT) {
     if (d % 64 != 0 || d <= 64 || d > 8192) return -1;
     cc = d - 64; /* ckv elements per row */
@@ -391,6 +401,35 @@ int kvo_quant_row_x(int mode, const uint16_t *v, int64_t d, int32_t group_size, 
       }
     }
     for (int64_t j = 0; j < 64; ++j) put_u16le(out + nope + 2 * j, v[nope + j]);
+    return 0;
+  }
+  if (mode == KVO_MODE_FP4_NOPE) {
+    /* "aclnnKvCompressEpilog" scene 3, nope segment: per group of
+     * group_size values scale_g = max|x_g| / 6, stored as bf16 (2 bytes,
+     * little-endian, after the codes), codes E2M1(x_i / scale_g) dividing
+     * by the scale as stored, two per byte (element 2j in the low nibble);
+     * an all-zero group has scale 0 and codes 0.  Bytes [0, 64) are the
+     * rope segment's and are not written here. */
+    if (fp16) return -1; /* x must be bf16 (约束说明) */
+    const int64_t nope = d - 64;
+    memset(out + 64, 0, (size_t)(kc - 64));
+    for (int64_t g = 0; g < sc; ++g) {
+      const int64_t i0 = g * group_size, i1 = i0 + group_size;
+      float amax = 0.0f;
+      for (int64_t i = i0; i < i1; ++i) {
+        float a = fabsf(kvo_bf16_to_f32(v[i]));
+        if (a > amax) amax = a;
+      }
+      const float s32 = amax / 6.0f; /* scale_g = max|x_g| / FP4_MAX */
+      const uint16_t sb = kvo_f32_to_bf16(s32);
+      put_u16le(out + 64 + nope / 2 + 2 * g, sb);
+      const float s_use = kvo_bf16_to_f32(sb);
+      for (int64_t i = i0; i < i1; ++i) {
+        const uint8_t c = s_use == 0.0f ? 0x0 : kvo_enc_e2m1(kvo_bf16_to_f32(v[i]) / s_use);
+        uint8_t *b = out + 64 + i / 2;
+        *b = (i % 2 == 0) ? (uint8_t)((*b & 0xF0) | c) : (uint8_t)((*b & 0x0F) | (c << 4));
+      }
+    }
     return 0;
   }
   if (mode == KVO_MODE_MXFP4) {
@@ -541,6 +580,7 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
                       mode == KVO_MODE_FP8_ROW;
   if (indexer && (gamma || cos)) return -1;
   if (mode == KVO_MODE_BF16_SPLIT && (!gamma || !cos)) return -1;
+  if (mode == KVO_MODE_FP4_NOPE && (cos || aux)) return -1; /* rope bytes not written */
   if ((indexer || mode == KVO_MODE_BF16_SPLIT) && !aux) return -1;
   if (x_fp16 && !indexer) return -1;
   const int64_t dk = rope_dim;
@@ -566,6 +606,11 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
       kvo_rmsnorm_row(xr, gamma, nope, eps, v);
     else
       memcpy(v, xr, (size_t)nope * sizeof(uint16_t));
+    if (mode == KVO_MODE_FP4_NOPE) {
+      kvo_quant_row(mode, v, d, group_size, row, NULL);
+      memcpy(row_ptr(cache, s, 1) + 64, row + 64, (size_t)(kc - 64));
+      continue;
+    }
     if (cos)
       kvo_rope_row_n(xr + nope, cos + t * dk, sin + t * dk, dk, v + nope);
     else

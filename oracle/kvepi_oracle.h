@@ -22,6 +22,13 @@
  *    values.  The same page's mxfp8 mode (E4M3 codes, groups of 32, e8m0
  *    scale) and fp8 mode (E4M3 codes, the whole row one group, one FLOAT
  *    scale per row in cache_scale).
+ *  - "aclnnKvCompressEpilog", 计算公式 scene 3 (quantMode=2) and 约束说明:
+ *    the nope segment in groups of quantGroupSize (16, 32 or 64) values,
+ *    scale_g = max|x_g| / FP4_MAX (6) stored in 2 bytes, codes
+ *    FLOAT4_E2M1(x_i / scale_g); the row is 64 rope bytes, (d-64)/2 code
+ *    bytes and 2 bytes per group, padded to 32 bytes.  The rope bytes are
+ *    HiFloat8 codes, a format the pages do not define: this mode writes the
+ *    rest of the row and leaves them untouched.
  *
  * Arithmetic: IEEE fp32 (the precision the quantiser's division is defined
  * in), evaluated in the order written, compiled with -ffp-contract=off.  The
@@ -46,6 +53,9 @@ extern "C" {
 #define KVO_MODE_BF16_SPLIT 4    /* RMSNorm -> ckv cache, RoPE -> k cache  */
 #define KVO_MODE_MXFP8 5         /* group-32 E4M3 codes, e8m0 scale row    */
 #define KVO_MODE_FP8_ROW 6       /* whole-row E4M3 codes, fp32 scale       */
+#define KVO_MODE_FP4_NOPE 7      /* quantMode 2's nope half: group-G E2M1  */
+                                 /* nibbles, bf16 scales; the 64 rope      */
+                                 /* bytes at the row start not written     */
 
 /* ---- number formats ---------------------------------------------------- */
 float kvo_bf16_to_f32(uint16_t h);

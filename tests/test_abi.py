@@ -63,7 +63,8 @@ def test_row_bytes_page_values(row):
 
 
 @pytest.mark.parametrize("mode,d,g,status", [
-    (2, 256, 64, 5), (7, 256, 64, 5), (0, 100, 64, 2), (0, 64, 64, 2), (1, 8256, 64, 2),
+    (2, 256, 64, 5), (8, 256, 64, 5), (7, 256, 8, 4), (7, 256, 128, 4), (7, 100, 32, 2),
+    (7, 8256, 64, 2), (0, 100, 64, 2), (0, 64, 64, 2), (1, 8256, 64, 2),
     (0, 256, 32, 4), (3, 48, 32, 2), (3, 128, 64, 4), (3, 8224, 32, 2),
     (5, 48, 32, 2), (5, 128, 64, 4), (5, 8224, 32, 2), (6, 96, 32, 4), (6, 48, 0, 2),
     (6, 128, 64, 4)])
