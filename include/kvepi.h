@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVEPI_VERSION 120 /* 1.2.0: options (fp16 rows, index modes, rope length) */
+#define KVEPI_VERSION 130 /* 1.3.0: mode 7 (quantMode 2's FP4 nope segment) */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KVEPI_API __attribute__((visibility("default")))
@@ -76,8 +76,9 @@ typedef enum kvepi_status {
  *  1  as 0, scale stored as one e8m0 byte, the power of two 2^E with E the
  *     smallest integer such that amax <= 448 * 2^E (quantMode=1).  Row is not
  *     padded.
- *  2  quantMode=2 of the page (HiFloat8 rope + FP4 nope): not implemented,
- *     the HiFloat8 encoding is not defined there -> KVEPI_ERR_UNSUPPORTED.
+ *  2  quantMode=2 of the page (HiFloat8 rope + FP4 nope): the HiFloat8
+ *     encoding is not defined there -> KVEPI_ERR_UNSUPPORTED; its nope half
+ *     is mode 7.
  *  3  MX-FP4: E2M1 codes of the whole row, two per byte (element 2j in the
  *     low nibble), one e8m0 scale (amax <= 6 * 2^E) per group of 32 written
  *     to cache_aux ("indexer_quant_cache", mxfp4 mode).
@@ -91,8 +92,20 @@ typedef enum kvepi_status {
  *     s = amax / 448 in fp32 (a zero row: s = 0, all codes 0), s written as
  *     one little-endian fp32 value to cache_aux, whose elements are 4-byte
  *     floats ("indexer_quant_cache", fp8 mode: cache_scale is FLOAT).
+ *  7  quantMode=2's FP4 nope segment ("aclnnKvCompressEpilog" 计算公式
+ *     scene 3, 约束说明): the d-64 nope values in groups of group_size (16,
+ *     32 or 64), scale = amax/6 stored as bf16, E2M1 codes of x / scale (the
+ *     stored scale) two per byte (element 2j in the low nibble).
+ *     Row: [64 rope bytes, NOT written | (d-64)/2 code bytes |
+ *     (d-64)/group_size bf16 scales | zero pad to a multiple of 32 bytes]:
+ *     the rope segment's HiFloat8 codes are left untouched.  Takes gamma
+ *     (RMSNorm over the nope values first), not cos/sin; bf16 x only.
  * Modes 3, 5 and 6 are the indexer modes: they take neither gamma nor
  * cos/sin and need cache_aux.
+ * NaN: the RMSNorm of an all-zero row with eps = 0 is 0/0 = NaN; NaN values
+ * are left out of a group's amax (a group of NaNs gets scale 0 and codes 0),
+ * and a NaN quotient is encoded as 0x7F (E4M3) or 0x7 (E2M1).  NaN or
+ * infinite inputs x are outside the contract.
  */
 #define KVEPI_MODE_FP8_BF16SCALE 0
 #define KVEPI_MODE_FP8_E8M0 1
@@ -129,16 +142,19 @@ typedef struct kvepi_cache {
  * concatCol rounded up to 32 bytes for mode 0; e.g. d=256 in mode 1 gives
  * 323.  "indexer_quant_cache", 约束: MX-FP4 codes take ceil(d/2) bytes and
  * scaleCol = ceil(d/32), e.g. d=128 gives 4; MX-FP8 codes take d bytes with
- * the same scaleCol; the per-row FP8 mode takes d bytes and scaleCol = 1.)
+ * the same scaleCol; the per-row FP8 mode takes d bytes and scaleCol = 1;
+ * "aclnnKvCompressEpilog", 约束说明, quantMode=2: concatCol = 64 + (d-64)/2 +
+ * ((d-64)/G) * 2, padded to 32 bytes, e.g. d=576, G=32 gives 352.)
  *   concat_col    bytes of data per row (mode 4: ckv elements per row)
  *   kv_cache_col  bytes written per row, the minimum headDim (mode 4: d-64)
  *   scale_col     scale entries per row (modes 3, 5, 6: the minimum
- *                 cache_aux headDim; mode 4: 64, the k-cache elements per row)
+ *                 cache_aux headDim; mode 4: 64, the k-cache elements per row;
+ *                 mode 7: the bf16 scales in the row)
  * Any out-pointer may be NULL.  Errors: KVEPI_ERR_UNSUPPORTED for an unknown
  * mode or mode 2, KVEPI_ERR_SHAPE for d outside the mode's range
- * (modes 0/1/4: d % 64 == 0 and 64 < d <= 8192; modes 3/5/6: d % 32 == 0
+ * (modes 0/1/4/7: d % 64 == 0 and 64 < d <= 8192; modes 3/5/6: d % 32 == 0
  * and 32 <= d <= 8192), KVEPI_ERR_PARAM for a group size other than 64
- * (modes 0/1), 32 (modes 3/5) or 0 or d (mode 6). */
+ * (modes 0/1), 32 (modes 3/5), 0 or d (mode 6) or 16/32/64 (mode 7). */
 KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t group_size,
                              int64_t *concat_col, int64_t *kv_cache_col,
                              int64_t *scale_col);
@@ -156,7 +172,8 @@ KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t gr
  *  cos, sin      DEVICE, bf16 [num_tokens, 64] contiguous, 16-byte aligned,
  *                both or neither; NULL for no RoPE (the rope columns are then
  *                copied unchanged).  Required in mode 4, rejected in modes
- *                3, 5, 6.
+ *                3, 5, 6 (KVEPI_ERR_UNSUPPORTED) and 7 (KVEPI_ERR_PARAM: the
+ *                rope bytes are not written).
  *  slot_mapping  DEVICE, int32 [num_tokens], 4-byte aligned.  -1 skips the
  *                token; any value outside [0, num_slots) is skipped too.
  *                Valid values must be distinct; with duplicates the result of
@@ -169,8 +186,8 @@ KVEPI_API kvepi_status kvepi_row_bytes(int32_t quant_mode, int64_t d, int32_t gr
  *                headDim >= 1) and mode 4 (k cache, bf16, headDim >= 64);
  *                same block_num and block_size as cache.
  *  quant_mode    KVEPI_MODE_*.
- *  group_size    64 (modes 0, 1), 32 (modes 3, 5), 0 or d (mode 6),
- *                ignored in mode 4.
+ *  group_size    64 (modes 0, 1), 32 (modes 3, 5), 0 or d (mode 6), 16, 32
+ *                or 64 (mode 7), ignored in mode 4.
  *  eps           RMSNorm epsilon, finite and >= 0 (used only with gamma).
  *  workspace_bytes  HOST out-parameter.
  * num_tokens == 0 is valid and makes kvepi_run a no-op. */

@@ -28,6 +28,7 @@ KVEPI_MODE_MXFP4 = 3
 KVEPI_MODE_BF16_SPLIT = 4
 KVEPI_MODE_MXFP8 = 5
 KVEPI_MODE_FP8_ROW = 6
+KVEPI_MODE_FP4_NOPE = 7
 
 KVEPI_X_BF16 = 0
 KVEPI_X_FP16 = 1

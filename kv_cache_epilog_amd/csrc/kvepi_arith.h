@@ -65,17 +65,29 @@ __device__ __forceinline__ uint32_t pack_bf16_rn(float a, float b) {
 }
 
 // max(|a|, |b|, |c|) in one instruction (the compiler's fmaxf chain adds
-// canonicalisations for inputs it cannot prove to be canonical).
+// canonicalisations for inputs it cannot prove to be canonical).  With the
+// IEEE mode of compute kernels, v_max3_f32 returns the larger number when an
+// operand is a quiet NaN.
 __device__ __forceinline__ float max3_abs(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// max(|a|, |b|, 0)
+__device__ __forceinline__ float max2_abs0(float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// The largest magnitude of eight values, NaN values left out (0 when all
+// eight are NaN): the last step takes 0 as its third operand.  (A NaN only
+// arises from 0 / 0 in RMSNorm, a zero row with eps = 0, where every value of
+// the row is NaN and the scale becomes 0.)
 __device__ __forceinline__ float amax8(const float (&v)[8]) {
   float m = max3_abs(v[0], v[1], v[2]);
   m = max3_abs(m, v[3], v[4]);
   m = max3_abs(m, v[5], v[6]);
-  return max3_abs(m, v[7], v[7]);
+  return max2_abs0(m, v[7]);
 }
 
 // E4M3FN code of q: round to nearest even, |q| > 448 saturates to 448,
@@ -99,8 +111,9 @@ __device__ __forceinline__ uint32_t enc_e4m3_sw(float q) {
 }
 
 // E2M1 code (4 bits) of q: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the
-// even code, saturating at 6.
+// even code, saturating at 6; a NaN gives 0x7 (E2M1 has no NaN).
 __device__ __forceinline__ uint32_t enc_e2m1_sw(float q) {
+  if (q != q) return 0x7u;
   const float a = __builtin_fabsf(q);
   const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
                      (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +

@@ -118,7 +118,6 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
                             int32_t group_size, float eps, const kvepi_options *opt,
                             kvepi_plan *p) {
   if (quant_mode == KVEPI_MODE_HIF8_FP4) return KVEPI_ERR_UNSUPPORTED;
-  if (quant_mode == KVEPI_MODE_FP4_NOPE) return KVEPI_ERR_UNSUPPORTED;  // no kernel yet
   const kvepi_options o = opt != nullptr ? *opt : kvepi_options{0, 0, 0, 0, 0};
   if (o.x_dtype != KVEPI_X_BF16 && o.x_dtype != KVEPI_X_FP16) return KVEPI_ERR_PARAM;
   if (o.index_mode < KVEPI_INDEX_SLOT || o.index_mode > KVEPI_INDEX_BATCH_START)
@@ -163,6 +162,8 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
     return KVEPI_ERR_SHAPE;
   if (quant_mode == KVEPI_MODE_BF16_SPLIT && (!has_norm || !has_rope))
     return KVEPI_ERR_PARAM;
+  // the FP4 nope mode leaves the rope bytes of its rows untouched: no RoPE
+  if (quant_mode == KVEPI_MODE_FP4_NOPE && has_rope) return KVEPI_ERR_PARAM;
   if (has_norm && (!isfinite(eps) || eps < 0.0f)) return KVEPI_ERR_PARAM;
   if (has_norm && !aligned(gamma, 16)) return KVEPI_ERR_LAYOUT;
   if (has_rope && (!aligned(cos, 16) || !aligned(sin, 16)))
@@ -217,6 +218,7 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
     q.concat_col = cc;
     q.kv_cache_col = kc;
     q.scale_col = sc;
+    q.group_size = group_size;
     q.eps = eps;
     *p = q;
   }

@@ -88,6 +88,9 @@ struct KArgs {
   uint64_t sq_magic;   // row / seq_len == (row * sq_magic) >> sq_shift
   int32_t sq_shift;
   int32_t n_chunk_b;   // index entries per batch in the block-index mode
+  int32_t glog;        // M_FP4_NOPE: log2(group size / 8), chunks per group 2^glog
+  int32_t img_bytes;   // FAST == 2: bytes of a row image staged in LDS
+  int32_t img_off;     // FAST == 2: where the image goes in the cache row
   int32_t rope_half;   // M_SPLIT_G: rope_dim / 2 output pairs per row
   int32_t rope_pitch;  // M_SPLIT_G: bytes per cos / sin row (2 * rope_dim)
   int32_t nwaves;      // waves in the grid
@@ -288,13 +291,17 @@ __device__ __forceinline__ void unpack8x(const uint4 w, float (&v)[8]) {
 constexpr int kSinkHalf = 16384;
 __device__ __attribute__((aligned(256))) uint8_t g_sink[2 * kSinkHalf + 64 * 16];
 enum { M_FP8_BF16 = 0, M_FP8_E8M0 = 1, M_MXFP4 = 3, M_SPLIT = 4, M_MXFP8 = 5, M_FP8_ROW = 6,
-       M_SPLIT_G = 7 /* the bf16 split with a rope segment of another length */ };
+       M_FP4_NOPE = 7 /* quantMode 2's nope segment: FP4 codes, bf16 scales */,
+       M_SPLIT_G = 8 /* the bf16 split with a rope segment of another length */ };
 // the indexer modes quantise the whole row (no rope segment)
 constexpr bool whole_row(int m) { return m == M_MXFP4 || m == M_MXFP8 || m == M_FP8_ROW; }
 // modes writing a second cache (scales or the k rows)
 constexpr bool has_aux(int m) { return m != M_FP8_BF16 && m != M_FP8_E8M0; }
-// the rope segment: the last 64 columns, or (M_SPLIT_G) rope_dim columns
-constexpr bool fixed_rope(int m) { return !whole_row(m) && m != M_SPLIT_G; }
+// the rope segment: the last 64 columns, or (M_SPLIT_G) rope_dim columns;
+// M_FP4_NOPE leaves the rope bytes of its rows alone and does not read them
+constexpr bool fixed_rope(int m) { return !whole_row(m) && m != M_SPLIT_G && m != M_FP4_NOPE; }
+// modes whose rows are assembled in LDS when the layout allows (FAST == 2)
+constexpr bool staged_mode(int m) { return m == M_FP8_BF16 || m == M_FP4_NOPE; }
 constexpr bool gen_rope(int m) { return m == M_SPLIT_G; }
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
@@ -475,6 +482,61 @@ __device__ __forceinline__ uint32_t codes_fp8_bf16scale(const float (&v)[8], flo
   return __float_as_uint(su) >> 16;
 }
 
+// m / 6 correctly rounded for a bf16 m in [2^-90, 2^100]: fma(m, H, m*Lo)
+// with H + Lo a double-length 1/6 (tests/fastdiv_check.c compares it with the
+// IEEE quotient for every such m).
+__device__ __forceinline__ float div6_fast(float m) {
+  constexpr float H6 = 1.0f / 6.0f;
+  constexpr float L6 = (float)(1.0 / 6.0 - (double)H6);
+  return __builtin_fmaf(m, H6, m * L6);
+}
+
+// Max of non-negative floats over aligned groups of 2^k lanes, k in 1..3
+// (wave-uniform); pairings as in grp_max.
+__device__ __forceinline__ float grp_max_k(float f, int k) {
+  uint32_t v = __float_as_uint(f);
+  v = max(v, dpp_u<0xB1>(v));
+  if (k >= 2) v = max(v, dpp_u<0x4E>(v));
+  if (k >= 3) v = max(v, dpp_u<0x141>(v));
+  return __uint_as_float(v);
+}
+
+// FP4 nope codes of one chunk of 8 values (v, group maximum m): the scale is
+// amax / 6 (IEEE), stored as bf16, and the codes are E2M1(v / s) with the
+// stored s; returns the bf16 scale bits and the 8 codes as one word (value 2i
+// in the low nibble of byte i).
+// fast (m in [2^-90, 2^100]): m / 6 from a double-length 1/6, v / s from a
+// double-length reciprocal rounded downwards (both exactly the IEEE quotient
+// for bf16 operands wherever a code can be nonzero, as in mode 0), codes from
+// v_cvt_scalef32_pk_fp4_f32 with scale 1, which rounds every fp32 quotient up
+// to 6.0625 to nearest even and saturates at 6 (tests/hw_check.hip); the
+// quotients stay below 6 / (1 - 2^-8).  Otherwise the group divides exactly
+// and encodes in software (a zero group: scale 0 and codes 0).
+__device__ __forceinline__ uint32_t codes_fp4_bf16scale(const float (&v)[8], float m, bool fast,
+                                                        uint32_t &w) {
+  const float su = round_bf16(fast ? div6_fast(m) : m / 6.0f);
+  if (fast) {
+    float rs = rcp_rn(su);
+    if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
+    const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
+    float q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = __builtin_fmaf(v[t], rs, v[t] * rl);
+    uint32_t x = 0;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[0], q[1], 1.0f, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[2], q[3], 1.0f, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[4], q[5], 1.0f, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[6], q[7], 1.0f, 3);
+    w = x;
+  } else {
+    uint32_t x = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x |= (su > 0.0f ? enc_e2m1_sw(v[t] / su) : 0u) << (4 * t);
+    w = x;
+  }
+  return __float_as_uint(su) >> 16;
+}
+
 template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST, bool XF16>
 __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
                                             const RowBuf<MODE, ROPE, L, C> &b,
@@ -626,6 +688,19 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       const float s0 = lo_f(b.gs[k]), s1 = hi_f(b.gs[k]);
       o.ry[k] = pack_bf16(xa * c0 + -xb * s0, xb * c1 + xa * s1);
     }
+  } else if constexpr (MODE == M_FP4_NOPE) {
+    // "aclnnKvCompressEpilog" quantMode 2, nope segment: groups of 16, 32 or
+    // 64 values (2, 4 or 8 lanes), scale amax / 6 as bf16, E2M1 codes
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float v[8];
+      unpack8(yw[j], v);
+      const float m = grp_max_k(amax8(v), a.glog);
+      const bool fast = m >= 0x1p-90f && m <= 0x1p+100f;
+      uint32_t w;
+      o.sb[j] = codes_fp4_bf16scale(v, m, fast, w);
+      o.w[j] = make_uint4(w, 0u, 0u, 0u);
+    }
   } else if constexpr (MODE == M_MXFP4) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
@@ -764,46 +839,81 @@ constexpr int max_row_bytes(int L, int C) {
 }
 
 // FAST == 2: writes the computed row into the wave's staging area (its own
-// image at stage + sub * kvCacheCol): codes, rope, scales, zero pad.
+// image at stage + sub * img_bytes).  Mode 0: codes, rope and scales; the FP4
+// nope mode: codes and scales (its image starts after the row's 64 rope
+// bytes).  The zero pad after the scales was written once when the wave
+// started (every row writes the same fields, so the pad bytes are never
+// overwritten).
 template <int MODE, int L, int C>
 __device__ __forceinline__ void stage_write(const KArgs &a, int li, int sub,
                                             const RowOut<MODE, L, C> &o, uint8_t *stage) {
-  static_assert(MODE == M_FP8_BF16 && L >= 32, "staged rows: mode 0");
-  constexpr int TPL = RopeShape<L>::TPL;
-  const int kc = a.kv_cache_col;
-  uint8_t *img = stage + sub * kc;
+  static_assert(staged_mode(MODE) && L >= 32, "staged rows: mode 0 and the FP4 nope mode");
+  uint8_t *img = stage + sub * a.img_bytes;
+  if constexpr (MODE == M_FP4_NOPE) {
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = li + L * j;
-    *reinterpret_cast<uint2 *>(img + 8 * c) = make_uint2(o.w[j].x, o.w[j].y);
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      *reinterpret_cast<uint32_t *>(img + 4 * c) = o.w[j].x;
+      *reinterpret_cast<uint16_t *>(img + a.nseg / 2 + 2 * (c >> a.glog)) = (uint16_t)o.sb[j];
+    }
+  } else {
+    constexpr int TPL = RopeShape<L>::TPL;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      *reinterpret_cast<uint2 *>(img + 8 * c) = make_uint2(o.w[j].x, o.w[j].y);
+    }
+    const int tail = a.nseg + 128;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = li + L * j;
+      *reinterpret_cast<uint16_t *>(img + tail + 2 * (c >> 3)) = (uint16_t)o.sb[j];
+    }
+#pragma unroll
+    for (int k = 0; k < TPL; ++k)
+      *reinterpret_cast<uint32_t *>(img + a.nseg + 4 * ((li + L * k) & 31)) = o.ry[k];
   }
-  // zero the scale and pad area, then the scales over it
-  const int tail = a.nseg + 128;
-  if (li < (kc - tail) / 16)
-    *reinterpret_cast<uint4 *>(img + tail + 16 * li) = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = li + L * j;
-    *reinterpret_cast<uint16_t *>(img + tail + 2 * (c >> 3)) = (uint16_t)o.sb[j];
-  }
-#pragma unroll
-  for (int k = 0; k < TPL; ++k)
-    *reinterpret_cast<uint32_t *>(img + a.nseg + 4 * ((li + L * k) & 31)) = o.ry[k];
+}
+
+// Orders a wave's LDS accesses across its lanes: the writes (reads) of one
+// lane before the reads (writes) of another that follow in program order.
+__device__ __forceinline__ void lds_handover() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // FAST == 2: stores the staged rows of a wave-iteration, one instruction per
-// row, 16 bytes per lane; dst[r] is the destination of row r (wave-uniform),
-// off the lane's piece offset.  (Destinations are pointers derived from the
-// cache or the sink, never integers, so that the stores stay global ones.)
+// row, 16 bytes per lane; dst[r] is where row r's image goes (wave-uniform),
+// off the lane's piece offset, img the bytes per image.  (Destinations are
+// pointers derived from the cache or the sink, never integers, so that the
+// stores stay global ones.)
 template <int R>
-__device__ __forceinline__ void stage_store(const uint8_t *stage, int kc, uint32_t off,
+__device__ __forceinline__ void stage_store(const uint8_t *stage, int img, uint32_t off,
                                             uint8_t *const (&dst)[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kc + off);
+    const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * img + off);
     // a global-memory pointer (an integer cast would otherwise give a flat
     // store, which also counts against the LDS counter)
     *reinterpret_cast<uint4 *>(dst[r] + off) = v;
+  }
+}
+
+// Zero padding of a row from concatCol to kvCacheCol (0..31 bytes): one store
+// per lane, duplicates allowed (lanes with nothing to write use the sink).
+template <int L>
+__device__ __forceinline__ void store_pad(const KArgs &a, int li, uint8_t *lsink, uint8_t *row) {
+  const int npad = a.kv_cache_col - a.concat_col;
+  if (a.pad16 == 1) {
+    *reinterpret_cast<uint4 *>(row + a.concat_col) = make_uint4(0, 0, 0, 0);
+  } else {
+    constexpr int PADIT = (31 + L - 1) / L;  // enough stores for 31 bytes
+#pragma unroll
+    for (int k = 0; k < PADIT; ++k) {
+      const int b = li + L * k;
+      st_u8(npad > 0 ? row + a.concat_col + (b < npad ? b : b % max(npad, 1)) : lsink + 12, 0u);
+    }
   }
 }
 
@@ -852,6 +962,18 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
       st_u32(in ? o.p0 + 4 * c : lsink, o.w[j].x, c_al);
       st_u8(in ? o.p1 + (c >> 2) : lsink + 8, o.sb[j]);  // every lane of the group
     }
+  } else if constexpr (MODE == M_FP4_NOPE) {
+    // after the 64 rope bytes: the codes (4 bytes per chunk), the group
+    // scales (every lane of a group writes its scale) and the zero pad
+    uint8_t *r0 = o.p0 + 64;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = chunk_of<L>(li, j);
+      const bool in = FAST || c < a.nchunk;
+      st_u32(in ? r0 + 4 * c : lsink, o.w[j].x, c_al);
+      st_u16(in ? r0 + a.nseg / 2 + 2 * (c >> a.glog) : lsink + 8, o.sb[j], c_al);
+    }
+    store_pad<L>(a, li, lsink, o.p0);
   } else if constexpr (MODE == M_MXFP8 || MODE == M_FP8_ROW) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
@@ -878,21 +1000,7 @@ __device__ __forceinline__ void store_row(const KArgs &a, int li, int lane,
 #pragma unroll
     for (int k = 0; k < TPL; ++k)
       st_u32(o.p0 + a.nseg + 4 * ((li + L * k) & 31), o.ry[k], c_al);
-    if constexpr (MODE == M_FP8_BF16) {
-      // zero padding (0..31 bytes): one store per lane, duplicates allowed
-      const int npad = a.kv_cache_col - a.concat_col;
-      if (a.pad16 == 1) {
-        *reinterpret_cast<uint4 *>(o.p0 + a.concat_col) = make_uint4(0, 0, 0, 0);
-      } else {
-        constexpr int PADIT = (31 + L - 1) / L;  // enough stores for 31 bytes
-#pragma unroll
-        for (int k = 0; k < PADIT; ++k) {
-          const int b = li + L * k;
-          st_u8(npad > 0 ? o.p0 + a.concat_col + (b < npad ? b : b % max(npad, 1)) : lsink + 12,
-                0u);
-        }
-      }
-    }
+    if constexpr (MODE == M_FP8_BF16) store_pad<L>(a, li, lsink, o.p0);
   }
 }
 
@@ -913,7 +1021,8 @@ template <int MODE, bool NORM, bool ROPE, int L, int C, int FAST, bool XF16 = fa
 __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   static_assert(!XF16 || whole_row(MODE), "fp16 rows: indexer modes");
   constexpr int R = 64 / L;  // rows per wave-iteration
-  static_assert(FAST != 2 || (R <= 2 && max_row_bytes(L, C) <= 1024), "staged rows");
+  static_assert(FAST != 2 || (staged_mode(MODE) && R <= 2 && max_row_bytes(L, C) <= 1024),
+                "staged rows");
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
   const int sub = lane / L;
@@ -931,8 +1040,14 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   }
   // per-wave staging area for FAST == 2, after gamma
   uint8_t *stage = reinterpret_cast<uint8_t *>(g_lds) + (NORM ? L * C * 32 : 0) +
-                   (threadIdx.x >> 6) * R * a.kv_cache_col;
-  const uint32_t piece = FAST == 2 ? 16u * (uint32_t)(lane % (a.kv_cache_col / 16)) : 0u;
+                   (threadIdx.x >> 6) * R * a.img_bytes;
+  const uint32_t piece = FAST == 2 ? 16u * (uint32_t)(lane % (a.img_bytes / 16)) : 0u;
+  if constexpr (FAST == 2) {
+    // the wave's R row images start as zeros: their pad stays zero
+    for (int b = 16 * lane; b < R * a.img_bytes; b += 64 * 16)
+      *reinterpret_cast<uint4 *>(stage + b) = make_uint4(0, 0, 0, 0);
+    lds_handover();
+  }
   int blk = blockIdx.x;
   if (a.xcd_blocks > 0) blk = (blk & 7) * a.xcd_blocks + (blk >> 3);
   const int wave = __builtin_amdgcn_readfirstlane(blk * 4 + (int)(threadIdx.x >> 6));
@@ -1039,6 +1154,9 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       compute_row<MODE, NORM, ROPE, L, C, FAST, XF16>(a, li, sub, b, g_lds, out);
       if constexpr (FAST == 2) stage_write<MODE, L, C>(a, li, sub, out, stage);
     }
+    // the staged bytes one lane writes are stored by another lane: order the
+    // LDS writes before the reads in stage_store (wave scope)
+    if constexpr (FAST == 2) lds_handover();
   };
   // destination of row r (the sink when it is not live)
   // (pointers, not integers, so that the compiler keeps them global)
@@ -1053,8 +1171,10 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
     if constexpr (FAST == 2) {
       uint8_t *d[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) d[r] = dst(t, r);
-      stage_store<R>(stage, a.kv_cache_col, piece, d);
+      for (int r = 0; r < R; ++r) d[r] = dst(t, r) + a.img_off;
+      stage_store<R>(stage, a.img_bytes, piece, d);
+      // ... and those reads before the next row's writes to the same image
+      lds_handover();
     } else {
       uint8_t *d, *ad = nullptr;
       if constexpr (R <= 2) {
@@ -1172,7 +1292,7 @@ kfn_t pick_indexer(int L, int C, int fast, bool xf16) {
 
 template <int MODE, bool NORM, bool ROPE>
 kfn_t pick_layout(int L, int C, int fast) {
-  if constexpr (MODE == M_FP8_BF16)
+  if constexpr (staged_mode(MODE))
     if (fast == 2)
       return C == 1 ? epilog_kernel<MODE, NORM, ROPE, 32, 1, 2>
                     : epilog_kernel<MODE, NORM, ROPE, 32, 2, 2>;
@@ -1200,6 +1320,9 @@ kfn_t pick(int mode, bool norm, bool rope, bool xf16, int L, int C, int fast) {
       return pick_indexer<M_MXFP8>(L, C, fast, xf16);
     case M_FP8_ROW:
       return pick_indexer<M_FP8_ROW>(L, C, fast, xf16);
+    case M_FP4_NOPE:
+      return norm ? pick_layout<M_FP4_NOPE, true, false>(L, C, fast)
+                  : pick_layout<M_FP4_NOPE, false, false>(L, C, fast);
     case M_SPLIT_G:
       return pick_layout<M_SPLIT_G, true, true>(L, C, fast);
     default:
@@ -1297,6 +1420,13 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   a.c_align = p.c_align;
   a.a_align = p.aux != nullptr ? p.a_align : 16;
   a.eps = p.eps;
+  // FP4 nope mode: chunks of 8 values per scale group (2, 4 or 8)
+  a.glog = p.mode == KVEPI_MODE_FP4_NOPE ? (p.group_size == 16 ? 1 : p.group_size == 32 ? 2 : 3)
+                                         : 0;
+  // staged rows: mode 0 stages the whole row, the FP4 nope mode the part
+  // after the 64 rope bytes
+  a.img_off = p.mode == KVEPI_MODE_FP4_NOPE ? 64 : 0;
+  a.img_bytes = (int32_t)(p.kv_cache_col - a.img_off);
   a.rope_half = (int32_t)(p.rope_dim / 2);
   a.rope_pitch = (int32_t)(2 * p.rope_dim);
   a.nseg_f = (float)p.nope;
@@ -1318,12 +1448,14 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   // assemble their rows in LDS
   const bool aligned = L * C == a.nchunk && a.c_align >= 16 &&
                        (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
-  const int fast = !aligned ? 0 : (p.mode == KVEPI_MODE_FP8_BF16SCALE && L == 32) ? 2 : 1;
+  const bool stages =
+      p.mode == KVEPI_MODE_FP8_BF16SCALE || p.mode == KVEPI_MODE_FP4_NOPE;
+  const int fast = !aligned ? 0 : (stages && L == 32) ? 2 : 1;
   // the bf16 split with a rope segment of another length than 64
   const int kmode = p.mode == KVEPI_MODE_BF16_SPLIT && p.rope_dim != 64 ? (int)M_SPLIT_G : p.mode;
   kfn_t fn = pick(kmode, p.norm, p.rope, p.x_fp16, L, C, fast);
   size_t lds = p.norm ? (size_t)L * C * 32 : 0;  // gamma as fp32, 32 KB at most
-  if (fast == 2) lds += (size_t)4 * (64 / L) * p.kv_cache_col;  // staging, 4 waves
+  if (fast == 2) lds += (size_t)4 * (64 / L) * a.img_bytes;  // staging, 4 waves
 
   // persistent waves: exactly as many blocks as the CUs hold at once
   const int cus = device_cus();

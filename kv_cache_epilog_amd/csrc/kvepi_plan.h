@@ -28,6 +28,7 @@ struct kvepi_plan {
   int32_t a_align;
   int64_t block_size, num_slots;
   int64_t concat_col, kv_cache_col, scale_col;
+  int32_t group_size;  // values per scale group
   float eps;
 };
 

@@ -172,8 +172,11 @@ uint8_t kvo_enc_e4m3(float v) {
  * saturating at 6 ("aclnnKvCompressEpilog" 计算公式 FLOAT4_E2M1(x / scale);
  * "indexer_quant_cache" 接口功能 MX-FP4).  Returns the 4-bit code. */
 uint8_t kvo_enc_e2m1(float v) {
+  /* E2M1 has no NaN: a NaN takes one canonical code, 0x7 (+6), whatever its
+   * sign bit (the sign of a NaN made by an invalid operation is
+   * processor-dependent) */
+  if (isnan(v)) return 0x7;
   uint8_t sign = signbit(v) ? 0x8 : 0x0;
-  if (isnan(v)) return (uint8_t)(sign | 0x7);
   double a = fabs((double)v);
   if (a > 6.0) return (uint8_t)(sign | 0x7);
   if (a < 1.0) {

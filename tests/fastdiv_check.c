@@ -15,7 +15,7 @@
  *     it v*rl can underflow); below it both must stay under 2^-10, where
  *     every E4M3 code is +-0, so the codes still agree.  Checked for every
  *     pair of bf16 significands and every exponent difference in [-140, 12],
- *     at three absolute scale exponents of s (2^-80, 2^0, 2^92).  With
+ *     at five absolute scale exponents of s (2^-98, 2^-80, 2^0, 2^92, 2^97).  With
  *     rl >= 0, v*rl has the sign of v, so q keeps the sign of a zero v; the
  *     check covers +-0 too.
  *  3. m / 448 for bf16 m, from the constants H = RN(1/448), Lo = RN(1/448 - H):
@@ -23,6 +23,9 @@
  *     must equal the IEEE quotient for every bf16 m in [2^-71, 2^100].
  *  4. the same for every positive finite fp16 m (fp16 rows of the indexer's
  *     fp8 mode; all of them lie in [2^-24, 65504], inside that range).
+ *  5. m / 6 for bf16 m (the FP4 nope mode's scale), from H6 = RN(1/6),
+ *     L6 = RN(1/6 - H6): q = fma(m, H6, m*L6) must equal the IEEE quotient
+ *     for every bf16 m in [2^-90, 2^100].
  * Prints the number of mismatches of each part and exits non-zero if any.
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math fastdiv_check.c -lm
  */
@@ -49,8 +52,8 @@ int main(void) {
     }
   }
   /* 2: bf16 / bf16 */
-  const int sexp[3] = {-80, 0, 92};
-  for (int k = 0; k < 3; ++k) {
+  const int sexp[5] = {-98, -80, 0, 92, 97};
+  for (int k = 0; k < 5; ++k) {
     for (uint32_t ms = 0; ms < 128; ++ms) {
       const float s = ldexpf(f_of(0x3F800000u | (ms << 16)), sexp[k]);
       float rs = 1.0f / s;
@@ -96,9 +99,22 @@ int main(void) {
     ++n4;
     if (q != m / 448.0f) ++bad4;
   }
+  /* 5: bf16 m / 6 */
+  long long bad5 = 0, n5 = 0;
+  const float H6 = 1.0f / 6.0f;
+  const float L6 = (float)(1.0 / 6.0 - (double)H6);
+  for (int em = -90; em < 100; ++em) {
+    for (uint32_t mm = 0; mm < 128; ++mm) {
+      const float m = ldexpf(f_of(0x3F800000u | (mm << 16)), em);
+      const float q = fmaf(m, H6, m * L6);
+      ++n5;
+      if (q != m / 6.0f) ++bad5;
+    }
+  }
   printf("markstein x/r: %lld of %lld differ\n", bad1, n1);
   printf("bf16/bf16 double reciprocal: %lld of %lld differ\n", bad2, n2);
   printf("m/448 double constant: %lld of %lld differ\n", bad3, n3);
   printf("fp16 m/448 double constant: %lld of %lld differ\n", bad4, n4);
-  return (bad1 || bad2 || bad3 || bad4) ? 1 : 0;
+  printf("m/6 double constant: %lld of %lld differ\n", bad5, n5);
+  return (bad1 || bad2 || bad3 || bad4 || bad5) ? 1 : 0;
 }

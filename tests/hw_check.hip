@@ -17,6 +17,11 @@
 //   rn16    fp32 -> fp16 ((_Float16), v_cvt_f16_f32) and fp32 -> bf16
 //           (pack_bf16_rn, v_cvt_pk_bf16_f32) == round to nearest even done
 //           on the bits, for every non-NaN fp32 value
+//   fp4q    v_cvt_scalef32_pk_fp4_f32(q, 1.0) == the nearest E2M1 value found
+//           by a search over the eight magnitudes (ties to the even code,
+//           saturating at 6), every fp32 |q| <= 6.0625: the FP4 nope mode
+//           converts quotients by a scale rounded to bf16, which exceed 6 by
+//           at most a factor 1 / (1 - 2^-8) < 1.004
 //   div16   div_fast(a, b, rcp_rn(b)) == a / b for every fp16 significand a
 //           against every fp32 significand b (quotient in (1/2, 2); exponents
 //           are a pure scaling while the quotient stays normal)
@@ -125,6 +130,33 @@ __global__ void k_div16(uint32_t n, unsigned *bad) {
   if (nb) atomicAdd(bad, nb);
 }
 
+// E2M1 code of q by search: the nearest of the eight magnitudes, the even
+// code on a tie, 6 above 6; the sign bit from q
+__device__ uint32_t e2m1_by_search(float q) {
+  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const float a = __builtin_fabsf(q);
+  uint32_t best = 7;
+  if (a <= 6.0f) {
+    float bd = __builtin_inff();
+    for (uint32_t c = 0; c < 8; ++c) {
+      const float dist = __builtin_fabsf(a - mag[c]);  // exact: both within [0, 6]
+      if (dist < bd || (dist == bd && (c & 1u) == 0u)) {
+        bd = dist;
+        best = c;
+      }
+    }
+  }
+  return best | ((__float_as_uint(q) >> 28) & 0x8u);
+}
+
+__global__ void k_fp4q(uint32_t base, uint32_t n, unsigned *bad) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float q = __uint_as_float(base + i);
+  const uint32_t got = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, -q, 1.0f, 0) & 0xFFu;
+  if (got != (e2m1_by_search(q) | (e2m1_by_search(-q) << 4))) atomicAdd(bad, 1u);
+}
+
 // index = (E + 100) * 65536 + bf16 (or fp16) bits
 __global__ void k_scaled(uint32_t n, int fp4, int f16, unsigned *bad, unsigned *count) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -176,10 +208,11 @@ int main() {
   for (uint64_t b = 0; b < (1ull << 32); b += (1ull << 28))
     hipLaunchKernelGGL(k_rn16, dim3((1u << 28) / 256), dim3(256), 0, 0, (uint32_t)b, 1u << 28,
                        d + 13);
+  launch_range(k_fp4q, 0x00000000u, 0x40C20000u, d + 14);     // [0, 6.0625]
   const uint32_t n_div = 1u << 23;
   hipLaunchKernelGGL(k_div16, dim3(n_div / 256), dim3(256), 0, 0, n_div, d + 12);
   const hipError_t e = hipDeviceSynchronize();
-  unsigned h[14] = {0};
+  unsigned h[15] = {0};
   (void)hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
   (void)hipFree(d);
   if (e != hipSuccess) {
@@ -196,5 +229,7 @@ int main() {
   printf("fp4s16: %u mismatches of %u\n", h[10], h[11]);
   printf("div16: %u mismatches of %llu\n", h[12], 1024ull << 23);
   printf("rn16: %u mismatches of %llu\n", h[13], 1ull << 32);
-  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12] | h[13]) ? 1 : 0;
+  printf("fp4q: %u mismatches of %u\n", h[14], 0x40C20000u + 1u);
+  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12] | h[13] | h[14]) ? 1
+                                                                                          : 0;
 }

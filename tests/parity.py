@@ -110,8 +110,11 @@ def _code_positions(w: kvgen.Workload):
     """Byte offsets of quantised codes in the main cache, and their count."""
     ts = token_slots(w)
     hit = ts[ts >= 0].astype(np.int64)
+    start = 0
     if w.mode in (kvgen.MODE_FP8_BF16SCALE, kvgen.MODE_FP8_E8M0):
         ncode = w.d - 64
+    elif w.mode == kvgen.MODE_FP4_NOPE:
+        start, ncode = 64, (w.d - 64) // 2  # code bytes after the 64 rope bytes
     elif w.mode == kvgen.MODE_MXFP4:
         ncode = w.d // 2
     elif w.mode in (kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
@@ -119,7 +122,7 @@ def _code_positions(w: kvgen.Workload):
     else:
         return np.zeros(0, np.int64), 0
     blk, pos = np.divmod(hit, w.cache.block_size)
-    base = blk * w.cache.block_stride + pos * w.cache.head_dim
+    base = blk * w.cache.block_stride + pos * w.cache.head_dim + start
     return (base[:, None] + np.arange(ncode)[None, :]).reshape(-1), hit.size * ncode
 
 
@@ -146,7 +149,7 @@ def compare(w: kvgen.Workload, got, want, agot=None, awant=None, label=""):
         assert bad.size == 0, (
             f"{label}: {bad.size} non-code bytes differ, first at {bad[:8].tolist()}: "
             f"got {got[bad[:8]].tolist()} want {want[bad[:8]].tolist()}")
-        nib = w.mode == kvgen.MODE_MXFP4
+        nib = w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_FP4_NOPE)
         steps = [_one_step(int(got[i]), int(want[i]), nib) for i in diff]
         assert all(steps), f"{label}: a code differs by more than one step"
         n_step = diff.size

@@ -40,7 +40,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.kvepi_version() == 120
+    assert B.kvepi_version() == 130
     for code, name in B.STATUS_NAMES.items():
         assert B.kvepi_status_str(code).startswith(name)
     assert "UNKNOWN" in B.kvepi_status_str(99)
@@ -120,11 +120,22 @@ def test_valid_call_reports_zero_workspace():
     k = _cache(data=0x70000, hd=64)
     assert call(1, d=576, mode=4, cache=ckv, aux=k, gamma=P16C, cos=P16D,
                 sin=P16D + 0x1000) == (0, 0)
+    # the FP4 nope mode, with and without RMSNorm, any of its group sizes
+    for g, hd in ((16, 384), (32, 352), (64, 352)):
+        assert call(1, d=576, mode=7, group=g, cache=_cache(hd=hd)) == (0, 0)
+    assert call(1, d=576, mode=7, group=32, cache=_cache(hd=352), gamma=P16C) == (0, 0)
 
 
 BAD = [
     # (description, kwargs, expected status)
     ("mode 2 (HiFloat8)", dict(mode=2), 5),
+    ("fp4 nope with RoPE", dict(mode=7, d=576, group=32, cache=_cache(hd=352), cos=P16C,
+                                sin=P16D), 4),
+    ("fp4 nope with an aux cache", dict(mode=7, d=576, group=32, cache=_cache(hd=352),
+                                        aux=_cache(hd=4)), 4),
+    ("fp4 nope group 8", dict(mode=7, d=576, group=8, cache=_cache(hd=352)), 4),
+    ("fp4 nope headDim below kvCacheCol", dict(mode=7, d=576, group=16, cache=_cache(hd=383)),
+     2),
     ("unknown mode", dict(mode=9), 5),
     ("d not a multiple of 64", dict(d=200), 2),
     ("d too large", dict(d=8256), 2),

@@ -194,10 +194,9 @@ def test_special_values(mode):
     if mode in (0, 1):
         w0 = _small(mode, T, d, seed=19, skip=0.0, norm=True, rope=False, x=xb, eps=0.0)
         # with eps = 0 a row whose squares all underflow has rms = 0: nonzero
-        # values become +-inf (kept), zeros become 0/0 = NaN, which is left
-        # unspecified -- such rows (0, 1, 3, 6) are replaced
-        for r in (0, 1, 3, 6):
-            w0.x[r] = kvgen.to_bf16(np.ones(d))
+        # values become +-inf, zeros 0/0 = NaN.  NaN values are left out of a
+        # group's maximum, so the all-zero rows (0, 1, 6) get scale 0 and
+        # codes 0, and the subnormal row (3) an infinite scale with NaN codes
         check(w0)
 
 
