@@ -44,35 +44,35 @@ def algorithmic_bytes(w: kvgen.Workload, dense: bool = False) -> int:
     x row (plus its cos and sin rows with RoPE) and the bytes written; gamma
     once.  dense: the x (and cos / sin) rows of skipped tokens counted as
     read too."""
-    from kv_cache_epilog_amd import kvepi_row_bytes
     hits = w.hits
-    x_row = 2 * w.d
+    # the FP4 nope mode neither reads nor writes the rope columns
+    x_row = 2 * (w.d - 64) if w.mode == kvgen.MODE_FP4_NOPE else 2 * w.d
     rope = 2 * 2 * 64 if w.cos is not None else 0
-    if w.mode == kvgen.MODE_BF16_SPLIT:
-        written = 2 * (w.d - 64) + 2 * 64
-    elif w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
-        _, kc, sc = kvepi_row_bytes(w.mode, w.d, w.group_size)
-        written = kc + sc * w.aux.elem_bytes  # codes + the cache_scale row
-    else:
-        _, kc, _ = kvepi_row_bytes(w.mode, w.d, w.group_size)
-        written = kc
+    written = row_written_bytes(w)
     gamma = 2 * (w.d - 64) if w.gamma is not None else 0
     read_rows = w.T if dense else hits
     return 4 * w.T + read_rows * (x_row + rope) + hits * written + gamma
 
 
-def algorithmic_split(w: kvgen.Workload):
-    """(read, written) parts of algorithmic_bytes."""
-    total = algorithmic_bytes(w)
+def row_written_bytes(w: kvgen.Workload) -> int:
+    """Bytes written per hit row: kvCacheCol (plus the cache_scale row of the
+    indexer modes, or the k row of the bf16 split); the FP4 nope mode leaves
+    the 64 rope bytes of its rows alone."""
     from kv_cache_epilog_amd import kvepi_row_bytes
     if w.mode == kvgen.MODE_BF16_SPLIT:
-        written = 2 * (w.d - 64) + 2 * 64
-    elif w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
-        _, kc, sc = kvepi_row_bytes(w.mode, w.d, w.group_size)
-        written = kc + sc * w.aux.elem_bytes
-    else:
-        written = kvepi_row_bytes(w.mode, w.d, w.group_size)[1]
-    return total - w.hits * written, w.hits * written
+        return 2 * (w.d - 64) + 2 * 64
+    _, kc, sc = kvepi_row_bytes(w.mode, w.d, w.group_size)
+    if w.mode in (kvgen.MODE_MXFP4, kvgen.MODE_MXFP8, kvgen.MODE_FP8_ROW):
+        return kc + sc * w.aux.elem_bytes  # codes + the cache_scale row
+    if w.mode == kvgen.MODE_FP4_NOPE:
+        return kc - 64
+    return kc
+
+
+def algorithmic_split(w: kvgen.Workload):
+    """(read, written) parts of algorithmic_bytes."""
+    written = w.hits * row_written_bytes(w)
+    return algorithmic_bytes(w) - written, written
 
 
 def code_text(text: str) -> str:
@@ -394,13 +394,16 @@ def pattern_ceiling(w: kvgen.Workload, dev, stream, launches: int = 50):
     cache's geometry.  Returns ms per launch back to back, and the kernel's
     bytes per launch."""
     import torch
-    src_row = 2 * w.d + (256 if w.cos is not None else 0)
+    src_row = 2 * (w.d - 64) if w.mode == kvgen.MODE_FP4_NOPE else 2 * w.d
+    src_row = src_row + (256 if w.cos is not None else 0)
     src_row = (src_row + 15) // 16 * 16
     from kv_cache_epilog_amd import kvepi_row_bytes
     if w.mode == kvgen.MODE_BF16_SPLIT:
         row = 2 * (w.d - 64)
     else:
         row = kvepi_row_bytes(w.mode, w.d, w.group_size)[1]
+        if w.mode == kvgen.MODE_FP4_NOPE:
+            row -= 64  # (written at the row start here, not after the rope bytes)
     row = (row + 15) // 16 * 16
     pitch = w.cache.head_dim * w.cache.elem_bytes
     bstride = w.cache.block_stride * w.cache.elem_bytes
@@ -520,7 +523,8 @@ def main():
     ap.add_argument("--config", type=int, default=4,
                     choices=range(len(kvgen.CONFIG_NAMES)),
                     help="workload index (default 4: the d=576 fused epilog; 5 and 6: "
-                         "the MX-FP8 and per-row FP8 indexer modes)")
+                         "the MX-FP8 and per-row FP8 indexer modes; 7: quantMode 2's "
+                         "FP4 nope segment after RMSNorm)")
     ap.add_argument("--drq", choices=kvgen.DRQ_NAMES,
                     help="time the dequant -> RoPE -> int8 KV cache operator on this "
                          "workload instead of the epilog")

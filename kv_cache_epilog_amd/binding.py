@@ -143,20 +143,67 @@ def cache_desc(cache) -> kvepi_cache:
                        cache.stride(0))
 
 
+# element size of the main cache and of cache_aux per mode: uint8 everywhere
+# except the bf16 split mode (bf16 ckv and k caches) and the per-row FP8
+# mode's fp32 cache_scale
+_CACHE_ELEM = {KVEPI_MODE_BF16_SPLIT: 2}
+_AUX_ELEM = {KVEPI_MODE_BF16_SPLIT: 2, KVEPI_MODE_FP8_ROW: 4}
+
+
+def _same_device(x, **tensors):
+    """Every given tensor is on x's device, and that is not host memory (the
+    library dereferences them on the GPU only)."""
+    if x.device.type == "cpu":
+        raise ValueError("x must be a device (cuda) tensor, not a host tensor")
+    for name, t in tensors.items():
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} must be on {x.device} (got {t.device})")
+
+
+def _index_entries(index_mode: int, T: int, seq_len: int, block_size: int) -> int:
+    """Length of the int32 index array of an index mode (see kvepi_options)."""
+    if index_mode in (KVEPI_INDEX_SLOT, KVEPI_INDEX_BATCH):
+        return T
+    if seq_len < 1 or T % seq_len:
+        raise ValueError("seq_len must be >= 1 and divide the token count")
+    B = T // seq_len
+    if index_mode == KVEPI_INDEX_BLOCK:
+        return B * -(-seq_len // block_size)
+    return B  # KVEPI_INDEX_BATCH_START
+
+
 def _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin, cache_aux, eps,
-          index_mode=KVEPI_INDEX_SLOT):
+          index_mode=KVEPI_INDEX_SLOT, seq_len=0, rope_dim=0):
+    import torch
+    _same_device(x, slot_mapping=slot_mapping, cache=cache, gamma=gamma, cos=cos, sin=sin,
+                 cache_aux=cache_aux)
     xp, T, d, xs = _x_view(x)
-    # one entry per token in the SLOT and BATCH index modes (the other modes'
-    # array lengths follow from seq_len and the block size)
-    if index_mode in (KVEPI_INDEX_SLOT, KVEPI_INDEX_BATCH) and slot_mapping.numel() != T:
-        raise ValueError("slot_mapping must have one entry per token row")
-    if slot_mapping.element_size() != 4 or not slot_mapping.is_contiguous():
+    if slot_mapping.dtype != torch.int32 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be a contiguous int32 tensor")
-    for name, t in (("gamma", gamma), ("cos", cos), ("sin", sin)):
-        if t is not None and (not t.is_contiguous() or t.element_size() != 2):
-            raise ValueError(f"{name} must be a contiguous bf16 tensor")
     c = cache_desc(cache)
-    a = None if cache_aux is None else cache_desc(cache_aux)
+    need = _index_entries(index_mode, T, seq_len, c.block_size)
+    if slot_mapping.numel() != need:
+        raise ValueError(f"the index array must have {need} entries for index mode "
+                         f"{index_mode} (got {slot_mapping.numel()})")
+    dk = rope_dim or 64
+    dv = d if quant_mode in (KVEPI_MODE_MXFP4, KVEPI_MODE_MXFP8, KVEPI_MODE_FP8_ROW) else d - dk
+    for name, t, n in (("gamma", gamma, dv), ("cos", cos, T * dk), ("sin", sin, T * dk)):
+        if t is None:
+            continue
+        if not t.is_contiguous() or t.element_size() != 2:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+        if t.numel() < n:
+            raise ValueError(f"{name} must hold at least {n} values (got {t.numel()})")
+    if cache.element_size() != _CACHE_ELEM.get(quant_mode, 1):
+        raise ValueError(f"the cache of mode {quant_mode} has {_CACHE_ELEM.get(quant_mode, 1)}-byte "
+                         f"elements (got {cache.dtype})")
+    a = None
+    if cache_aux is not None:
+        if cache_aux.element_size() != _AUX_ELEM.get(quant_mode, 1):
+            raise ValueError(f"cache_aux of mode {quant_mode} has "
+                             f"{_AUX_ELEM.get(quant_mode, 1)}-byte elements "
+                             f"(got {cache_aux.dtype})")
+        a = cache_desc(cache_aux)
     return (xp, T, d, xs, _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(slot_mapping),
             ctypes.byref(c), None if a is None else ctypes.byref(a),
             int(quant_mode), int(group_size), ctypes.c_float(eps)), (c, a)
@@ -177,7 +224,7 @@ def kvepi_get_workspace(x, slot_mapping, cache, quant_mode: int, group_size: int
     """Stage one.  x may be bf16 or (indexer modes) fp16; index_mode and
     seq_len select how slot_mapping places the tokens (see kvepi_options)."""
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
-                        cache_aux, eps, index_mode)
+                        cache_aux, eps, index_mode, seq_len, rope_dim)
     opt = _options(x, index_mode, seq_len, rope_dim)
     ws = ctypes.c_uint64()
     st = lib().kvepi_get_workspace_ex(*args, ctypes.byref(opt), ctypes.byref(ws))
@@ -199,7 +246,7 @@ def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
     error (the check synchronises the stream)."""
     import torch
     args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
-                        cache_aux, eps, index_mode)
+                        cache_aux, eps, index_mode, seq_len, rope_dim)
     opt = _options(x, index_mode, seq_len, rope_dim)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
@@ -259,13 +306,45 @@ def drq_params(x, cos, sin, k_cache, v_cache, indices, *, nq: int, nkv: int, hea
                scale_k, scale_v, q_out, k_out=None, v_out=None, weight_scale=None,
                act_scale=None, bias=None, offset_k=None, offset_v=None,
                cache_mode: int = KVEPI_DRQ_PAGE, seq_len: int = 0) -> kvepi_drq_params:
-    """torch tensors -> kvepi_drq_params (pointers, sizes and dtype codes)."""
+    """torch tensors -> kvepi_drq_params (pointers, sizes and dtype codes).
+    Checks what the pointers alone cannot carry: every tensor on x's device,
+    their dtypes and element counts (ValueError otherwise)."""
+    import torch
+    _same_device(x, cos=cos, sin=sin, k_cache=k_cache, v_cache=v_cache, indices=indices,
+                 scale_k=scale_k, scale_v=scale_v, q_out=q_out, k_out=k_out, v_out=v_out,
+                 weight_scale=weight_scale, act_scale=act_scale, bias=bias, offset_k=offset_k,
+                 offset_v=offset_v)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be [T, H] with contiguous rows")
-    for name, t in (("cos", cos), ("sin", sin), ("q_out", q_out), ("k_out", k_out),
-                    ("v_out", v_out), ("indices", indices)):
-        if t is not None and not t.is_contiguous():
+    T, D = x.shape[0], head_dim
+    H, HK = (nq + 2 * nkv) * D, nkv * D
+    if x.shape[1] != H:
+        raise ValueError(f"x must have (nq + 2 nkv) * head_dim = {H} columns")
+    out16 = (torch.bfloat16, torch.float16)
+    f32 = torch.float32
+    if cos.dtype not in out16 or sin.dtype != cos.dtype:
+        raise ValueError("cos and sin must be bf16 or fp16 tensors of one dtype")
+    if indices.dtype != torch.int32:
+        raise ValueError("indices must be int32")
+    if k_cache.element_size() != 1 or v_cache.element_size() != 1:
+        raise ValueError("k_cache and v_cache are int8 caches (1-byte elements)")
+    need_idx = T if cache_mode == KVEPI_DRQ_PAGE else (T // seq_len if seq_len else -1)
+    checks = [("cos", cos, T * D, None), ("sin", sin, T * D, None),
+              ("indices", indices, need_idx, None), ("scale_k", scale_k, HK, f32),
+              ("scale_v", scale_v, HK, f32), ("q_out", q_out, T * nq * D, cos.dtype),
+              ("k_out", k_out, T * HK, cos.dtype), ("v_out", v_out, T * HK, cos.dtype),
+              ("weight_scale", weight_scale, H, f32), ("act_scale", act_scale, T, f32),
+              ("bias", bias, H, None), ("offset_k", offset_k, HK, f32),
+              ("offset_v", offset_v, HK, f32)]
+    for name, t, n, dt in checks:
+        if t is None:
+            continue
+        if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if dt is not None and t.dtype != dt:
+            raise ValueError(f"{name} must be {dt} (got {t.dtype})")
+        if t.numel() < n:
+            raise ValueError(f"{name} must hold at least {n} values (got {t.numel()})")
     return kvepi_drq_params(
         _ptr(x), _dtype_code(x), _dtype_code(cos), x.shape[0], x.stride(0), nq, nkv, head_dim,
         _ptr(cos), _ptr(sin), _ptr(weight_scale), _ptr(act_scale), _ptr(bias),

@@ -98,6 +98,15 @@ def test_algorithmic_split_by_hand():
     assert bench.algorithmic_split(w) == (4 * 131072 + 129761 * 256, 129761 * 68)
 
 
+def test_fp4_nope_bytes_by_hand():
+    # quantMode 2's nope segment: the 512 nope values of x are read (the rope
+    # columns are neither read nor written), gamma once, and 352 - 64 = 288
+    # bytes (256 code bytes, 16 bf16 scales) written per hit row
+    w = kvgen.config(7)
+    hits = int(((w.slots >= 0) & (w.slots < w.cache.num_slots)).sum())
+    assert bench.algorithmic_split(w) == (4 * 262144 + hits * 1024 + 1024, hits * 288)
+
+
 def test_ceiling_mix_follows_the_workload():
     # the streaming mix closest (in log ratio) to the workload's read:write
     assert bench.mix_of(1408, 672) == (2, 1)
