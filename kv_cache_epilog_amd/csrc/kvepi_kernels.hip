@@ -460,10 +460,31 @@ __device__ __forceinline__ float div448_fast(float m) {
 // keeps its sign.  Otherwise the group divides exactly (an infinite scale,
 // from an infinite RMSNorm output, gives +-0 for finite values and the NaN
 // code for inf / inf).
+// The exact codes of a chunk of 8 bf16 values (packed in w) divided by su:
+// IEEE division and the software encoder, rolled over the four words (the
+// rare branch: little code, few registers).  Code byte i is value i's.
+__device__ __forceinline__ void codes_fp8_exact(uint4 w, float su, uint32_t (&cw)[2]) {
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll 1
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t e0 = su > 0.0f ? enc_e4m3_sw(lo_f(w.x) / su) : 0u;
+    const uint32_t e1 = su > 0.0f ? enc_e4m3_sw(hi_f(w.x) / su) : 0u;
+    c0 = (c0 >> 16) | (c1 << 16);
+    c1 = (c1 >> 16) | ((e0 | (e1 << 8)) << 16);
+    w = make_uint4(w.y, w.z, w.w, w.x);
+  }
+  cw[0] = c0;
+  cw[1] = c1;
+}
+
 __device__ __forceinline__ uint32_t codes_fp8_bf16scale(const float (&v)[8], float m, bool fast,
-                                                        uint32_t (&cw)[2]) {
+                                                        uint32_t (&cw)[2],
+                                                        uint4 packed = make_uint4(0, 0, 0, 0),
+                                                        bool rolled = false) {
   const float su = round_bf16(fast ? div448_fast(m) : m / 448.0f);
-  if (fast) {
+  if (rolled && !fast) {
+    codes_fp8_exact(packed, su, cw);
+  } else if (fast) {
     float rs = rcp_rn(su);
     if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
     const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
@@ -576,14 +597,25 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     // square that underflows and rounds, and the fused sum above would then
     // round once where the definition rounds the square first: such waves,
     // rare, sum the separately rounded squares.
+    // (The rare branches below run as rolled loops over the words of a
+    // chunk, rotating the words through one register set, so that they add
+    // little code and few registers to the common path.)
     if (__builtin_amdgcn_ballot_w64(mn < 0x1p-67f) != 0) {
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        float v[8], q[8];
-        unpack8(b.xw[j], v);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) q[t] = v[t] * v[t];
-        s8[j] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+        uint4 w = b.xw[j];
+        float pr[4];  // pair sums (x[2q]^2 + x[2q+1]^2), each square rounded
+#pragma unroll 1
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = lo_f(w.x), v1 = hi_f(w.x);
+          const float p2 = v0 * v0 + v1 * v1;
+          w = make_uint4(w.y, w.z, w.w, __float_as_uint(p2));
+        }
+        pr[0] = __uint_as_float(w.x);
+        pr[1] = __uint_as_float(w.y);
+        pr[2] = __uint_as_float(w.z);
+        pr[3] = __uint_as_float(w.w);
+        s8[j] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
       }
 #pragma unroll
       for (int j = 0; j < C; ++j) part[j] = grp_sum<L>(s8[j]);
@@ -629,13 +661,17 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     } else {
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        float v[8], g[8], y[8];
-        unpack8(b.xw[j], v);
-        gamma8<L * C>(g_lds, j * L + li, g);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) y[q] = (v[q] / rms) * g[q];
-        yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
-                           pack_bf16(y[6], y[7]));
+        uint4 w = b.xw[j];
+        const float *gp = reinterpret_cast<const float *>(g_lds + (j * L + li));
+#pragma unroll 1
+        for (int q = 0; q < 4; ++q) {
+          // values 2q, 2q+1: gamma plane q / 2, entries 2 (q % 2) + {0, 1}
+          const float *gq = gp + (q >> 1) * 4 * (L * C) + 2 * (q & 1);
+          const float y0 = (lo_f(w.x) / rms) * gq[0];
+          const float y1 = (hi_f(w.x) / rms) * gq[1];
+          w = make_uint4(w.y, w.z, w.w, pack_bf16(y0, y1));
+        }
+        yw[j] = w;
       }
     }
   } else {
@@ -816,7 +852,8 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], true, cw[i]);
       } else {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], inr[i], cw[i]);
+        for (int i = 0; i < NB; ++i)
+          o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], inr[i], cw[i], yw[j0 + i], true);
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) o.w[j0 + i] = make_uint4(cw[i][0], cw[i][1], 0u, 0u);
