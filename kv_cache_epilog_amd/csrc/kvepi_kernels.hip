@@ -301,6 +301,12 @@ constexpr bool has_aux(int m) { return m != M_FP8_BF16 && m != M_FP8_E8M0; }
 constexpr bool fixed_rope(int m) { return !whole_row(m) && m != M_SPLIT_G && m != M_FP4_NOPE; }
 // modes whose rows are assembled in LDS when the layout allows (FAST == 2)
 constexpr bool staged_mode(int m) { return m == M_FP8_BF16 || m == M_FP4_NOPE; }
+// Speculative rows (staged mode-0 rows after RMSNorm): the row is computed
+// with the fast arithmetic only, while a flag records whether any input is
+// outside the ranges where that arithmetic is exact; a wave-iteration with
+// such a row computes its rows again with exact arithmetic (exact_row_fp8).
+// This keeps the checks off the branches of the common path.
+constexpr bool spec_rows(int m, bool norm, int fast) { return m == M_FP8_BF16 && norm && fast == 2; }
 constexpr bool gen_rope(int m) { return m == M_SPLIT_G; }
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
@@ -399,6 +405,7 @@ struct RowOut {
   uint8_t *p0, *p1;
   uint4 w[C];
   uint32_t sb[C];
+  bool redo;  // (speculative rows) the fast arithmetic may be inexact here
   uint32_t ry[whole_row(MODE) ? 1 : (gen_rope(MODE) ? RopeShape<L>::TPG : RopeShape<L>::TPL)];
 };
 
@@ -593,6 +600,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 #pragma unroll
       for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
     float ss = part[0];
+    constexpr bool SPEC = spec_rows(MODE, NORM, FAST);
     // A smaller magnitude (zeros included, which costs nothing) can have a
     // square that underflows and rounds, and the fused sum above would then
     // round once where the definition rounds the square first: such waves,
@@ -600,7 +608,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     // (The rare branches below run as rolled loops over the words of a
     // chunk, rotating the words through one register set, so that they add
     // little code and few registers to the common path.)
-    if (__builtin_amdgcn_ballot_w64(mn < 0x1p-67f) != 0) {
+    if (!SPEC && __builtin_amdgcn_ballot_w64(mn < 0x1p-67f) != 0) {
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         uint4 w = b.xw[j];
@@ -628,9 +636,9 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     const float mean = a.inv_nseg != 0.0f ? ss * a.inv_nseg : ss / a.nseg_f;
     const float xs = mean + a.eps;
     // (a wave-uniform choice, so only one of the two square roots runs)
-    const float rms = __builtin_amdgcn_ballot_w64(!(xs >= 0x1p-96f && xs <= 0x1p+127f)) == 0
-                          ? sqrt_rn(xs)
-                          : __builtin_sqrtf(xs);
+    const bool xs_ok = xs >= 0x1p-96f && xs <= 0x1p+127f;
+    const float rms = SPEC || __builtin_amdgcn_ballot_w64(!xs_ok) == 0 ? sqrt_rn(xs)
+                                                                     : __builtin_sqrtf(xs);
     // The fast division needs a normal rms with a normal reciprocal, every
     // quotient normal (|x| >= 2^(e(rms) - 252) guarantees it) and an exact
     // FMA residual (|x| >= 2^-100).  Rows holding a smaller magnitude --
@@ -640,7 +648,11 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     const float thr = __uint_as_float((uint32_t)(k + 127) << 23);  // 2^k
     const bool tiny = mn < thr;
     bool fast = re >= 127 - 100 && re <= 127 + 100;
-    if constexpr (L == 64) {
+    if constexpr (SPEC) {
+      // checks the fast branches need, answered after the row is done
+      o.redo = mn < 0x1p-67f || tiny || !xs_ok || !fast;
+      fast = true;
+    } else if constexpr (L == 64) {
       fast = fast && __builtin_amdgcn_ballot_w64(tiny) == 0;
     } else {
       const uint64_t bal = __builtin_amdgcn_ballot_w64(tiny);
@@ -847,7 +859,11 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         all = all && inr[i];
       }
       uint32_t cw[NB][2];
-      if (NORM && __builtin_amdgcn_ballot_w64(!all) == 0) {
+      if constexpr (spec_rows(MODE, NORM, FAST)) {
+        o.redo = o.redo || !all;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], true, cw[i]);
+      } else if (NORM && __builtin_amdgcn_ballot_w64(!all) == 0) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], true, cw[i]);
       } else {
@@ -860,6 +876,57 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
     }
 #pragma unroll
     for (int k = 0; k < TPL; ++k) o.ry[k] = ry[k];
+  }
+}
+
+// Exact arithmetic for a speculative row (mode 0 after RMSNorm): the sum of
+// separately rounded squares, the library square root, IEEE division by rms,
+// then per group the scale amax / 448 by IEEE division and the codes of the
+// exact quotients -- the definitions themselves, for rows holding inputs
+// outside the ranges of the fast arithmetic.  Rewrites the codes and scales
+// of o (the rope words are unchanged).  Rolled loops: rare, little code.
+template <int L, int C>
+__device__ __forceinline__ void exact_row_fp8(const KArgs &a, int li, const uint4 (&xw)[C],
+                                                        const float4 *g_lds,
+                                                        RowOut<M_FP8_BF16, L, C> &o) {
+  float part[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    uint4 w = xw[j];
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      const float v0 = lo_f(w.x), v1 = hi_f(w.x);
+      w = make_uint4(w.y, w.z, w.w, __float_as_uint(v0 * v0 + v1 * v1));
+    }
+    const float s8 = (__uint_as_float(w.x) + __uint_as_float(w.y)) +
+                     (__uint_as_float(w.z) + __uint_as_float(w.w));
+    part[j] = grp_sum<L>(s8);
+  }
+#pragma unroll
+  for (int w = 1; w < C; w *= 2)
+#pragma unroll
+    for (int j = 0; j < C; j += 2 * w) part[j] = part[j] + part[j + w];
+  const float mean = a.inv_nseg != 0.0f ? part[0] * a.inv_nseg : part[0] / a.nseg_f;
+  const float rms = __builtin_sqrtf(mean + a.eps);
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    uint4 w = xw[j];
+    const float *gp = reinterpret_cast<const float *>(g_lds + (j * L + li));
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      const float *gq = gp + (q >> 1) * 4 * (L * C) + 2 * (q & 1);
+      const float y0 = (lo_f(w.x) / rms) * gq[0];
+      const float y1 = (hi_f(w.x) / rms) * gq[1];
+      w = make_uint4(w.y, w.z, w.w, pack_bf16(y0, y1));
+    }
+    float v[8];
+    unpack8(w, v);
+    const float m = grp_max<8>(amax8(v));  // 64 values = 8 lanes
+    const float su = round_bf16(m / 448.0f);
+    uint32_t cw[2];
+    codes_fp8_exact(w, su, cw);
+    o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
+    o.sb[j] = __float_as_uint(su) >> 16;
   }
 }
 
@@ -1187,9 +1254,18 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   // the next loads)
   RowOut<MODE, L, C> out;
   auto compute = [&](const IterInfo<R> &t, const RowBuf<MODE, ROPE, L, C> &b) {
+    out.redo = false;
     if (lane_live(t)) {
       compute_row<MODE, NORM, ROPE, L, C, FAST, XF16>(a, li, sub, b, g_lds, out);
       if constexpr (FAST == 2) stage_write<MODE, L, C>(a, li, sub, out, stage);
+    }
+    if constexpr (spec_rows(MODE, NORM, FAST)) {
+      // a row whose inputs leave the fast ranges: both rows again, exactly
+      if (__builtin_amdgcn_ballot_w64(out.redo) != 0 && lane_live(t)) {
+        lds_handover();
+        exact_row_fp8<L, C>(a, li, b.xw, g_lds, out);
+        stage_write<MODE, L, C>(a, li, sub, out, stage);
+      }
     }
     // the staged bytes one lane writes are stored by another lane: order the
     // LDS writes before the reads in stage_store (wave scope)
