@@ -1557,8 +1557,8 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   const int64_t n_groups = (p.T + rows_per_wave - 1) / rows_per_wave;
   // FAST: whole chunks per lane and 16-byte aligned rows (4-byte aligned k
   // rows in the bf16 split mode); stores then need no alignment dispatch
-  // 2: mode 0 rows laid out on 32 lanes (one or two chunks each) also
-  // assemble their rows in LDS
+  // 2: mode 0 and FP4 nope rows laid out on 32 lanes (one or two chunks
+  // each) also assemble their rows in LDS
   const bool aligned = L * C == a.nchunk && a.c_align >= 16 &&
                        (p.mode != KVEPI_MODE_BF16_SPLIT || a.a_align >= 4);
   const bool stages =
