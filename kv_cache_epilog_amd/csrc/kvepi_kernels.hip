@@ -445,6 +445,51 @@ __device__ __forceinline__ void codes_fp8(const float (&q)[8], uint32_t (&cw)[2]
   cw[1] = (uint32_t)w1;
 }
 
+// E4M3 codes of eight values q_i / sc, sc a power of two in [2^-100, 2^100]
+// (v_cvt_scalef32_pk_fp8_f32 takes the exponent of sc); every |q_i / sc| at
+// most 456 (tests/hw_check.hip checks the convert for fp32 inputs against the
+// software encoder of the scaled value).
+__device__ __forceinline__ void codes_fp8_scaled(const float (&q)[8], float sc,
+                                                 uint32_t (&cw)[2]) {
+  s16x2_t w0 = {0, 0}, w1 = {0, 0};
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, q[0], q[1], sc, false);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w0, q[2], q[3], sc, true);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, q[4], q[5], sc, false);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w1, q[6], q[7], sc, true);
+  cw[0] = __builtin_bit_cast(uint32_t, w0);
+  cw[1] = __builtin_bit_cast(uint32_t, w1);
+}
+
+// Reciprocals of the 128 significands of bf16 scales, kept in LDS by the
+// staged instances: entry k holds, for m = 1 + k/128, rs = 1/m rounded
+// downwards and rl = RN((1 - m rs) rs), the double-length reciprocal the
+// quotient v / m = fma(v, rs, v rl) takes.  They are computed at block start
+// with the very arithmetic the per-group path uses (rcp_rn, then one step
+// down when it rounded up).  A scale s = m 2^e then divides as v / m with the
+// convert scaled by 2^e: v / s and (v / m) 2^-e are the same fp32 value
+// wherever it is normal, and below that every code is +-0.
+__device__ __forceinline__ float2 recip_entry(int k) {
+  const float m = 1.0f + (float)k * 0x1p-7f;
+  float rs = rcp_rn(m);
+  if (__builtin_fmaf(-m, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
+  return make_float2(rs, __builtin_fmaf(-m, rs, 1.0f) * rs);
+}
+
+// The table sits at the start of the block's dynamic LDS (every extern
+// shared array names that same start).
+__device__ __forceinline__ const float2 *recip_table() {
+  extern __shared__ float2 kvepi_recip_lds[];
+  return kvepi_recip_lds;
+}
+constexpr int RECIP_BYTES = 128 * 8;
+
+// the table entry of a positive normal bf16-valued scale su, and 2^e(su)
+__device__ __forceinline__ float2 recip_of(float su, float &pow2) {
+  const uint32_t sb = __float_as_uint(su);
+  pow2 = __uint_as_float(sb & 0x7F800000u);
+  return recip_table()[__builtin_amdgcn_ubfe(sb, 16, 7)];
+}
+
 // m / 448 correctly rounded for a bf16 m in [2^-71, 2^100]: fma(m, H, m*Lo)
 // with H + Lo a double-length 1/448 (tests/fastdiv_check.c compares it with
 // the IEEE quotient for every such m).
@@ -484,6 +529,9 @@ __device__ __forceinline__ void codes_fp8_exact(uint4 w, float su, uint32_t (&cw
   cw[1] = c1;
 }
 
+// TBL (staged instances): rs and rl of the scale's significand from the LDS
+// table, the exponent applied by the scaled convert.
+template <bool TBL = false>
 __device__ __forceinline__ uint32_t codes_fp8_bf16scale(const float (&v)[8], float m, bool fast,
                                                         uint32_t (&cw)[2],
                                                         uint4 packed = make_uint4(0, 0, 0, 0),
@@ -491,6 +539,13 @@ __device__ __forceinline__ uint32_t codes_fp8_bf16scale(const float (&v)[8], flo
   const float su = round_bf16(fast ? div448_fast(m) : m / 448.0f);
   if (rolled && !fast) {
     codes_fp8_exact(packed, su, cw);
+  } else if (TBL && fast) {
+    float sc;
+    const float2 r = recip_of(su, sc);
+    float qv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qv[t] = __builtin_fmaf(v[t], r.x, v[t] * r.y);
+    codes_fp8_scaled(qv, sc, cw);
   } else if (fast) {
     float rs = rcp_rn(su);
     if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
@@ -539,10 +594,25 @@ __device__ __forceinline__ float grp_max_k(float f, int k) {
 // to 6.0625 to nearest even and saturates at 6 (tests/hw_check.hip); the
 // quotients stay below 6 / (1 - 2^-8).  Otherwise the group divides exactly
 // and encodes in software (a zero group: scale 0 and codes 0).
+// TBL (staged instances): the significand's reciprocal from the LDS table and
+// the scale's exponent applied by the convert, as in mode 0.
+template <bool TBL = false>
 __device__ __forceinline__ uint32_t codes_fp4_bf16scale(const float (&v)[8], float m, bool fast,
                                                         uint32_t &w) {
   const float su = round_bf16(fast ? div6_fast(m) : m / 6.0f);
-  if (fast) {
+  if (TBL && fast) {
+    float sc;
+    const float2 r = recip_of(su, sc);
+    float q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = __builtin_fmaf(v[t], r.x, v[t] * r.y);
+    uint32_t x = 0;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[0], q[1], sc, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[2], q[3], sc, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[4], q[5], sc, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[6], q[7], sc, 3);
+    w = x;
+  } else if (fast) {
     float rs = rcp_rn(su);
     if (__builtin_fmaf(-su, rs, 1.0f) < 0.0f) rs = __uint_as_float(__float_as_uint(rs) - 1u);
     const float rl = __builtin_fmaf(-su, rs, 1.0f) * rs;
@@ -745,7 +815,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       const float m = grp_max_k(amax8(v), a.glog);
       const bool fast = m >= 0x1p-90f && m <= 0x1p+100f;
       uint32_t w;
-      o.sb[j] = codes_fp4_bf16scale(v, m, fast, w);
+      o.sb[j] = codes_fp4_bf16scale<FAST == 2>(v, m, fast, w);
       o.w[j] = make_uint4(w, 0u, 0u, 0u);
     }
   } else if constexpr (MODE == M_MXFP4) {
@@ -862,14 +932,14 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       if constexpr (spec_rows(MODE, NORM, FAST)) {
         o.redo = o.redo || !all;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], true, cw[i]);
+        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale<FAST == 2>(vv[i], mm[i], true, cw[i]);
       } else if (NORM && __builtin_amdgcn_ballot_w64(!all) == 0) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], true, cw[i]);
+        for (int i = 0; i < NB; ++i) o.sb[j0 + i] = codes_fp8_bf16scale<FAST == 2>(vv[i], mm[i], true, cw[i]);
       } else {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          o.sb[j0 + i] = codes_fp8_bf16scale(vv[i], mm[i], inr[i], cw[i], yw[j0 + i], true);
+          o.sb[j0 + i] = codes_fp8_bf16scale<FAST == 2>(vv[i], mm[i], inr[i], cw[i], yw[j0 + i], true);
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) o.w[j0 + i] = make_uint4(cw[i][0], cw[i][1], 0u, 0u);
@@ -1129,8 +1199,14 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
   const int lane = threadIdx.x & 63;
   const int li = lane & (L - 1);
   const int sub = lane / L;
-  // gamma (the same for every row) staged once per block in LDS
-  extern __shared__ float4 g_lds[];
+  // dynamic LDS: (FAST == 2) the reciprocal table; gamma (the same for every
+  // row) staged once per block; (FAST == 2) the waves' row images
+  extern __shared__ float4 lds_base[];
+  if constexpr (FAST == 2) {
+    float2 *tb = reinterpret_cast<float2 *>(lds_base);
+    for (int k = threadIdx.x; k < 128; k += 256) tb[k] = recip_entry(k);
+  }
+  float4 *g_lds = lds_base + (FAST == 2 ? RECIP_BYTES / 16 : 0);
   if constexpr (NORM) {
     for (int i = threadIdx.x; i < L * C; i += 256) {
       const int c = chunk_of<L>(i % L, i / L);
@@ -1139,8 +1215,8 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       g_lds[i] = make_float4(g[0], g[1], g[2], g[3]);
       g_lds[i + L * C] = make_float4(g[4], g[5], g[6], g[7]);
     }
-    __syncthreads();
   }
+  if constexpr (NORM || FAST == 2) __syncthreads();
   // per-wave staging area for FAST == 2, after gamma
   uint8_t *stage = reinterpret_cast<uint8_t *>(g_lds) + (NORM ? L * C * 32 : 0) +
                    (threadIdx.x >> 6) * R * a.img_bytes;
@@ -1568,7 +1644,7 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   const int kmode = p.mode == KVEPI_MODE_BF16_SPLIT && p.rope_dim != 64 ? (int)M_SPLIT_G : p.mode;
   kfn_t fn = pick(kmode, p.norm, p.rope, p.x_fp16, L, C, fast);
   size_t lds = p.norm ? (size_t)L * C * 32 : 0;  // gamma as fp32, 32 KB at most
-  if (fast == 2) lds += (size_t)4 * (64 / L) * a.img_bytes;  // staging, 4 waves
+  if (fast == 2) lds += 128 * 8 + (size_t)4 * (64 / L) * a.img_bytes;  // table, staging
 
   // persistent waves: exactly as many blocks as the CUs hold at once
   const int cus = device_cus();

@@ -22,6 +22,14 @@
 //           saturating at 6), every fp32 |q| <= 6.0625: the FP4 nope mode
 //           converts quotients by a scale rounded to bf16, which exceed 6 by
 //           at most a factor 1 / (1 - 2^-8) < 1.004
+//   fp8sq, fp4sq  the scaled converts of fp32 inputs (the quotients by a
+//           scale's significand that the staged quantisers convert with the
+//           scale's exponent): v_cvt_scalef32_pk_{fp8,fp4}_f32(u 2^E, 2^E) ==
+//           the software encoder of u, every fp32 u in [2^-12, 456] (FP8) or
+//           [2^-4, 6.0625] (FP4) and zero, every E in [-100, 100] with u 2^E
+//           normal; below those ranges, where every code is +-0, inputs q with
+//           |q| < 2^(E-12) (every 1021st pattern, subnormals included) give
+//           +-0 with the sign of q
 //   div16   div_fast(a, b, rcp_rn(b)) == a / b for every fp16 significand a
 //           against every fp32 significand b (quotient in (1/2, 2); exponents
 //           are a pure scaling while the quotient stays normal)
@@ -182,6 +190,77 @@ __global__ void k_scaled(uint32_t n, int fp4, int f16, unsigned *bad, unsigned *
   if (got != want) atomicAdd(bad, 1u);
 }
 
+// index i: u = bits base + i; q = u 2^E (skipped where not normal)
+__global__ void k_scaledq(uint32_t base, uint32_t n, int E, int fp4, unsigned *bad,
+                          unsigned long long *count) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  bool checked = false;
+  if (i < n) {
+    const float u = __uint_as_float(base + i);
+    const float q = u * __uint_as_float((uint32_t)(E + 127) << 23);  // exact when normal
+    if (u == 0.0f || __builtin_fabsf(q) >= 0x1p-126f) {
+      const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
+      uint32_t got, want;
+      if (fp4) {
+        got = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, -q, sc, 0) & 0xFFu;
+        want = enc_e2m1_sw(u) | (enc_e2m1_sw(-u) << 4);
+      } else {
+        s16x2_t w = {0, 0};
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, q, -q, sc, false);
+        got = (uint32_t)(uint16_t)w[0];
+        want = enc_e4m3_sw(u) | (enc_e4m3_sw(-u) << 8);
+      }
+      checked = true;
+      if (got != want) atomicAdd(bad, 1u);
+    }
+  }
+  const uint64_t b = __builtin_amdgcn_ballot_w64(checked);
+  if ((threadIdx.x & 63) == 0 && b != 0)
+    atomicAdd(count, (unsigned long long)__builtin_popcountll(b));
+}
+
+// tiny inputs: q bits = 1021 i below 2^(E-12); codes +-0 with q's sign
+__global__ void k_scaledtiny(uint32_t n, int E, int fp4, unsigned *bad,
+                             unsigned long long *count) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t lim = (uint32_t)(E - 12 + 127) << 23;
+  bool checked = false;
+  if (i < n && (uint64_t)i * 1021u < lim) {
+    const float q = __uint_as_float(i * 1021u);
+    const float sc = __uint_as_float((uint32_t)(E + 127) << 23);
+    uint32_t got, want;
+    if (fp4) {
+      got = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, -q, sc, 0) & 0xFFu;
+      want = 0x80u;
+    } else {
+      s16x2_t w = {0, 0};
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, q, -q, sc, false);
+      got = (uint32_t)(uint16_t)w[0];
+      want = 0x8000u;
+    }
+    checked = true;
+    if (got != want) atomicAdd(bad, 1u);
+  }
+  const uint64_t b = __builtin_amdgcn_ballot_w64(checked);
+  if ((threadIdx.x & 63) == 0 && b != 0)
+    atomicAdd(count, (unsigned long long)__builtin_popcountll(b));
+}
+
+static void launch_scaledq(uint32_t lo, uint32_t hi, int fp4, unsigned *bad,
+                           unsigned long long *count) {
+  for (int E = -100; E <= 100; ++E) {
+    hipLaunchKernelGGL(k_scaledq, dim3(1), dim3(64), 0, 0, 0u, 1u, E, fp4, bad, count);  // zero
+    for (uint64_t b = lo; b <= hi; b += (1ull << 28)) {
+      const uint32_t n = (uint32_t)((hi + 1 - b) < (1ull << 28) ? (hi + 1 - b) : (1ull << 28));
+      hipLaunchKernelGGL(k_scaledq, dim3((n + 255) / 256), dim3(256), 0, 0, (uint32_t)b, n, E,
+                         fp4, bad, count);
+    }
+    const uint32_t nt = (uint32_t)((((uint64_t)(E - 12 + 127) << 23) + 1020) / 1021);
+    hipLaunchKernelGGL(k_scaledtiny, dim3((nt + 255) / 256), dim3(256), 0, 0, nt, E, fp4, bad,
+                       count + 1);
+  }
+}
+
 static void launch_range(void (*fn)(uint32_t, uint32_t, unsigned *), uint64_t lo, uint64_t hi,
                          unsigned *bad) {
   for (uint64_t b = lo; b <= hi; b += (1ull << 28)) {
@@ -209,12 +288,20 @@ int main() {
     hipLaunchKernelGGL(k_rn16, dim3((1u << 28) / 256), dim3(256), 0, 0, (uint32_t)b, 1u << 28,
                        d + 13);
   launch_range(k_fp4q, 0x00000000u, 0x40C20000u, d + 14);     // [0, 6.0625]
+  unsigned long long *dc = nullptr;  // checks counted by k_scaledq / k_scaledtiny
+  if (hipMalloc(&dc, 4 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  (void)hipMemset(dc, 0, 4 * sizeof(unsigned long long));
+  launch_scaledq(0x39800000u, 0x43E40000u, 0, d + 15, dc + 0);  // [2^-12, 456]
+  launch_scaledq(0x3D800000u, 0x40C20000u, 1, d + 16, dc + 2);  // [2^-4, 6.0625]
   const uint32_t n_div = 1u << 23;
   hipLaunchKernelGGL(k_div16, dim3(n_div / 256), dim3(256), 0, 0, n_div, d + 12);
   const hipError_t e = hipDeviceSynchronize();
-  unsigned h[15] = {0};
+  unsigned h[17] = {0};
+  unsigned long long hc[4] = {0, 0, 0, 0};
   (void)hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
+  (void)hipMemcpy(hc, dc, sizeof(hc), hipMemcpyDeviceToHost);
   (void)hipFree(d);
+  (void)hipFree(dc);
   if (e != hipSuccess) {
     printf("hip error %d\n", (int)e);
     return 2;
@@ -230,6 +317,9 @@ int main() {
   printf("div16: %u mismatches of %llu\n", h[12], 1024ull << 23);
   printf("rn16: %u mismatches of %llu\n", h[13], 1ull << 32);
   printf("fp4q: %u mismatches of %u\n", h[14], 0x40C20000u + 1u);
-  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12] | h[13] | h[14]) ? 1
-                                                                                          : 0;
+  printf("fp8sq: %u mismatches of %llu (+ %llu tiny)\n", h[15], hc[0], hc[1]);
+  printf("fp4sq: %u mismatches of %llu (+ %llu tiny)\n", h[16], hc[2], hc[3]);
+  const bool none_checked = hc[0] == 0 || hc[1] == 0 || hc[2] == 0 || hc[3] == 0;
+  return (h[0] | h[1] | h[2] | h[3] | h[5] | h[7] | h[8] | h[10] | h[12] | h[13] | h[14] |
+          h[15] | h[16]) || none_checked ? 1 : 0;
 }
