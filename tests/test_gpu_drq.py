@@ -172,3 +172,27 @@ def _drq_fuzz_case(k):
 @pytest.mark.parametrize("k", range(80))
 def test_fuzz(k):
     compare(_drq_fuzz_case(k), f"fuzz {k}")
+
+
+# int32 x runs in persistent blocks that keep the per-channel parameters in
+# LDS and load each thread's next unit before storing the current one; a grid
+# capped at 1 or 3 blocks makes every thread run many units, through the
+# pipeline's whole cycle (first unit, steady state, a last unit with nothing
+# after it), on rows of every shape class
+_MANY = [
+    dict(T=300, nq=4, nkv=2, D=64, bias_dtype=F32, act=True, offsets=True),
+    dict(T=257, nq=2, nkv=1, D=128, bias_dtype=BF, offsets=False, skip=0.3),
+    dict(T=150, nq=30, nkv=1, D=128, bias_dtype=I32, offsets=True),
+    dict(T=1000, nq=8, nkv=8, D=16, bias_dtype=None, act=False, kv_output=False),
+    dict(T=7 * 13, nq=2, nkv=1, D=128, bias_dtype=FP, cache_mode=1, seq_len=13, bs=13),
+    dict(T=64, nq=1, nkv=1, D=64, bias_dtype=FP, x_pad=40, skip=0.0),
+]
+
+
+@pytest.mark.parametrize("blocks", [1, 3])
+@pytest.mark.parametrize("k", range(len(_MANY)))
+@pytest.mark.parametrize("out", [BF, FP])
+def test_int32_many_units_per_thread(monkeypatch, blocks, k, out):
+    monkeypatch.setenv("KVEPI_DRQ_MAX_BLOCKS", str(blocks))
+    c = make_case(1100 + 10 * k + out, x_dtype=I32, out_dtype=out, **_MANY[k])
+    compare(c, f"int32, {blocks} blocks, case {k}")
