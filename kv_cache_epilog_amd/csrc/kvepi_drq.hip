@@ -77,6 +77,23 @@ __device__ __forceinline__ void ldw(const uint8_t *p, uint32_t (&w)[NW]) {
     w[0] = *reinterpret_cast<const uint32_t *>(p);
   }
 }
+// the same as a streamed (nontemporal) store: the q / k / v outputs are
+// contiguous rows written once, and streaming them measured 8 % faster for
+// 16-bit x and 3 % for int32 x (the int8 cache rows, scattered 64-byte
+// pieces, measured slower streamed and keep plain stores)
+typedef unsigned int u32x2v_t __attribute__((ext_vector_type(2)));
+template <int NW>
+__device__ __forceinline__ void stw_nt(uint8_t *p, const uint32_t (&w)[NW]) {
+  if constexpr (NW == 4) {
+    const u32x4v_t v = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4v_t *>(p));
+  } else if constexpr (NW == 2) {
+    const u32x2v_t v = {w[0], w[1]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2v_t *>(p));
+  } else {
+    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t *>(p));
+  }
+}
 template <int NW>
 __device__ __forceinline__ void stw(uint8_t *p, const uint32_t (&w)[NW]) {
   if constexpr (NW == 4)
@@ -328,8 +345,8 @@ __device__ __forceinline__ void compute_unit(const DArgs &a, const Unit<XT, V> &
   pack<OT, V>(y1, w1);
   if ((int32_t)head < nq) {
     uint8_t *qo = a.q_out + 2 * ((int64_t)t * nq * D + h0);
-    stw<V / 2>(qo, w0);
-    stw<V / 2>(qo + 2 * half, w1);
+    stw_nt<V / 2>(qo, w0);
+    stw_nt<V / 2>(qo + 2 * half, w1);
     return;
   }
   // k or v head: the 16-bit output, then the int8 codes of the rounded values
@@ -339,8 +356,8 @@ __device__ __forceinline__ void compute_unit(const DArgs &a, const Unit<XT, V> &
   uint8_t *out = is_k ? a.k_out : a.v_out;
   if (out != nullptr) {
     uint8_t *o = out + 2 * ((int64_t)t * nkv * D + c);
-    stw<V / 2>(o, w0);
-    stw<V / 2>(o + 2 * half, w1);
+    stw_nt<V / 2>(o, w0);
+    stw_nt<V / 2>(o + 2 * half, w1);
   }
   // the token's cache row (page: its slot; contiguous: row start[b] + s of
   // block b); -1 or a row outside the cache skips the write
