@@ -301,12 +301,15 @@ constexpr bool has_aux(int m) { return m != M_FP8_BF16 && m != M_FP8_E8M0; }
 constexpr bool fixed_rope(int m) { return !whole_row(m) && m != M_SPLIT_G && m != M_FP4_NOPE; }
 // modes whose rows are assembled in LDS when the layout allows (FAST == 2)
 constexpr bool staged_mode(int m) { return m == M_FP8_BF16 || m == M_FP4_NOPE; }
-// Speculative rows (staged mode-0 rows after RMSNorm): the row is computed
-// with the fast arithmetic only, while a flag records whether any input is
-// outside the ranges where that arithmetic is exact; a wave-iteration with
-// such a row computes its rows again with exact arithmetic (exact_row_fp8).
-// This keeps the checks off the branches of the common path.
-constexpr bool spec_rows(int m, bool norm, int fast) { return m == M_FP8_BF16 && norm && fast == 2; }
+// Speculative rows (staged rows of mode 0 and of the FP4 nope mode after
+// RMSNorm): the row is computed with the fast arithmetic only, while a flag
+// records whether any input is outside the ranges where that arithmetic is
+// exact; a wave-iteration with such a row computes its rows again with exact
+// arithmetic (exact_row).  This keeps the checks off the branches of the
+// common path.
+constexpr bool spec_rows(int m, bool norm, int fast) {
+  return staged_mode(m) && norm && fast == 2;
+}
 constexpr bool gen_rope(int m) { return m == M_SPLIT_G; }
 
 // Rope work is split into 32 tasks: task tau = 16h + p produces outputs
@@ -815,7 +818,12 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       const float m = grp_max_k(amax8(v), a.glog);
       const bool fast = m >= 0x1p-90f && m <= 0x1p+100f;
       uint32_t w;
-      o.sb[j] = codes_fp4_bf16scale<FAST == 2>(v, m, fast, w);
+      if constexpr (spec_rows(MODE, NORM, FAST)) {
+        o.redo = o.redo || !fast;
+        o.sb[j] = codes_fp4_bf16scale<true>(v, m, true, w);
+      } else {
+        o.sb[j] = codes_fp4_bf16scale<FAST == 2>(v, m, fast, w);
+      }
       o.w[j] = make_uint4(w, 0u, 0u, 0u);
     }
   } else if constexpr (MODE == M_MXFP4) {
@@ -949,16 +957,16 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
   }
 }
 
-// Exact arithmetic for a speculative row (mode 0 after RMSNorm): the sum of
-// separately rounded squares, the library square root, IEEE division by rms,
-// then per group the scale amax / 448 by IEEE division and the codes of the
-// exact quotients -- the definitions themselves, for rows holding inputs
-// outside the ranges of the fast arithmetic.  Rewrites the codes and scales
-// of o (the rope words are unchanged).  Rolled loops: rare, little code.
-template <int L, int C>
-__device__ __forceinline__ void exact_row_fp8(const KArgs &a, int li, const uint4 (&xw)[C],
-                                                        const float4 *g_lds,
-                                                        RowOut<M_FP8_BF16, L, C> &o) {
+// Exact arithmetic for a speculative row (mode 0 or the FP4 nope mode after
+// RMSNorm): the sum of separately rounded squares, the library square root,
+// IEEE division by rms, then per group the scale amax / 448 (amax / 6) by
+// IEEE division and the codes of the exact quotients -- the definitions
+// themselves, for rows holding inputs outside the ranges of the fast
+// arithmetic.  Rewrites the codes and scales of o (mode 0's rope words are
+// unchanged).  Rolled loops where they matter: rare, little code.
+template <int MODE, int L, int C>
+__device__ __forceinline__ void exact_row(const KArgs &a, int li, const uint4 (&xw)[C],
+                                          const float4 *g_lds, RowOut<MODE, L, C> &o) {
   float part[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
@@ -991,12 +999,19 @@ __device__ __forceinline__ void exact_row_fp8(const KArgs &a, int li, const uint
     }
     float v[8];
     unpack8(w, v);
-    const float m = grp_max<8>(amax8(v));  // 64 values = 8 lanes
-    const float su = round_bf16(m / 448.0f);
-    uint32_t cw[2];
-    codes_fp8_exact(w, su, cw);
-    o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
-    o.sb[j] = __float_as_uint(su) >> 16;
+    if constexpr (MODE == M_FP4_NOPE) {
+      const float m = grp_max_k(amax8(v), a.glog);
+      uint32_t cw;
+      o.sb[j] = codes_fp4_bf16scale<false>(v, m, false, cw);
+      o.w[j] = make_uint4(cw, 0u, 0u, 0u);
+    } else {
+      const float m = grp_max<8>(amax8(v));  // 64 values = 8 lanes
+      const float su = round_bf16(m / 448.0f);
+      uint32_t cw[2];
+      codes_fp8_exact(w, su, cw);
+      o.w[j] = make_uint4(cw[0], cw[1], 0u, 0u);
+      o.sb[j] = __float_as_uint(su) >> 16;
+    }
   }
 }
 
@@ -1339,7 +1354,7 @@ __global__ __launch_bounds__(256) void epilog_kernel(const KArgs a) {
       // a row whose inputs leave the fast ranges: both rows again, exactly
       if (__builtin_amdgcn_ballot_w64(out.redo) != 0 && lane_live(t)) {
         lds_handover();
-        exact_row_fp8<L, C>(a, li, b.xw, g_lds, out);
+        exact_row<MODE, L, C>(a, li, b.xw, g_lds, out);
         stage_write<MODE, L, C>(a, li, sub, out, stage);
       }
     }
