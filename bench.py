@@ -181,16 +181,23 @@ def cold_launches(step, dev, stream, launches: int = 20, scrub_mib: int = 512,
     read-only reduction over scrub_mib MiB (twice the 256 MB Infinity Cache
     and far beyond L2) evicts the inputs and leaves clean lines, so no
     write-back of the scrub lands inside the timed launch; HIP events on the
-    launch stream time each launch alone (its dispatch included)."""
+    launch stream time each launch alone (its dispatch included).  The host
+    enqueues each launch while the device still runs the kernel before it
+    (the scrub, or without scrub a short busy kernel, kvc_clock), so no host
+    time falls between the events."""
     import torch
-    n = scrub_mib << 20
+    n = scrub_mib << 20 if scrub else 4
     a = torch.zeros(n // 4, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
     evs = []
     with torch.cuda.stream(stream):
         for _ in range(launches):
             if scrub:
                 torch.amax(a, out=sink)
+            else:
+                _check(ceiling_lib().kvc_clock(clk.data_ptr(), 8000, stream.cuda_stream),
+                       "kvc_clock")
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -198,7 +205,7 @@ def cold_launches(step, dev, stream, launches: int = 20, scrub_mib: int = 512,
             e1.record(stream)
             evs.append((e0, e1))
     torch.cuda.synchronize()
-    del a, sink
+    del a, sink, clk
     return sum(e0.elapsed_time(e1) for e0, e1 in evs) / launches
 
 
@@ -248,6 +255,67 @@ def time_back_to_back(launch, stream, launches: int, warmup: int = 5) -> float:
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / launches
+
+
+def time_host_launched(step, stream, launches: int):
+    """The warm-up: `launches` calls of step() from the host, back to back,
+    HIP events around them.  Their rate includes the host's time per call
+    wherever that exceeds the kernel's (short launches); null for none."""
+    if launches <= 0:
+        return None
+    ms = time_back_to_back(step, stream, launches, warmup=0)
+    return {"ms_per_launch": ms, "launches": launches,
+            "note": "the warm-up launches, each a call through the Python binding and the C ABI "
+                    "from the host; the timed region replays the same launches from a HIP graph"}
+
+
+def capture(launch, launches: int):
+    """`launches` calls of launch() captured in one HIP graph (torch's
+    CUDAGraph); launch() enqueues on torch's current stream.  One call runs
+    first, on a side stream, outside the capture.  Replaying the graph
+    dispatches the launches back to back with no host work between them:
+    the library's host path (the Python binding's checks, the C ABI's
+    validation, the launch) takes about 9-12 us per call, longer than a short
+    launch's kernel, so timing eager calls would time the host."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            launch()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, launches: int, stream, warm: bool = True) -> float:
+    """ms per launch of one replay of g (a graph of `launches` launches),
+    HIP events on the stream around it; an untimed replay first if warm."""
+    import torch
+    with torch.cuda.stream(stream):
+        if warm:
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / launches
+
+
+def time_launches(launch, stream, launches: int) -> float:
+    """ms per launch of `launches` launches captured in one graph and
+    replayed (after a warm replay)."""
+    g = capture(launch, launches)
+    ms = time_graph(g, launches, stream)
+    del g
+    return ms
 
 
 def shader_clock_mhz(dev, stream) -> float:
@@ -309,9 +377,11 @@ class StreamCeiling:
         self.per_cu = per_cu
 
     def launch(self):
+        import torch
         _check(ceiling_lib().kvc_stream(self.src.data_ptr(), self.dst.data_ptr(),
                                         self.sink.data_ptr(), self.steps, self.r, self.w,
-                                        self.per_cu * device_cus(), self.stream.cuda_stream),
+                                        self.per_cu * device_cus(),
+                                        torch.cuda.current_stream().cuda_stream),
                "kvc_stream")
 
     def gbps(self, ms: float) -> float:
@@ -324,7 +394,7 @@ class StreamCeiling:
         times = {}
         for per_cu in (2, 4, 8):
             self.per_cu = per_cu
-            times[per_cu] = time_back_to_back(self.launch, self.stream, launches)
+            times[per_cu] = time_launches(self.launch, self.stream, launches)
         self.per_cu = min(times, key=times.get)
         return times[self.per_cu]
 
@@ -357,8 +427,12 @@ def ceilings(dev, stream, abytes: int, read_bytes: int, write_bytes: int, launch
     out["_same_size"] = c
     lib = ceiling_lib()
     blocks = 8 * device_cus()
-    out["empty_launch_us"] = 1e3 * time_back_to_back(
-        lambda: _check(lib.kvc_empty(blocks, stream.cuda_stream), "kvc_empty"), stream, launches)
+
+    def empty():
+        import torch
+        _check(lib.kvc_empty(blocks, torch.cuda.current_stream().cuda_stream), "kvc_empty")
+
+    out["empty_launch_us"] = 1e3 * time_launches(empty, stream, launches)
     return out
 
 
@@ -418,10 +492,11 @@ def pattern_ceiling(w: kvgen.Workload, dev, stream, launches: int = 50):
     def launch():
         _check(lib.kvc_scatter_rows(src.data_ptr(), src_row, src_row, slots.data_ptr(), w.T,
                                     dst.data_ptr(), row, w.cache.block_size, pitch, bstride,
-                                    w.cache.num_slots, blocks, stream.cuda_stream),
+                                    w.cache.num_slots, blocks,
+                                    torch.cuda.current_stream().cuda_stream),
                "kvc_scatter_rows")
 
-    ms = time_back_to_back(launch, stream, launches)
+    ms = time_launches(launch, stream, launches)
     nbytes = 4 * w.T + w.hits * (src_row + row)
     del src, dst, slots
     return {"ms_per_launch": ms, "bytes": nbytes, "achieved": nbytes / (ms * 1e-3) / 1e9,
@@ -572,9 +647,9 @@ def main():
     t = upload(w, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(s=stream):
         kvepi_run(t["x"], t["slots"], t["cache"], w.mode, w.group_size, gamma=t["gamma"],
-                  cos=t["cos"], sin=t["sin"], cache_aux=t["aux"], eps=w.eps, stream=stream)
+                  cos=t["cos"], sin=t["sin"], cache_aux=t["aux"], eps=w.eps, stream=s)
 
     abytes = algorithmic_bytes(w)
     rbytes, wbytes = algorithmic_split(w)
@@ -582,23 +657,24 @@ def main():
     # the epilog's own warm-up (see the copy_ceiling entry of the line).
     cc = ceilings(dev, stream, abytes, rbytes, wbytes)
     pat = pattern_ceiling(w, dev, stream)
+    # the K timed launches, captured in one HIP graph (before the settle
+    # launches: the capture leaves the device idle and its clock low)
+    g_steps = capture(lambda: step(None), args.steps)
     st = settle(step, dev, stream, args.settle_ms) if args.settle_ms > 0 else None
 
-    for _ in range(args.warmup):
-        step()
+    host = time_host_launched(step, stream, args.warmup)
     torch.cuda.synchronize()
-    # HIP events on the launch stream around the K back-to-back launches:
-    # the host enqueues faster than the kernel runs, so the region is the
-    # kernels plus their dispatch gaps (an event between launches would
-    # add its own gap to every launch)
+    # HIP events on the launch stream around one replay of the graph: the K
+    # launches back to back, their dispatch gaps included, no host work
+    # between them
     total0 = torch.cuda.Event(enable_timing=True)
     total1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        total0.record(stream)
+        g_steps.replay()
+        total1.record(stream)
     torch.cuda.synchronize()
-    total0.record(stream)
-    for _ in range(args.steps):
-        step()
-    total1.record(stream)
-    torch.cuda.synchronize()
+    del g_steps
     ms_total = total0.elapsed_time(total1)
     ms_per_step = ms_total / args.steps
     ms_kernel = ms_per_step
@@ -627,6 +703,7 @@ def main():
                      "kernel_ms_mean": ms_kernel},
     }
     result["settle"] = dict(st or {"launches": 0, "ms": 0.0}, sclk_mhz_after_timed=sclk_after)
+    result["host_launched"] = host
     result["copy_ceiling"] = finish_ceiling(cc, achieved, stream, dev)
     if pat is not None:
         result["copy_ceiling"]["pattern"] = dict(
@@ -724,18 +801,19 @@ def main_drq(args):
     rbytes, wbytes = drq_algorithmic_split(w)
     # reference kernels first (they also bring the device out of idle)
     cc = ceilings(dev, stream, abytes, rbytes, wbytes)
+    g_steps = capture(lambda: B.kvepi_drq_run(p), args.steps)
     st = (settle(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream, args.settle_ms)
           if args.settle_ms > 0 else None)
-    for _ in range(args.warmup):
-        B.kvepi_drq_run(p, stream=stream)
+    host = time_host_launched(lambda: B.kvepi_drq_run(p, stream=stream), stream, args.warmup)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        B.kvepi_drq_run(p, stream=stream)
-    e1.record(stream)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g_steps.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
+    del g_steps
     ms = e0.elapsed_time(e1) / args.steps
     sclk_after = shader_clock_mhz(dev, stream)
     achieved = abytes / (ms * 1e-3) / 1e9
@@ -757,6 +835,7 @@ def main_drq(args):
                      "kernel_ms_mean": ms},
     }
     result["settle"] = dict(st or {"launches": 0, "ms": 0.0}, sclk_mhz_after_timed=sclk_after)
+    result["host_launched"] = host
     result["copy_ceiling"] = finish_ceiling(cc, achieved, stream, dev)
     ms_cold = cold_launches(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream)
     ms_single = cold_launches(lambda: B.kvepi_drq_run(p, stream=stream), dev, stream,

@@ -308,7 +308,11 @@ def drq_params(x, cos, sin, k_cache, v_cache, indices, *, nq: int, nkv: int, hea
                cache_mode: int = KVEPI_DRQ_PAGE, seq_len: int = 0) -> kvepi_drq_params:
     """torch tensors -> kvepi_drq_params (pointers, sizes and dtype codes).
     Checks what the pointers alone cannot carry: every tensor on x's device,
-    their dtypes and element counts (ValueError otherwise)."""
+    their dtypes and element counts (ValueError otherwise).  The returned
+    params hold references to the tensors: a launch made with them reads
+    device memory that stays allocated while the params are alive (the
+    pointers alone would not keep a temporary tensor's memory, which torch
+    may free and even return to the device, as a graph capture does)."""
     import torch
     _same_device(x, cos=cos, sin=sin, k_cache=k_cache, v_cache=v_cache, indices=indices,
                  scale_k=scale_k, scale_v=scale_v, q_out=q_out, k_out=k_out, v_out=v_out,
@@ -345,12 +349,15 @@ def drq_params(x, cos, sin, k_cache, v_cache, indices, *, nq: int, nkv: int, hea
             raise ValueError(f"{name} must be {dt} (got {t.dtype})")
         if t.numel() < n:
             raise ValueError(f"{name} must hold at least {n} values (got {t.numel()})")
-    return kvepi_drq_params(
+    params = kvepi_drq_params(
         _ptr(x), _dtype_code(x), _dtype_code(cos), x.shape[0], x.stride(0), nq, nkv, head_dim,
         _ptr(cos), _ptr(sin), _ptr(weight_scale), _ptr(act_scale), _ptr(bias),
         KVEPI_DT_FP32 if bias is None else _dtype_code(bias), _ptr(scale_k), _ptr(scale_v),
         _ptr(offset_k), _ptr(offset_v), _ptr(indices), cache_mode, seq_len,
         cache_desc(k_cache), cache_desc(v_cache), _ptr(q_out), _ptr(k_out), _ptr(v_out))
+    params._tensors = (x, cos, sin, k_cache, v_cache, indices, scale_k, scale_v, q_out, k_out,
+                       v_out, weight_scale, act_scale, bias, offset_k, offset_v)
+    return params
 
 
 def kvepi_drq_get_workspace(params: kvepi_drq_params) -> int:

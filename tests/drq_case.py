@@ -26,7 +26,7 @@ def run_oracle(c: DrqCase):
     return q, ko, vo, kc, vc
 
 
-def run_gpu(c: DrqCase, device="cuda:0"):
+def run_gpu(c: DrqCase, device="cuda:0", before_run=None):
     import torch
     from kv_cache_epilog_amd import binding as B
 
@@ -68,6 +68,8 @@ def run_gpu(c: DrqCase, device="cuda:0"):
                      bias=bias, offset_k=dev(c.offset_k), offset_v=dev(c.offset_v),
                      cache_mode=c.cache_mode, seq_len=c.seq_len)
     assert B.kvepi_drq_get_workspace(p) == 0
+    if before_run is not None:
+        before_run()
     B.kvepi_drq_run(p, device=device)
     torch.cuda.synchronize()
     as16 = lambda t: None if t is None else t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa

@@ -94,6 +94,21 @@ def test_drq_valid_arguments_pass():
         act_scale=t(32, dtype=torch.float32), bias=t(256, dtype=torch.bfloat16))
 
 
+def test_drq_params_hold_their_tensors():
+    # the params keep every tensor they point into alive, temporaries included
+    import gc
+    import weakref
+    sk = t(64, dtype=torch.float32)
+    ref = weakref.ref(sk)
+    p = drq(scale_k=sk)
+    del sk
+    gc.collect()
+    assert ref() is not None and any(x is ref() for x in p._tensors)
+    del p
+    gc.collect()
+    assert ref() is None
+
+
 @pytest.mark.parametrize("kw", [
     dict(x=t(32, 256, dtype=torch.int32, device="cpu")),
     dict(scale_k=t(64, dtype=torch.float32, device="cpu")),

@@ -46,6 +46,10 @@ def _check(d, steps, warmup):
     assert c["mix"] in ("1:1", "2:1", "4:1") and c["empty_launch_us"] > 0
     assert r["algorithmic_read_bytes"] + r["algorithmic_write_bytes"] == \
         r["algorithmic_bytes_per_launch"]
+    # the warm-up launches from the host; the timed region is a graph replay
+    h = d["host_launched"]
+    assert h["launches"] == warmup and h["ms_per_launch"] > 0
+    assert d["cold"]["ms_per_launch_unscrubbed"] > 0
 
 
 def test_epilog_bench_line():

@@ -196,3 +196,17 @@ def test_int32_many_units_per_thread(monkeypatch, blocks, k, out):
     monkeypatch.setenv("KVEPI_DRQ_MAX_BLOCKS", str(blocks))
     c = make_case(1100 + 10 * k + out, x_dtype=I32, out_dtype=out, **_MANY[k])
     compare(c, f"int32, {blocks} blocks, case {k}")
+
+
+def test_params_keep_their_tensors():
+    # run_gpu passes temporaries (cos, sin, indices, scales, ...) straight
+    # into drq_params; the params hold them, so freeing torch's cached blocks
+    # back to the device before the launch (as a graph capture does) leaves
+    # the launch's inputs allocated
+    import torch
+    from drq_case import run_gpu, run_oracle
+    c = make_case(1200, T=200, nq=4, nkv=2, D=64, x_dtype=I32, out_dtype=BF, bias_dtype=F32)
+    got = run_gpu(c, before_run=lambda: (__import__("gc").collect(), torch.cuda.empty_cache()))
+    want = run_oracle(c)
+    for g, w in zip(got, want):
+        assert (g is None and w is None) or np.array_equal(g, w)
