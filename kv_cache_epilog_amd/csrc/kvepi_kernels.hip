@@ -1684,10 +1684,15 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
     const long v = strtol(cap, nullptr, 10);
     if (v >= 4 && v < max_waves) max_waves = v & ~3L;
   }
-  // at least two iterations per wave, so that every wave's loads of its
-  // second iteration overlap its first (short launches measured 15-20 %
-  // faster than with one iteration per wave)
-  const int64_t waves = n_groups >= 2 * max_waves ? max_waves : (n_groups + 1) / 2;
+  // Two iterations per wave, so that every wave's loads of its second
+  // iteration overlap its first: with 2048 to 16384 row groups (up to 8 per
+  // SIMD) that measured 7-20 % faster than one iteration per wave.  With no
+  // more row groups than SIMDs, one iteration per wave spreads them over
+  // more SIMDs and measured 6-15 % faster (launches timed as HIP-graph
+  // replays, 128 to 2048 tokens).
+  const int64_t simds = (int64_t)cus * 4;
+  const int64_t waves = n_groups <= simds ? (n_groups < max_waves ? n_groups : max_waves)
+                        : n_groups >= 2 * max_waves ? max_waves : (n_groups + 1) / 2;
   const int64_t blocks = (waves + 3) / 4;
   a.nwaves = (int32_t)(blocks * 4);
   a.n_groups = (int32_t)n_groups;
