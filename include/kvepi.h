@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVEPI_VERSION 130 /* 1.3.0: mode 7 (quantMode 2's FP4 nope segment) */
+#define KVEPI_VERSION 140 /* 1.4.0: prepared calls (kvepi_prepare_ex) */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KVEPI_API __attribute__((visibility("default")))
@@ -302,6 +302,58 @@ KVEPI_API kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d
                           const kvepi_cache *cache_aux, int32_t quant_mode,
                           int32_t group_size, float eps, const kvepi_options *options,
                           void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* ---- prepared calls (version 1.4) ----------------------------------------
+ *
+ * For callers that launch the same call again and again over fixed buffers
+ * (a serving loop that refills its x and slot_mapping buffers every step):
+ * kvepi_prepare_ex does the work of a kvepi_run_ex call that does not depend
+ * on the buffers' contents once -- the validation, the choice of kernel and
+ * its grid on the current device -- and stores it in a caller-owned
+ * kvepi_prepared; kvepi_run_prepared then only checks the device and
+ * enqueues the kernel.  A run of a prepared call writes exactly what
+ * kvepi_run_ex with the same arguments writes for the buffers' contents at
+ * the time the kernel executes.
+ *
+ *  kvepi_prepare_ex  takes the arguments of kvepi_get_workspace_ex (the
+ *        workspace size is 0 for every call, so there is no out-parameter)
+ *        and a HOST pointer to the kvepi_prepared to fill.  It returns what
+ *        kvepi_get_workspace_ex returns for the same arguments; then, for
+ *        num_tokens > 0, it reads the current HIP device (KVEPI_ERR_RUNTIME
+ *        if that fails) and the KVEPI_MAX_WAVES cap described at kvepi_run.
+ *        It launches nothing and never synchronises.  On any error status
+ *        *prepared is marked invalid.
+ *  kvepi_run_prepared  enqueues a prepared call on `stream` (as kvepi_run).
+ *        KVEPI_ERR_NULLPTR for a NULL prepared, KVEPI_ERR_PARAM for a struct
+ *        that kvepi_prepare_ex did not fill with KVEPI_OK, or when the
+ *        current HIP device is not the one that was current at preparation;
+ *        KVEPI_ERR_RUNTIME if the launch is refused.  A prepared call of 0
+ *        tokens is a no-op.  The KVEPI_CHECK_SLOTS debug check is applied at
+ *        every run, as in kvepi_run.
+ *
+ * Ownership.  The kvepi_prepared belongs to the caller; it holds the device
+ * pointers it was prepared with and nothing else (no allocation, no pointer
+ * into itself): it may be copied bytewise, used from several threads at
+ * once, and dropped without any call.  Those buffers must stay allocated,
+ * at the same addresses, for as long as the prepared call is run; their
+ * contents may change between runs (the stream orders the kernel after the
+ * writes enqueued before it, as for any launch).
+ */
+#define KVEPI_PREPARED_BYTES 1024
+
+typedef struct kvepi_prepared {
+  uint64_t opaque[KVEPI_PREPARED_BYTES / 8];
+} kvepi_prepared;
+
+KVEPI_API kvepi_status kvepi_prepare_ex(const void *x, int64_t num_tokens, int64_t d,
+                              int64_t x_row_stride, const void *gamma,
+                              const void *cos, const void *sin,
+                              const int32_t *slot_mapping, const kvepi_cache *cache,
+                              const kvepi_cache *cache_aux, int32_t quant_mode,
+                              int32_t group_size, float eps, const kvepi_options *options,
+                              kvepi_prepared *prepared);
+
+KVEPI_API kvepi_status kvepi_run_prepared(const kvepi_prepared *prepared, void *stream);
 
 /* Static text for a status code (never NULL). */
 KVEPI_API const char *kvepi_status_str(kvepi_status status);

@@ -10,6 +10,7 @@ from .binding import (KVEPI_MODE_BF16_SPLIT, KVEPI_MODE_FP8_BF16SCALE, KVEPI_MOD
                       KVEPI_DT_FP32, KVEPI_DT_INT32, drq_params, kvepi_drq_get_workspace,
                       kvepi_drq_params, kvepi_drq_run, KvepiError, cache_desc, kvepi_options,
                       kvepi_cache, kvepi_get_workspace, kvepi_row_bytes, kvepi_run,
+                      KvepiPrepared, kvepi_prepare, kvepi_prepared, kvepi_run_prepared,
                       kvepi_status_str, kvepi_version, lib)
 
 __all__ = ["KVEPI_MODE_BF16_SPLIT", "KVEPI_MODE_FP8_BF16SCALE", "KVEPI_MODE_FP8_E8M0",
@@ -19,4 +20,5 @@ __all__ = ["KVEPI_MODE_BF16_SPLIT", "KVEPI_MODE_FP8_BF16SCALE", "KVEPI_MODE_FP8_
            "KVEPI_DRQ_PAGE", "KVEPI_DT_BF16", "KVEPI_DT_FP16", "KVEPI_DT_FP32", "KVEPI_DT_INT32",
            "drq_params", "kvepi_drq_get_workspace", "kvepi_drq_params", "kvepi_drq_run",
            "KvepiError", "cache_desc", "kvepi_cache", "kvepi_get_workspace", "kvepi_row_bytes",
-           "kvepi_run", "kvepi_status_str", "kvepi_version", "lib"]
+           "kvepi_run", "KvepiPrepared", "kvepi_prepare", "kvepi_prepared",
+           "kvepi_run_prepared", "kvepi_status_str", "kvepi_version", "lib"]

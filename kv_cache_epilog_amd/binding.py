@@ -56,6 +56,10 @@ class kvepi_options(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class kvepi_prepared(ctypes.Structure):
+    _fields_ = [("opaque", ctypes.c_uint64 * 128)]  # KVEPI_PREPARED_BYTES
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -84,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.kvepi_run_ex.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F, OP, P,
                                    ctypes.c_uint64, P]
         L.kvepi_run_ex.restype = ctypes.c_int
+        PP = ctypes.POINTER(kvepi_prepared)
+        L.kvepi_prepare_ex.argtypes = [P, I64, I64, I64, P, P, P, P, CP, CP, I32, I32, F, OP,
+                                       PP]
+        L.kvepi_prepare_ex.restype = ctypes.c_int
+        L.kvepi_run_prepared.argtypes = [PP, P]
+        L.kvepi_run_prepared.restype = ctypes.c_int
         L.kvepi_status_str.argtypes = [ctypes.c_int]
         L.kvepi_status_str.restype = ctypes.c_char_p
         L.kvepi_version.argtypes = []
@@ -256,6 +266,55 @@ def kvepi_run(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
                             ctypes.c_void_p(stream.cuda_stream))
     if st != KVEPI_OK:
         raise KvepiError(st, "kvepi_run")
+
+
+class KvepiPrepared:
+    """A prepared epilog call (kvepi_prepare_ex): the C struct, the torch
+    device and references to the tensors it was prepared with, which keeps
+    their memory allocated (at the same addresses) while it is alive."""
+
+    __slots__ = ("struct", "ref", "device", "tensors")
+
+    def __init__(self, struct, device, tensors):
+        self.struct = struct
+        self.ref = ctypes.byref(struct)
+        self.device = device
+        self.tensors = tensors
+
+
+def kvepi_prepare(x, slot_mapping, cache, quant_mode: int, group_size: int = 64, *,
+                  gamma=None, cos=None, sin=None, cache_aux=None, eps: float = 1e-6,
+                  index_mode: int = KVEPI_INDEX_SLOT, seq_len: int = 0,
+                  rope_dim: int = 0) -> KvepiPrepared:
+    """Validates a kvepi_run call once and works out its launch on the
+    current device (kvepi_prepare_ex); kvepi_run_prepared then enqueues it.
+    The same checks as kvepi_run, ValueError or KvepiError otherwise.  The
+    tensors' contents may change between runs; the tensors themselves are
+    fixed (a run reads and writes the memory they had at preparation)."""
+    import torch
+    args, _keep = _args(x, slot_mapping, cache, quant_mode, group_size, gamma, cos, sin,
+                        cache_aux, eps, index_mode, seq_len, rope_dim)
+    opt = _options(x, index_mode, seq_len, rope_dim)
+    prep = kvepi_prepared()
+    with torch.cuda.device(x.device):
+        st = lib().kvepi_prepare_ex(*args, ctypes.byref(opt), ctypes.byref(prep))
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_prepare_ex")
+    return KvepiPrepared(prep, x.device, (x, slot_mapping, cache, gamma, cos, sin, cache_aux))
+
+
+def kvepi_run_prepared(prepared: KvepiPrepared, stream=None) -> None:
+    """Enqueue a prepared call on `stream` (a torch.cuda.Stream; default:
+    torch's current stream on the prepared call's device).  The host's work
+    per call is this one C call: no argument is validated or converted
+    again.  Raises KvepiError on a rejected call (another current device
+    than at preparation, or a refused launch)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream(prepared.device)
+    st = (_lib or lib()).kvepi_run_prepared(prepared.ref, stream.cuda_stream)
+    if st != KVEPI_OK:
+        raise KvepiError(st, "kvepi_run_prepared")
 
 
 # ---- dequant -> RoPE -> int8 KV cache (include/kvepi_drq.h) -------------------------

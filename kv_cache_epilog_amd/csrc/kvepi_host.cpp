@@ -1,10 +1,12 @@
-// kvepi_host.cpp -- argument validation, row geometry and the two-stage C ABI
-// of the fused KV-cache write epilog.  Pure host code: no call in this file
-// touches the GPU, so every check can run (and be tested) without one (the
-// optional duplicate-slot check that kvepi_run calls lives in
-// kvepi_debug.cpp).
+// kvepi_host.cpp -- argument validation, row geometry, the two-stage C ABI
+// of the fused KV-cache write epilog and its prepared calls.  Pure host
+// code: the GPU is reached only through the launcher and the device query
+// of kvepi_kernels.hip and the optional duplicate-slot check of
+// kvepi_debug.cpp, each after every check has passed, so every check can run
+// (and be tested) without a GPU.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "kvepi.h"
 #include "kvepi_plan.h"
@@ -23,6 +25,19 @@ int32_t pow2_align(uint64_t v) {
 }
 
 int32_t min_align(int32_t a, int32_t b) { return a < b ? a : b; }
+
+// What a kvepi_prepared holds: the validated plan and its launch.
+constexpr uint64_t PREPARED_MAGIC = 0x3172706970657624ull;
+struct prepared_state {
+  uint64_t magic;        // PREPARED_MAGIC once kvepi_prepare_ex returned KVEPI_OK
+  uint64_t state_bytes;  // sizeof(prepared_state) of the library that wrote it
+  kvepi_plan plan;
+  kvepi_launch_cfg cfg;  // meaningful for plan.T > 0
+};
+static_assert(sizeof(prepared_state) <= sizeof(kvepi_prepared),
+              "kvepi_prepared must hold a prepared_state");
+static_assert(alignof(prepared_state) <= alignof(kvepi_prepared),
+              "kvepi_prepared must be aligned for a prepared_state");
 
 // Row geometry ("aclnnKvCompressEpilog" 约束说明 headDim rule;
 // "indexer_quant_cache" 约束 headDim/scaleCol rule).
@@ -278,6 +293,47 @@ kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d,
   st = kvepi_debug_check_slots(plan, slot_mapping, stream);
   if (st != KVEPI_OK) return st;
   return kvepi_launch(plan, stream);
+}
+
+kvepi_status kvepi_prepare_ex(const void *x, int64_t num_tokens, int64_t d,
+                              int64_t x_row_stride, const void *gamma,
+                              const void *cos, const void *sin,
+                              const int32_t *slot_mapping, const kvepi_cache *cache,
+                              const kvepi_cache *cache_aux, int32_t quant_mode,
+                              int32_t group_size, float eps, const kvepi_options *options,
+                              kvepi_prepared *prepared) {
+  if (prepared == nullptr) return KVEPI_ERR_NULLPTR;
+  memset(prepared, 0, sizeof *prepared);  // invalid unless every step succeeds
+  prepared_state ps;
+  memset(&ps, 0, sizeof ps);
+  kvepi_status st =
+      kvepi_validate(x, num_tokens, d, x_row_stride, gamma, cos, sin,
+                     slot_mapping, cache, cache_aux, quant_mode, group_size,
+                     eps, options, &ps.plan);
+  if (st != KVEPI_OK) return st;
+  if (ps.plan.T > 0) {
+    st = kvepi_configure(ps.plan, &ps.cfg);
+    if (st != KVEPI_OK) return st;
+  }
+  ps.magic = PREPARED_MAGIC;
+  ps.state_bytes = sizeof ps;
+  memcpy(prepared, &ps, sizeof ps);
+  return KVEPI_OK;
+}
+
+kvepi_status kvepi_run_prepared(const kvepi_prepared *prepared, void *stream) {
+  if (prepared == nullptr) return KVEPI_ERR_NULLPTR;
+  prepared_state ps;
+  memcpy(&ps, prepared, sizeof ps);
+  if (ps.magic != PREPARED_MAGIC || ps.state_bytes != sizeof ps) return KVEPI_ERR_PARAM;
+  if (ps.plan.T == 0) return KVEPI_OK;
+  int32_t dev = -1;
+  kvepi_status st = kvepi_current_device(&dev);
+  if (st != KVEPI_OK) return st;
+  if (dev != ps.cfg.device) return KVEPI_ERR_PARAM;
+  st = kvepi_debug_check_slots(ps.plan, ps.plan.slots, stream);
+  if (st != KVEPI_OK) return st;
+  return kvepi_enqueue(ps.cfg, stream);
 }
 
 kvepi_status kvepi_get_workspace(const void *x, int64_t num_tokens, int64_t d,

@@ -56,6 +56,7 @@
 #include <stdint.h>
 
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -1588,8 +1589,13 @@ int blocks_per_cu(kfn_t fn, size_t lds) {
 
 }  // namespace kvepi
 
-kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
+static_assert(sizeof(kvepi::KArgs) <= KVEPI_KARGS_BYTES && alignof(kvepi::KArgs) <= 8,
+              "the kernel arguments must fit kvepi_launch_cfg::args");
+
+kvepi_status kvepi_configure(const kvepi_plan &p, kvepi_launch_cfg *cfg) {
   using namespace kvepi;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVEPI_ERR_RUNTIME;
   KArgs a{};
   a.x = p.x;
   a.gamma = p.gamma;
@@ -1697,8 +1703,33 @@ kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
   a.nwaves = (int32_t)(blocks * 4);
   a.n_groups = (int32_t)n_groups;
 
-  void *args[] = {&a};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)blocks),
-                                 dim3(256), args, lds, static_cast<hipStream_t>(stream));
+  *cfg = kvepi_launch_cfg{};
+  cfg->fn = reinterpret_cast<const void *>(fn);
+  cfg->blocks = (uint32_t)blocks;
+  cfg->lds = (uint32_t)lds;
+  cfg->device = dev;
+  memcpy(cfg->args, &a, sizeof a);
+  return KVEPI_OK;
+}
+
+kvepi_status kvepi_enqueue(const kvepi_launch_cfg &cfg, void *stream) {
+  // the kernel takes its KArgs by value: HIP copies sizeof(KArgs) bytes from
+  // the address given for argument 0
+  void *args[] = {const_cast<unsigned char *>(cfg.args)};
+  hipError_t e = hipLaunchKernel(cfg.fn, dim3(cfg.blocks), dim3(256), args, cfg.lds,
+                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVEPI_OK : KVEPI_ERR_RUNTIME;
+}
+
+kvepi_status kvepi_current_device(int32_t *device) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVEPI_ERR_RUNTIME;
+  *device = dev;
+  return KVEPI_OK;
+}
+
+kvepi_status kvepi_launch(const kvepi_plan &p, void *stream) {
+  kvepi_launch_cfg cfg;
+  const kvepi_status st = kvepi_configure(p, &cfg);
+  return st != KVEPI_OK ? st : kvepi_enqueue(cfg, stream);
 }

@@ -42,8 +42,28 @@ kvepi_status kvepi_validate(const void *x, int64_t num_tokens, int64_t d,
                             int32_t group_size, float eps, const kvepi_options *options,
                             kvepi_plan *plan);
 
-// Enqueue the kernel for a validated plan (T > 0).
+// A launch worked out from a validated plan on the current device: the
+// kernel instance, its grid and LDS bytes, and the kernel's argument block
+// as plain bytes (so that host-only files need no device types).  It holds
+// no pointer into itself and may be copied bytewise.
+#define KVEPI_KARGS_BYTES 256
+struct kvepi_launch_cfg {
+  const void *fn;
+  uint32_t blocks;
+  uint32_t lds;
+  int32_t device;  // the HIP device current when the launch was worked out
+  int32_t reserved;
+  alignas(8) unsigned char args[KVEPI_KARGS_BYTES];
+};
+
+// Works out the launch of a validated plan (T > 0) on the current device.
+kvepi_status kvepi_configure(const kvepi_plan &plan, kvepi_launch_cfg *cfg);
+// Enqueues a launch worked out by kvepi_configure.
+kvepi_status kvepi_enqueue(const kvepi_launch_cfg &cfg, void *stream);
+// Both of the above: enqueue the kernel for a validated plan (T > 0).
 kvepi_status kvepi_launch(const kvepi_plan &plan, void *stream);
+// The current HIP device (KVEPI_ERR_RUNTIME if it cannot be read).
+kvepi_status kvepi_current_device(int32_t *device);
 // The optional duplicate-slot check (KVEPI_CHECK_SLOTS; kvepi_debug.cpp):
 // KVEPI_OK unless it is enabled and two tokens name the same row.
 kvepi_status kvepi_debug_check_slots(const kvepi_plan &plan, const int32_t *slot_mapping,

@@ -252,10 +252,20 @@ def epilog(mode: int, x, slot_mapping, cache_bytes, cache_geom, *, group_size: i
     gamma = None if gamma is None else _c(gamma, np.uint16)
     cos = None if cos is None else _c(cos, np.uint16)
     sin = None if sin is None else _c(sin, np.uint16)
+    # the buffers must hold every row of their geometry (elements of 2
+    # bytes for the split mode's caches, 4 for the per-row FP8 scales)
+    def span(g):
+        bn, bs, hd, stride = (int(v) for v in g)
+        return (bn - 1) * stride + bs * hd if bn > 0 else 0
+
+    esz = 2 if mode == MODE_BF16_SPLIT else 1
+    assert cache_bytes.size >= span(cache_geom) * esz
     c = _Cache(cache_bytes.ctypes.data, *[int(v) for v in cache_geom])
     a = None
     if aux_bytes is not None:
         assert aux_bytes.dtype == np.uint8 and aux_bytes.flags.c_contiguous
+        aesz = {MODE_BF16_SPLIT: 2, MODE_FP8_ROW: 4}.get(mode, 1)
+        assert aux_bytes.size >= span(aux_geom) * aesz
         a = _Cache(aux_bytes.ctypes.data, *[int(v) for v in aux_geom])
     rc = lib().kvo_epilog_ex(mode, T, d, x.ctypes.data_as(ctypes.c_void_p),
                              x.strides[0] // 2, int(x_fp16), _ptr(gamma), _ptr(cos),

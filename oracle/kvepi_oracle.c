@@ -586,6 +586,18 @@ int kvo_epilog_ex(int mode, int64_t T, int64_t d, const uint16_t *x, int64_t x_r
   if (mode == KVO_MODE_FP4_NOPE && (cos || aux)) return -1; /* rope bytes not written */
   if ((indexer || mode == KVO_MODE_BF16_SPLIT) && !aux) return -1;
   if (x_fp16 && !indexer) return -1;
+  /* every row written must fit its cache row, and the rows of a block its
+   * block: headDim >= kvCacheCol ("aclnnKvCompressEpilog", 约束说明;
+   * "indexer_quant_cache", 约束 for cache_scale); in the split mode the ckv
+   * rows hold Dv and the k rows Dk bf16 elements */
+  if (!cache || cache->head_dim < kc || cache->block_stride < cache->block_size * cache->head_dim)
+    return -1;
+  if (aux) {
+    const int64_t need = mode == KVO_MODE_FP8_ROW ? 1 : sc;
+    if (aux->head_dim < need || aux->block_stride < aux->block_size * aux->head_dim ||
+        aux->block_num != cache->block_num || aux->block_size != cache->block_size)
+      return -1;
+  }
   const int64_t dk = rope_dim;
   int64_t nope = d - dk;
   uint16_t *v = (uint16_t *)malloc((size_t)d * sizeof(uint16_t));

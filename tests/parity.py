@@ -46,10 +46,13 @@ def cache_tensor(spec: kvgen.CacheSpec, init: np.ndarray, device, offset: int = 
 
 
 def run_gpu(w: kvgen.Workload, device="cuda:0", offset: int = 0, aux_offset: int = 0,
-            x_pad: int = 0, stream=None, repeat: int = 1):
-    """Runs the HIP path; returns (cache_bytes, aux_bytes) as numpy arrays."""
+            x_pad: int = 0, stream=None, repeat: int = 1, prepared: bool = False):
+    """Runs the HIP path; returns (cache_bytes, aux_bytes) as numpy arrays.
+    prepared: through kvepi_prepare / kvepi_run_prepared instead of
+    kvepi_run."""
     torch = _torch()
-    from kv_cache_epilog_amd import kvepi_get_workspace, kvepi_run
+    from kv_cache_epilog_amd import (kvepi_get_workspace, kvepi_prepare, kvepi_run,
+                                     kvepi_run_prepared)
     if x_pad:
         xb = np.zeros((w.T, w.d + x_pad), np.uint16)
         xb[:, :w.d] = w.x
@@ -72,9 +75,15 @@ def run_gpu(w: kvgen.Workload, device="cuda:0", offset: int = 0, aux_offset: int
     ws = kvepi_get_workspace(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos,
                              sin=sin, cache_aux=aux, eps=w.eps, **ix)
     assert ws == 0
+    if prepared:
+        prep = kvepi_prepare(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos,
+                             sin=sin, cache_aux=aux, eps=w.eps, **ix)
     for _ in range(repeat):
-        kvepi_run(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos, sin=sin,
-                  cache_aux=aux, eps=w.eps, stream=stream, **ix)
+        if prepared:
+            kvepi_run_prepared(prep, stream=stream)
+        else:
+            kvepi_run(x, slots, cache, w.mode, w.group_size, gamma=gamma, cos=cos, sin=sin,
+                      cache_aux=aux, eps=w.eps, stream=stream, **ix)
     torch.cuda.synchronize()
     got = flat[offset:offset + w.cache.alloc_bytes].cpu().numpy()
     # bytes outside the cache view must be untouched as well

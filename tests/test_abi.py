@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kvepi_row_bytes", "kvepi_get_workspace", "kvepi_run",
                           "kvepi_get_workspace_ex", "kvepi_run_ex", "kvepi_status_str",
-                          "kvepi_version", "kvepi_drq_get_workspace", "kvepi_drq_run"}
+                          "kvepi_version", "kvepi_drq_get_workspace", "kvepi_drq_run",
+                          "kvepi_prepare_ex", "kvepi_run_prepared"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -40,7 +41,7 @@ def test_only_the_c_abi_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.kvepi_version() == 130
+    assert B.kvepi_version() == 140
     for code, name in B.STATUS_NAMES.items():
         assert B.kvepi_status_str(code).startswith(name)
     assert "UNKNOWN" in B.kvepi_status_str(99)
@@ -98,6 +99,13 @@ def call(stage, *, x=P16, T=64, d=256, xs=None, gamma=None, cos=None, sin=None, 
         st = L.kvepi_get_workspace(x, T, d, xs, gamma, cos, sin, slots, cp, ap, mode, group,
                                    ctypes.c_float(eps), ctypes.byref(ws))
         return st, ws.value
+    if stage == 3:
+        # kvepi_prepare_ex: the checks of stage one, then the device query
+        prep = B.kvepi_prepared()
+        prep.opaque[0] = 0xFFFF  # overwritten: invalid unless KVEPI_OK
+        st = L.kvepi_prepare_ex(x, T, d, xs, gamma, cos, sin, slots, cp, ap, mode, group,
+                                ctypes.c_float(eps), None, ctypes.byref(prep))
+        return st, prep
     # stage 2: a valid call would launch -- only invalid calls are made here
     st = L.kvepi_run(x, T, d, xs, gamma, cos, sin, slots, cp, ap, mode, group,
                      ctypes.c_float(eps), None, ws_bytes, None)
@@ -190,10 +198,14 @@ BAD = [
 
 
 @pytest.mark.parametrize("desc,kw,status", BAD, ids=[b[0] for b in BAD])
-@pytest.mark.parametrize("stage", [1, 2])
+@pytest.mark.parametrize("stage", [1, 2, 3])
 def test_rejects(desc, kw, status, stage):
-    st, _ = call(stage, **kw)
+    st, prep = call(stage, **kw)
     assert st == status, (desc, B.kvepi_status_str(st))
+    if stage == 3:
+        # a rejected preparation leaves a struct that kvepi_run_prepared refuses
+        assert not any(prep.opaque)
+        assert B.lib().kvepi_run_prepared(ctypes.byref(prep), None) == 4
 
 
 def test_workspace_out_pointer_required():
@@ -234,6 +246,11 @@ def call_ex(stage, opt, **kw):
                                       ap, mode, group, ctypes.c_float(1e-6), op,
                                       ctypes.byref(ws))
         return st, ws.value
+    if stage == 3:
+        prep = B.kvepi_prepared()
+        st = L.kvepi_prepare_ex(x, T, d, d, gamma, cos, sin, slots, ctypes.byref(cache), ap,
+                                mode, group, ctypes.c_float(1e-6), op, ctypes.byref(prep))
+        return st, prep
     st = L.kvepi_run_ex(x, T, d, d, gamma, cos, sin, slots, ctypes.byref(cache), ap, mode,
                         group, ctypes.c_float(1e-6), op, None, 0, None)
     return st, None
@@ -287,7 +304,7 @@ BAD_EX = [
 
 
 @pytest.mark.parametrize("desc,opt,kw,status", BAD_EX, ids=[b[0] for b in BAD_EX])
-@pytest.mark.parametrize("stage", [1, 2])
+@pytest.mark.parametrize("stage", [1, 2, 3])
 def test_ex_rejects(desc, opt, kw, status, stage):
     st, _ = call_ex(stage, opt, **kw)
     assert st == status, (desc, B.kvepi_status_str(st))
@@ -312,3 +329,45 @@ def test_slot_check_without_a_device_reports_runtime_error(monkeypatch):
         pytest.skip("a GPU is present")
     monkeypatch.setenv("KVEPI_CHECK_SLOTS", "1")
     assert call(2) == (7, None)
+
+
+# ---- prepared calls ----------------------------------------------------------
+
+def test_prepare_needs_its_out_pointer():
+    L = B.lib()
+    c = _cache()
+    assert L.kvepi_prepare_ex(P16, 64, 256, 256, None, None, None, P16B, ctypes.byref(c), None,
+                              0, 64, ctypes.c_float(1e-6), None, None) == 1
+
+
+def test_run_prepared_refuses_null_and_unprepared_structs():
+    L = B.lib()
+    assert L.kvepi_run_prepared(None, None) == 1
+    prep = B.kvepi_prepared()
+    assert L.kvepi_run_prepared(ctypes.byref(prep), None) == 4
+    for i in range(len(prep.opaque)):
+        prep.opaque[i] = 0x0123456789ABCDEF
+    assert L.kvepi_run_prepared(ctypes.byref(prep), None) == 4
+
+
+def test_prepared_empty_call_runs_as_a_no_op():
+    # num_tokens == 0 needs no device: prepared and run without one
+    st, prep = call(3, T=0, x=None, slots=None)
+    assert st == 0 and any(prep.opaque)
+    assert B.lib().kvepi_run_prepared(ctypes.byref(prep), None) == 0
+    st, prep = call_ex(3, O(index_mode=1, seq_len=1), T=0, x=None, slots=None)
+    assert st == 0
+    assert B.lib().kvepi_run_prepared(ctypes.byref(prep), None) == 0
+    # a bytewise copy is as good as the original
+    copy = B.kvepi_prepared.from_buffer_copy(prep)
+    assert B.lib().kvepi_run_prepared(ctypes.byref(copy), None) == 0
+
+
+def test_valid_prepare_without_a_device_reports_runtime_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, prep = call(3)
+    assert st == 7 and not any(prep.opaque)
+    st, prep = call_ex(3, O(index_mode=2, seq_len=8))
+    assert st == 7

@@ -126,3 +126,13 @@ def test_drq_params_hold_their_tensors():
 def test_drq_misuse_raises(kw):
     with pytest.raises(ValueError):
         drq(**kw)
+
+
+@pytest.mark.parametrize("kw", [dict(x=t(64, 576, device="cpu")),
+                                dict(slot_mapping=t(63, dtype=torch.int32))])
+def test_prepare_checks_as_run(kw):
+    # kvepi_prepare shares kvepi_run's checks: they raise before any call
+    a = args(**kw)
+    with pytest.raises(ValueError):
+        B.kvepi_prepare(a.pop("x"), a.pop("slot_mapping"), a.pop("cache"), a.pop("quant_mode"),
+                        a.pop("group_size"), **a)

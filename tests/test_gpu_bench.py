@@ -55,6 +55,7 @@ def _check(d, steps, warmup):
 def test_epilog_bench_line():
     d = _run("--config", "0", "--steps", "3", "--warmup", "2")
     _check(d, 3, 2)
+    assert d["host_launched"]["prepared_ms_per_launch"] > 0
     assert d["config"]["workload"] == "mode0_tiny_d256"
     assert d["metric"].endswith("mode0_tiny_d256")
     pat = d["copy_ceiling"]["pattern"]

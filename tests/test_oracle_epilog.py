@@ -154,3 +154,24 @@ def test_rejects_bad_args(mode):
         oracle.epilog(mode, w.x, w.slots, w.cache_init.copy(), w.cache.geom,
                       group_size=16, aux_bytes=None if w.aux is None else w.aux_init.copy(),
                       aux_geom=None if w.aux is None else w.aux.geom)
+
+
+@pytest.mark.parametrize("mode,d,group,head,aux_head,ok", [
+    (7, 576, 16, 384, None, True), (7, 576, 16, 383, None, False),  # kvCacheCol 384
+    (0, 576, 64, 672, None, True), (0, 576, 64, 656, None, False),  # 656 -> 672 with padding
+    (3, 128, 32, 64, 4, True), (3, 128, 32, 63, 4, False), (3, 128, 32, 64, 3, False),
+])
+def test_rejects_rows_wider_than_the_cache(mode, d, group, head, aux_head, ok):
+    # headDim >= kvCacheCol ("aclnnKvCompressEpilog", 约束说明; "indexer_quant_cache",
+    # 约束): a narrower cache is refused, never written past its rows
+    aux = None if aux_head is None else CacheSpec(4, 16, aux_head, 16 * aux_head)
+    w = small(mode, 20, d, seed=2, cache=CacheSpec(4, 16, head, 16 * head), aux=aux,
+              group_size=group)
+    args = (mode, w.x, w.slots, w.cache_init.copy(), w.cache.geom)
+    kw = dict(group_size=group, aux_bytes=None if aux is None else w.aux_init.copy(),
+              aux_geom=None if aux is None else aux.geom)
+    if ok:
+        oracle.epilog(*args, **kw)
+    else:
+        with pytest.raises(ValueError):
+            oracle.epilog(*args, **kw)

@@ -57,7 +57,7 @@ def test_split_mode_closed_forms(dk):
 
 def test_rope_dim_rejections():
     x = np.zeros((1, 96), np.uint16)
-    c = np.zeros(8 * 64, np.uint8)
+    c = np.zeros(8 * 64 * 2, np.uint8)  # 8 rows of 64 bf16
     a = np.zeros(8 * 64, np.uint8)
     g = np.zeros(64, np.uint16)
     cs = np.zeros((1, 32), np.uint16)
