@@ -88,7 +88,27 @@ def build_hw_check(verbose: bool = False) -> str:
     return HW_CHECK_BIN
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client.c")
+C_CLIENT_BIN = os.path.join(ROOT, "tests", "c_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Builds tests/c_client, a plain C11 program (gcc, no C++) that drives
+    the epilog through include/kvepi.h and the HIP runtime's C API only,
+    linked against the in-tree libkvepi.so (run by a GPU test)."""
+    tmp = C_CLIENT_BIN + ".tmp"
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), "-o", tmp, C_CLIENT_SRC,
+           "-L", PKG, "-lkvepi", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../kv_cache_epilog_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    _run(cmd, verbose)
+    os.replace(tmp, C_CLIENT_BIN)
+    return C_CLIENT_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_ceiling(verbose=True))
     print(build_hw_check(verbose=True))
+    print(build_c_client(verbose=True))

@@ -371,3 +371,17 @@ def test_valid_prepare_without_a_device_reports_runtime_error():
     assert st == 7 and not any(prep.opaque)
     st, prep = call_ex(3, O(index_mode=2, seq_len=8))
     assert st == 7
+
+
+@pytest.mark.parametrize("header", ["kvepi.h", "kvepi_drq.h"])
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c", "-std=c11"), ("c++", "-std=c++11")])
+def test_headers_compile_as_strict_c_and_cxx(header, lang, std, tmp_path):
+    # the ABI headers are plain C: no HIP or torch types, no compiler extensions
+    import subprocess
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text(f'#include "{header}"\n#include "{header}"\nint main(void) {{ return 0; }}\n')
+    cc = "gcc" if lang == "c" else "g++"
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -197,3 +197,25 @@ def test_prepared_grid_is_fixed_at_preparation(monkeypatch):
     want, _ = run_oracle(w)
     got, _ = _got(w, t)
     assert np.array_equal(got, want)
+
+
+# ---- the seeded random workloads of the other parity files, prepared ------------
+
+@pytest.mark.parametrize("k", range(0, 160, 4))
+def test_prepared_fuzz(k):
+    from test_gpu_parity import _fuzz_case
+    w, kw = _fuzz_case(k)
+    assert check(w, f"prepared fuzz {k}: {w.name}", prepared=True, repeat=2, **kw) == 0
+
+
+@pytest.mark.parametrize("k", range(0, 60, 3))
+def test_prepared_index_fuzz(k):
+    from test_gpu_options import _index_fuzz_case
+    check(_index_fuzz_case(k), f"prepared index fuzz {k}", prepared=True)
+
+
+@pytest.mark.parametrize("k", range(0, 30, 3))
+def test_prepared_rope_length_fuzz(k):
+    from test_gpu_options import _rope_length_fuzz_case
+    w, x_pad = _rope_length_fuzz_case(k)
+    check(w, f"prepared rope length fuzz {k}", prepared=True, x_pad=x_pad)
