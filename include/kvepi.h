@@ -334,7 +334,9 @@ KVEPI_API kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d
  * Ownership.  The kvepi_prepared belongs to the caller; it holds the device
  * pointers it was prepared with and nothing else (no allocation, no pointer
  * into itself): it may be copied bytewise, used from several threads at
- * once, and dropped without any call.  Those buffers must stay allocated,
+ * once, and dropped without any call.  It is meaningful only in the process
+ * that prepared it, while this library stays loaded (it names the library's
+ * kernel by address).  Those buffers must stay allocated,
  * at the same addresses, for as long as the prepared call is run; their
  * contents may change between runs (the stream orders the kernel after the
  * writes enqueued before it, as for any launch).
