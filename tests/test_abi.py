@@ -385,3 +385,11 @@ def test_headers_compile_as_strict_c_and_cxx(header, lang, std, tmp_path):
                         "-I", os.path.join(ROOT, "include"), str(src)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_prepared_struct_size_matches_the_header():
+    import re as _re
+    text = open(os.path.join(ROOT, "include", "kvepi.h")).read()
+    n = int(_re.search(r"#define KVEPI_PREPARED_BYTES (\d+)", text).group(1))
+    assert ctypes.sizeof(B.kvepi_prepared) == n == 1024
+    assert ctypes.alignment(B.kvepi_prepared) == 8
