@@ -643,7 +643,12 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
                                             const RowBuf<MODE, ROPE, L, C> &b,
                                             const float4 *g_lds, RowOut<MODE, L, C> &o) {
   // ---- RMSNorm -> packed bf16 yw ----
+  // Speculative rows only quantise the normalised values, so they keep them
+  // as fp32 holding the bf16-rounded value (one convert per value) instead of
+  // packing pairs and unpacking them again.
+  constexpr bool DIRECT = spec_rows(MODE, NORM, FAST);
   uint4 yw[C];
+  float yf[DIRECT ? C : 1][8];
   if constexpr (NORM) {
     float s8[C];
     float mn = __builtin_inff();  // smallest magnitude of the lane's values
@@ -741,8 +746,13 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
         gamma8<L * C>(g_lds, j * L + li, g);
 #pragma unroll
         for (int q = 0; q < 8; ++q) y[q] = div_fast(v[q], rms, rcp) * g[q];
-        yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
-                           pack_bf16(y[6], y[7]));
+        if constexpr (DIRECT) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) yf[j][q] = round_bf16(y[q]);
+        } else {
+          yw[j] = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                             pack_bf16(y[6], y[7]));
+        }
       }
     } else {
 #pragma unroll
@@ -758,6 +768,7 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
           w = make_uint4(w.y, w.z, w.w, pack_bf16(y0, y1));
         }
         yw[j] = w;
+        if constexpr (DIRECT) unpack8(w, yf[j]);
       }
     }
   } else {
@@ -815,7 +826,12 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       float v[8];
-      unpack8(yw[j], v);
+      if constexpr (DIRECT) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = yf[j][q];
+      } else {
+        unpack8(yw[j], v);
+      }
       const float m = grp_max_k(amax8(v), a.glog);
       const bool fast = m >= 0x1p-90f && m <= 0x1p+100f;
       uint32_t w;
@@ -926,7 +942,12 @@ __device__ __forceinline__ void compute_row(const KArgs &a, int li, int sub,
       float vv[NB][8], mm[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        unpack8(yw[j0 + i], vv[i]);
+        if constexpr (DIRECT) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) vv[i][q] = yf[j0 + i][q];
+        } else {
+          unpack8(yw[j0 + i], vv[i]);
+        }
         mm[i] = amax8(vv[i]);
       }
 #pragma unroll
