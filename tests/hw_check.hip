@@ -1,15 +1,17 @@
 // hw_check.hip -- GPU check of the gfx950 instructions the epilog's fast paths
-// rely on, against IEEE arithmetic or the kernel's own software encoders
-// (kvepi_arith.h), over every input the kernels can give them:
+// rely on, against IEEE arithmetic or references written here from the
+// format definitions (the FP8 and FP4 codes by a nearest-value search over
+// the decoded code table, not the kernels' software encoders), over every
+// input the kernels can give them:
 //   rcp     rcp_rn(b) == 1/b for every fp32 significand, exponents [-100, 100]
 //   sqrt    sqrt_rn(x) == sqrtf(x) for every fp32 x in [2^-96, 2^127]
-//   fp8     v_cvt_pk_fp8_f32(q) == E4M3 encoder, every fp32 |q| <= 456 (a
+//   fp8     v_cvt_pk_fp8_f32(q) == E4M3 search, every fp32 |q| <= 456 (a
 //           quotient by a scale rounded to bf16 exceeds 448 by at most a
 //           factor 1 / (1 - 2^-8), below 450; from 464 on the convert no
 //           longer saturates to 448, so the kernels never give it such values)
-//   fp8s    v_cvt_scalef32_pk_fp8_f32(v, 2^E) == E4M3 encoder of v / 2^E, every
+//   fp8s    v_cvt_scalef32_pk_fp8_f32(v, 2^E) == E4M3 search of v / 2^E, every
 //           bf16 v with |v / 2^E| <= 448, E in [-100, 100]
-//   fp4s    v_cvt_scalef32_pk_fp4_f32(v, 2^E) == E2M1 encoder of v / 2^E, every
+//   fp4s    v_cvt_scalef32_pk_fp4_f32(v, 2^E) == E2M1 search of v / 2^E, every
 //           bf16 v with |v / 2^E| <= 6, E in [-100, 100]
 //   f16     f16_lo / f16_hi (v_cvt_f32_f16) == a bit-level binary16 decode, every
 //           pattern
@@ -25,7 +27,7 @@
 //   fp8sq, fp4sq  the scaled converts of fp32 inputs (the quotients by a
 //           scale's significand that the staged quantisers convert with the
 //           scale's exponent): v_cvt_scalef32_pk_{fp8,fp4}_f32(u 2^E, 2^E) ==
-//           the software encoder of u, every fp32 u in [2^-12, 456] (FP8) or
+//           the search of u, every fp32 u in [2^-12, 456] (FP8) or
 //           [2^-4, 6.0625] (FP4) and zero, every E in [-100, 100] with u 2^E
 //           normal; below those ranges, where every code is +-0, inputs q with
 //           |q| < 2^(E-12) (every 1021st pattern, subnormals included) give
@@ -60,12 +62,60 @@ __global__ void k_sqrt(uint32_t base, uint32_t n, unsigned *bad) {
   if (sqrt_rn(x) != __builtin_sqrtf(x)) atomicAdd(bad, 1u);
 }
 
+// E4M3FN magnitude of code c in 0..126 (bias 7, 3 fraction bits; exponent
+// field 0 holds the subnormals c * 2^-9; code 127 is NaN and not a value)
+__device__ float e4m3_value(uint32_t c) {
+  if (c < 8u) return (float)c * 0x1p-9f;
+  return __uint_as_float(((c >> 3) + 120u) << 23 | (c & 7u) << 20);
+}
+
+// E4M3FN code of q by search: the largest magnitude not above |q| (binary
+// search over the 127 increasing values), then the nearer of it and the next
+// one, the even code on a tie, 448 above 448 (callers keep |q| <= 456, below
+// the point 464 where a saturating rounding could differ); the sign bit from
+// q.  The two distances are exact in fp32 (Sterbenz: the neighbours lie within
+// a factor 2 of |q|, or one of them is 0).
+__device__ uint32_t e4m3_by_search(float q) {
+  const float a = __builtin_fabsf(q);
+  uint32_t lo = 0, hi = 126;  // e4m3_value(lo) <= a
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    if (e4m3_value(mid) <= a) lo = mid; else hi = mid - 1;
+  }
+  uint32_t best = lo;
+  if (lo < 126u) {
+    const float d0 = a - e4m3_value(lo), d1 = e4m3_value(lo + 1) - a;
+    if (d1 < d0 || (d1 == d0 && ((lo + 1) & 1u) == 0u)) best = lo + 1;
+  }
+  return best | ((__float_as_uint(q) >> 24) & 0x80u);
+}
+
+// E2M1 code of q by search: the nearest of the eight magnitudes, the even
+// code on a tie, 6 above 6; the sign bit from q
+__device__ uint32_t e2m1_by_search(float q) {
+  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  const float a = __builtin_fabsf(q);
+  uint32_t best = 7;
+  if (a <= 6.0f) {
+    float bd = __builtin_inff();
+    for (uint32_t c = 0; c < 8; ++c) {
+      const float dist = __builtin_fabsf(a - mag[c]);  // exact for the two nearest
+      if (dist < bd || (dist == bd && (c & 1u) == 0u)) {
+        bd = dist;
+        best = c;
+      }
+    }
+  }
+  return best | ((__float_as_uint(q) >> 28) & 0x8u);
+}
+
 __global__ void k_fp8(uint32_t base, uint32_t n, unsigned *bad) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const float q = __uint_as_float(base + i);
   const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, -q, 0, false);
-  if ((w & 0xFFu) != enc_e4m3_sw(q) || ((w >> 8) & 0xFFu) != enc_e4m3_sw(-q)) atomicAdd(bad, 1u);
+  if ((w & 0xFFu) != e4m3_by_search(q) || ((w >> 8) & 0xFFu) != e4m3_by_search(-q))
+    atomicAdd(bad, 1u);
 }
 
 typedef short s16x2_t __attribute__((ext_vector_type(2)));
@@ -138,25 +188,6 @@ __global__ void k_div16(uint32_t n, unsigned *bad) {
   if (nb) atomicAdd(bad, nb);
 }
 
-// E2M1 code of q by search: the nearest of the eight magnitudes, the even
-// code on a tie, 6 above 6; the sign bit from q
-__device__ uint32_t e2m1_by_search(float q) {
-  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-  const float a = __builtin_fabsf(q);
-  uint32_t best = 7;
-  if (a <= 6.0f) {
-    float bd = __builtin_inff();
-    for (uint32_t c = 0; c < 8; ++c) {
-      const float dist = __builtin_fabsf(a - mag[c]);  // exact: both within [0, 6]
-      if (dist < bd || (dist == bd && (c & 1u) == 0u)) {
-        bd = dist;
-        best = c;
-      }
-    }
-  }
-  return best | ((__float_as_uint(q) >> 28) & 0x8u);
-}
-
 __global__ void k_fp4q(uint32_t base, uint32_t n, unsigned *bad) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -179,12 +210,12 @@ __global__ void k_scaled(uint32_t n, int fp4, int f16, unsigned *bad, unsigned *
   uint32_t got, want;
   if (fp4) {
     got = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, -v, sc, 0) & 0xFFu;
-    want = enc_e2m1_sw(q) | (enc_e2m1_sw(-q) << 4);
+    want = e2m1_by_search(q) | (e2m1_by_search(-q) << 4);
   } else {
     s16x2_t w = {0, 0};
     w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v, -v, sc, false);
     got = (uint32_t)(uint16_t)w[0];
-    want = enc_e4m3_sw(q) | (enc_e4m3_sw(-q) << 8);
+    want = e4m3_by_search(q) | (e4m3_by_search(-q) << 8);
   }
   atomicAdd(count, 1u);
   if (got != want) atomicAdd(bad, 1u);
@@ -203,12 +234,12 @@ __global__ void k_scaledq(uint32_t base, uint32_t n, int E, int fp4, unsigned *b
       uint32_t got, want;
       if (fp4) {
         got = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, -q, sc, 0) & 0xFFu;
-        want = enc_e2m1_sw(u) | (enc_e2m1_sw(-u) << 4);
+        want = e2m1_by_search(u) | (e2m1_by_search(-u) << 4);
       } else {
         s16x2_t w = {0, 0};
         w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, q, -q, sc, false);
         got = (uint32_t)(uint16_t)w[0];
-        want = enc_e4m3_sw(u) | (enc_e4m3_sw(-u) << 8);
+        want = e4m3_by_search(u) | (e4m3_by_search(-u) << 8);
       }
       checked = true;
       if (got != want) atomicAdd(bad, 1u);
