@@ -325,8 +325,12 @@ KVEPI_API kvepi_status kvepi_run_ex(const void *x, int64_t num_tokens, int64_t d
  *        *prepared is marked invalid.
  *  kvepi_run_prepared  enqueues a prepared call on `stream` (as kvepi_run).
  *        KVEPI_ERR_NULLPTR for a NULL prepared, KVEPI_ERR_PARAM for a struct
- *        that kvepi_prepare_ex did not fill with KVEPI_OK, or when the
- *        current HIP device is not the one that was current at preparation;
+ *        whose header does not mark it as filled by a kvepi_prepare_ex that
+ *        returned KVEPI_OK (a zeroed or uninitialised struct, or one whose
+ *        preparation failed), or when the current HIP device is not the one
+ *        that was current at preparation; only that header is checked, so
+ *        running a struct whose other bytes changed after preparation is
+ *        undefined;
  *        KVEPI_ERR_RUNTIME if the launch is refused.  A prepared call of 0
  *        tokens is a no-op.  The KVEPI_CHECK_SLOTS debug check is applied at
  *        every run, as in kvepi_run.
