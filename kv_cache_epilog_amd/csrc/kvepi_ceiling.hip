@@ -30,7 +30,8 @@
 //                        void *stream);
 //     byte sizes; src_row_bytes, row_bytes, src_pitch, dst_pitch and
 //     block_stride multiples of 16 and src / dst 16-byte aligned; rows of
-//     up to 2 KiB (32 lanes x 4 pieces of 16 bytes); slots outside
+//     up to 2 KiB (32 lanes x 4 pieces of 16 bytes; rows of up to 256
+//     bytes on 16 lanes, four rows per wave step); slots outside
 //     [0, num_slots) skip the row.
 //   int kvc_empty(int32_t blocks, void *stream);
 //   int kvc_clock(uint64_t *out, int32_t spins, void *stream);
@@ -90,14 +91,18 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4_t *__restrict__
   if constexpr (W == 0) sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
-// The epilog's memory pattern: a wave takes two rows per step (lanes 0-31
-// row 2g, lanes 32-63 row 2g + 1), reads each live row's src bytes with
-// 16-byte loads and writes row_bytes to its slot's cache row with 16-byte
-// stores; the steps of a wave are nwaves apart, two of them in flight (the
-// loads of both issued before the stores of either).  A lane's read pieces
-// past the written ones are folded into its first written piece.
-constexpr int kMaxPieces = 4;  // 16-byte pieces per lane and row: rows up to 2 KiB
-
+// The epilog's memory pattern: a wave takes 64 / LR rows per step (lanes
+// LR*i .. LR*i + LR-1 row RPS*g + i), as the epilog lays its rows out (32
+// lanes a row, or 16 for rows of up to 256 bytes), reads each live row's src
+// bytes with 16-byte loads (KP per lane) and writes row_bytes to its slot's
+// cache row with 16-byte stores; the steps of a wave are nwaves apart, two of
+// them in flight (the loads of both issued before the stores of either).  A
+// lane's read pieces past the written ones are folded into its first written
+// piece.  (A lane that writes no piece of a row still issues its loads: their
+// use depends on the row widths, which the compiler does not know.  An
+// accumulator of those loads cost the 32-lane form 5 VGPRs and a wave per
+// SIMD.)
+template <int LR, int KP>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict__ src,
                                                       int64_t src_pitch, int32_t src_row_bytes,
                                                       const int32_t *__restrict__ slots,
@@ -105,25 +110,25 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
                                                       int32_t row_bytes, int32_t block_size,
                                                       int64_t dst_pitch, int64_t block_stride,
                                                       int32_t num_slots) {
-  constexpr int U = 2;
+  constexpr int U = 2, RPS = 64 / LR;
   const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, li = lane & 31;
+  const int sub = lane / LR, li = lane % LR;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t n_steps = ((int64_t)n_rows + 1) / 2;
+  const int64_t n_steps = ((int64_t)n_rows + RPS - 1) / RPS;
   const int rp = src_row_bytes / 16, wp = row_bytes / 16;
   for (int64_t g0 = wave; g0 < n_steps; g0 += U * nwaves) {
     int32_t s[U];
     bool live[U];
-    u32x4_t v[U][kMaxPieces];
+    u32x4_t v[U][KP];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = 2 * (g0 + u * nwaves) + half;
+      const int64_t row = RPS * (g0 + u * nwaves) + sub;
       s[u] = row < n_rows ? __builtin_nontemporal_load(slots + row) : -1;
       live[u] = s[u] >= 0 && s[u] < num_slots;
 #pragma unroll
-      for (int k = 0; k < kMaxPieces; ++k) {
-        const int p = li + 32 * k;
+      for (int k = 0; k < KP; ++k) {
+        const int p = li + LR * k;
         v[u][k] = (live[u] && p < rp)
                       ? ld_nt(reinterpret_cast<const u32x4_t *>(src + row * src_pitch + 16 * p))
                       : (u32x4_t){0u, 0u, 0u, 0u};
@@ -136,11 +141,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t *__restrict_
                    (int64_t)(s[u] % block_size) * dst_pitch;
       u32x4_t extra = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < kMaxPieces; ++k)
-        if (li + 32 * k >= wp) extra ^= v[u][k];
+      for (int k = 0; k < KP; ++k)
+        if (li + LR * k >= wp) extra ^= v[u][k];
 #pragma unroll
-      for (int k = 0; k < kMaxPieces; ++k) {
-        const int p = li + 32 * k;
+      for (int k = 0; k < KP; ++k) {
+        const int p = li + LR * k;
         if (p < wp)
           *reinterpret_cast<u32x4_t *>(d + 16 * p) = k == 0 ? v[u][k] ^ extra : v[u][k];
       }
@@ -196,15 +201,21 @@ __attribute__((visibility("default"))) int kvc_scatter_rows(
     int32_t n_rows, void *dst, int32_t row_bytes, int32_t block_size, int64_t dst_pitch,
     int64_t block_stride, int32_t num_slots, int32_t blocks, void *stream) {
   if (blocks < 1 || n_rows < 0 || block_size < 1 || src_row_bytes % 16 != 0 ||
-      row_bytes % 16 != 0 || src_row_bytes > 32 * 16 * kMaxPieces ||
-      row_bytes > 32 * 16 * kMaxPieces || src_pitch % 16 != 0 || dst_pitch % 16 != 0 ||
-      block_stride % 16 != 0)
+      row_bytes % 16 != 0 || src_row_bytes > 2048 || row_bytes > 2048 ||
+      src_pitch % 16 != 0 || dst_pitch % 16 != 0 || block_stride % 16 != 0)
     return (int)hipErrorInvalidValue;
   if (n_rows == 0) return 0;
-  hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint8_t *>(src), src_pitch, src_row_bytes, slots, n_rows,
-                     static_cast<uint8_t *>(dst), row_bytes, block_size, dst_pitch, block_stride,
-                     num_slots);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t *s = static_cast<const uint8_t *>(src);
+  uint8_t *d = static_cast<uint8_t *>(dst);
+  if (src_row_bytes <= 256 && row_bytes <= 256)  // 16 lanes a row, one piece each
+    hipLaunchKernelGGL((scatter_kernel<16, 1>), dim3(blocks), dim3(256), 0, st, s, src_pitch,
+                       src_row_bytes, slots, n_rows, d, row_bytes, block_size, dst_pitch,
+                       block_stride, num_slots);
+  else  // 32 lanes a row, up to four pieces each (rows up to 2 KiB)
+    hipLaunchKernelGGL((scatter_kernel<32, 4>), dim3(blocks), dim3(256), 0, st, s, src_pitch,
+                       src_row_bytes, slots, n_rows, d, row_bytes, block_size, dst_pitch,
+                       block_stride, num_slots);
   return (int)hipGetLastError();
 }
 
