@@ -294,9 +294,28 @@ def capture(launch, launches: int):
     return g
 
 
+_LEAD_BUF = {}
+
+
+def lead_in(stream) -> None:
+    """Enqueue a one-wave busy kernel (kvc_clock, about 0.33 ms) on the
+    stream just before a timed region's start event.  After a synchronize
+    the device is idle, so without it the start event would execute at once
+    and the host's submission of the graph that follows (tens of
+    microseconds) would fall inside the timed region; with it the graph is
+    queued behind the busy kernel by the time the start event executes."""
+    import torch
+    dev = stream.device
+    buf = _LEAD_BUF.get(dev)
+    if buf is None:
+        buf = _LEAD_BUF[dev] = torch.zeros(4, dtype=torch.int64, device=dev)
+    _check(ceiling_lib().kvc_clock(buf.data_ptr(), 20000, stream.cuda_stream), "kvc_clock")
+
+
 def time_graph(g, launches: int, stream, warm: bool = True) -> float:
     """ms per launch of one replay of g (a graph of `launches` launches),
-    HIP events on the stream around it; an untimed replay first if warm."""
+    HIP events on the stream around it (after a lead-in, so that no host
+    time falls inside); an untimed replay first if warm."""
     import torch
     with torch.cuda.stream(stream):
         if warm:
@@ -304,6 +323,7 @@ def time_graph(g, launches: int, stream, warm: bool = True) -> float:
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        lead_in(stream)
         e0.record(stream)
         g.replay()
         e1.record(stream)
@@ -672,6 +692,7 @@ def main():
     total0 = torch.cuda.Event(enable_timing=True)
     total1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
+        lead_in(stream)
         total0.record(stream)
         g_steps.replay()
         total1.record(stream)
@@ -820,6 +841,7 @@ def main_drq(args):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
+        lead_in(stream)
         e0.record(stream)
         g_steps.replay()
         e1.record(stream)
