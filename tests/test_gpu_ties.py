@@ -91,8 +91,11 @@ def test_reachable_significands_cover_most_of_the_table():
     assert _reachable(6.0) >= 100
 
 
+# pad: extra bytes per cache row; a pitch that is not a multiple of 16 bytes
+# takes the unstaged quantiser (a reciprocal per group instead of the table)
+@pytest.mark.parametrize("pad", [0, 1])
 @pytest.mark.parametrize("rope", [False, True])
-def test_mode0_ties_at_every_scale_significand(rope):
+def test_mode0_ties_at_every_scale_significand(rope, pad):
     import oracle
     rng = np.random.default_rng(61 + rope)
     d = 576
@@ -102,13 +105,14 @@ def test_mode0_ties_at_every_scale_significand(rope):
     bs = 4
     nblk = (T + bs - 1) // bs + 2
     w = kvgen.make(f"ties_m0_rope{rope}", 0, T, d, seed=62, x=x, rope=rope,
-                   cache=CacheSpec(nblk, bs, kc, bs * kc), skip_frac=0.0)
+                   cache=CacheSpec(nblk, bs, kc + pad, bs * (kc + pad)), skip_frac=0.0)
     assert nk >= 100
     assert check(w) == 0
 
 
+@pytest.mark.parametrize("pad", [0, 1])
 @pytest.mark.parametrize("g", [16, 32, 64])
-def test_fp4_nope_ties_at_every_scale_significand(g):
+def test_fp4_nope_ties_at_every_scale_significand(g, pad):
     import oracle
     rng = np.random.default_rng(70 + g)
     d = 576
@@ -119,6 +123,6 @@ def test_fp4_nope_ties_at_every_scale_significand(g):
     bs = 4
     nblk = (T + bs - 1) // bs + 2
     w = kvgen.make(f"ties_fp4nope_g{g}", mode, T, d, seed=71, x=x, group_size=g,
-                   cache=CacheSpec(nblk, bs, kc, bs * kc), skip_frac=0.0)
+                   cache=CacheSpec(nblk, bs, kc + pad, bs * (kc + pad)), skip_frac=0.0)
     assert nk >= 100
     assert check(w) == 0
